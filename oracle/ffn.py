@@ -1,0 +1,193 @@
+"""Expert FFN, combine and full-layer oracle, in float64.
+
+Test infrastructure only (see ``oracle/__init__``).
+
+* An expert is gate, up and down projections stored as w13 [2F, H] (gate
+  rows first, then up rows) and w2 [H, F] ([MoE] "Shapes, sourced": the
+  fused w13_weight / w2_weight shapes; [MegaMoE] §3.5: the checkpoint keeps
+  the gate columns before the up columns).
+* Its output for one hidden state x is w2 . (silu(g) * u) with g = W1 x and
+  u = W3 x, silu(g) = g / (1 + exp(-g)) ([Kernels] "The fused expert GEMM":
+  SwiGLU silu(g) * u; [MegaMoE] §1.1: silu(gate) * up).
+* The layer output of token t is sum_j w[t, j] * o[t, j], summed over the k
+  slots in slot order ([Kernels] "Combine ...": a gather per token summing
+  its k rows in a fixed order; [MegaMoE] §3.7: sum the slots in slot order).
+  The grouped form (loop over experts, scatter back) is the other form of the
+  [MoE] numpy check; the tests pin the two against each other.
+
+Weight formats (dequantised exactly, never approximated):
+
+* ``bf16``  - w13 / w2 as bf16 bits.
+* ``fp8``   - e4m3 codes with one float32 scale per 128 x 128 block of the
+  [N, K] matrix ([Kernels] "Combine, backward and low precision": 128 x 128
+  weight blocks, 1 x 128 activation tiles).
+* ``mxfp4`` - e2m1 codes packed two per byte along K plus one e8m0 scale per
+  32 values along K ([MegaMoE] §1.1).
+
+Activation modes:
+
+* ``dense`` (headline parity reference): activations are not quantised.
+* ``emulate`` (diagnostic): x and the SwiGLU output are quantised as the
+  quantised paths do: fp8 - e4m3 with a float scale amax/448 per 1 x 128
+  group; mxfp4 - e4m3 with a power-of-two scale pow2_at_least(amax/448) per
+  32 ([MegaMoE] §3.5 requantisation); an all-zero group gets scale 1.
+  The exact scale computation of the GPU (float32) is not reproduced, so
+  this mode is a diagnostic and carries no parity claim
+  ("parity unpinned" for the emulate mode).
+"""
+
+import numpy as np
+
+from .formats import (E4M3_MAX, bf16_bits_to_f64, e2m1_decode, e4m3_decode,
+                      e4m3_round, e8m0_decode, pow2_at_least, unpack_fp4)
+
+WFORMATS = ("bf16", "fp8", "mxfp4")
+
+
+def dequant(fmt, data, scale=None):
+    """Exact float64 value of one stored [N, K] weight matrix."""
+    if fmt == "bf16":
+        return bf16_bits_to_f64(data)
+    if fmt == "fp8":
+        q = e4m3_decode(data)
+        s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        n, k = q.shape
+        rows = np.repeat(s, 128, axis=0)[:n]
+        return q * np.repeat(rows, 128, axis=1)[:, :k]
+    if fmt == "mxfp4":
+        q = e2m1_decode(unpack_fp4(data, axis=-1))
+        s = e8m0_decode(scale)
+        return q * np.repeat(s, 32, axis=1)[:, : q.shape[1]]
+    raise ValueError(f"unknown weight format {fmt!r}")
+
+
+class ExpertWeights:
+    """Lazy per-expert access to stored weights.
+
+    ``w13``, ``w2`` (and the scale tensors) may be anything indexable by an
+    expert id that yields a numpy array for that expert (a numpy array of all
+    experts works; tests wrap device tensors so that only the experts that
+    are needed are copied)."""
+
+    def __init__(self, fmt, w13, w2, w13_scale=None, w2_scale=None):
+        if fmt not in WFORMATS:
+            raise ValueError(f"unknown weight format {fmt!r}")
+        self.fmt = fmt
+        self.w13, self.w2 = w13, w2
+        self.w13_scale, self.w2_scale = w13_scale, w2_scale
+
+    def expert(self, e):
+        s13 = None if self.w13_scale is None else np.asarray(self.w13_scale[e])
+        s2 = None if self.w2_scale is None else np.asarray(self.w2_scale[e])
+        W13 = dequant(self.fmt, np.asarray(self.w13[e]), s13)
+        W2 = dequant(self.fmt, np.asarray(self.w2[e]), s2)
+        return W13, W2
+
+
+def silu(g):
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def quantize_act(v, fmt):
+    """Emulate-mode activation quantisation of rows of ``v`` along its last
+    axis (see module docstring).  Returns dequantised float64 values."""
+    v = np.asarray(v, dtype=np.float64)
+    if fmt == "bf16":
+        return v
+    group = 128 if fmt == "fp8" else 32
+    n, K = v.shape
+    out = np.empty_like(v)
+    for c0 in range(0, K, group):
+        blk = v[:, c0:c0 + group]
+        amax = np.abs(blk).max(axis=1)
+        for i in range(n):
+            if amax[i] == 0.0:
+                s = 1.0
+            elif fmt == "fp8":
+                s = amax[i] / E4M3_MAX
+            else:
+                s = pow2_at_least(amax[i] / E4M3_MAX)
+            out[i, c0:c0 + group] = e4m3_round(blk[i] / s) * s
+    return out
+
+
+def expert_forward(X, W13, W2, act_fmt=None):
+    """SwiGLU expert on the rows of X [n, H] -> [n, H].  With ``act_fmt``
+    the SwiGLU output is quantised as in the emulate mode."""
+    F = W13.shape[0] // 2
+    g = X @ W13[:F].T
+    u = X @ W13[F:].T
+    a = silu(g) * u
+    if act_fmt is not None:
+        a = quantize_act(a, act_fmt)
+    return a @ W2.T
+
+
+def combine_direct(outputs, w):
+    """y[t] = sum_j w[t, j] * outputs[t, j] in slot order."""
+    outputs = np.asarray(outputs, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    y = np.zeros((outputs.shape[0], outputs.shape[2]))
+    for j in range(outputs.shape[1]):
+        y += w[:, j, None] * outputs[:, j]
+    return y
+
+
+def layer_direct(x, ids, w, expert_fn):
+    """Per token and slot: y[t] = sum_j w[t, j] * expert_fn(ids[t, j], x[t]).
+    ``expert_fn(e, rows) -> outputs`` works on a [n, H] block of rows."""
+    x = np.asarray(x, dtype=np.float64)
+    T, k = np.asarray(ids).shape
+    outs = np.zeros((T, k, x.shape[1]))
+    for t in range(T):
+        for j in range(k):
+            outs[t, j] = expert_fn(int(ids[t][j]), x[t:t + 1])[0]
+    return combine_direct(outs, w), outs
+
+
+def layer_grouped(x, ids, w, expert_fn, E):
+    """Loop over experts, run each on the rows routed to it, scatter the
+    weighted results back (the grouped form of the [MoE] numpy check).
+    Also returns the per-assignment outputs [T, k, H]."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(ids)
+    w = np.asarray(w, dtype=np.float64)
+    T, k = ids.shape
+    outs = np.zeros((T, k, x.shape[1]))
+    for e in range(E):
+        toks, slots = np.nonzero(ids == e)
+        if len(toks) == 0:
+            continue
+        outs[toks, slots] = expert_fn(e, x[toks])
+    return combine_direct(outs, w), outs
+
+
+def make_expert_fn(weights, mode="dense"):
+    """expert_fn for ``layer_*`` from an ExpertWeights; caches each expert's
+    dequantised matrices for the lifetime of the returned function."""
+    cache = {}
+    act_fmt = None if mode == "dense" else weights.fmt
+
+    def fn(e, rows):
+        if e not in cache:
+            cache[e] = weights.expert(e)
+        W13, W2 = cache[e]
+        if act_fmt is not None:
+            rows = quantize_act(rows, act_fmt)
+        return expert_forward(rows, W13, W2, act_fmt)
+
+    return fn
+
+
+def layer(x_bits, route_out, weights, E, mode="dense", tokens=None):
+    """The full layer for the tokens in ``tokens`` (all by default), given a
+    router result (``oracle.router.route``).  Returns (y [n, H] float64,
+    per-assignment outputs [n, k, H])."""
+    x = bf16_bits_to_f64(x_bits)
+    ids = route_out["ids"]
+    w = route_out["weights"]
+    if tokens is not None:
+        x, ids, w = x[tokens], ids[tokens], w[tokens]
+    fn = make_expert_fn(weights, mode)
+    return layer_grouped(x, ids, w, fn, E)

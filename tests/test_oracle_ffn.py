@@ -1,0 +1,115 @@
+"""Pins for the expert / combine / layer oracle: the [MoE] numpy combine
+example, grouped == direct, the E = 1 reduction to a dense SwiGLU MLP
+computed with torch's own silu and matmul, exact dequantisation checked
+against torch's float8 cast, and error bounds of the activation quantiser."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ffn as offn
+from oracle import formats as fm
+from oracle import router as orouter
+from synth import get_config, make_inputs, to_numpy
+from synth.generate import quantize_fp8_block, quantize_mxfp4
+
+
+def test_combine_example(golden):
+    g = golden("combine_numpy.json")
+    x = np.array(g["x"])
+    scal = g["expert_scalars"]
+
+    def expert_fn(e, rows):
+        return rows @ (scal[e] * np.eye(2)).T
+
+    yd, _ = offn.layer_direct(x, g["ids"], g["routing"], expert_fn)
+    yg, _ = offn.layer_grouped(x, g["ids"], g["routing"], expert_fn, E=3)
+    assert np.allclose(yd, g["derived_y"], rtol=0, atol=1e-14)
+    assert np.allclose(yg, yd, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_grouped_equals_direct(fmt):
+    cfg = get_config("toy", wformat=fmt, E=6, k=3, H=256, F=128)
+    inp = make_inputs(cfg, 24)
+    W = offn.ExpertWeights(fmt, to_numpy(inp["w13"]), to_numpy(inp["w2"]),
+                           to_numpy(inp["w13_scale"]), to_numpy(inp["w2_scale"]))
+    r = orouter.route(to_numpy(inp["x"]), inp["gate"].numpy(), None, cfg.k, "softmax")
+    x = fm.bf16_bits_to_f64(to_numpy(inp["x"]))
+    fn = offn.make_expert_fn(W)
+    yd, od = offn.layer_direct(x, r["ids"], r["weights"], fn)
+    yg, og = offn.layer_grouped(x, r["ids"], r["weights"], fn, cfg.E)
+    scale = np.abs(yd).max()
+    assert np.abs(yd - yg).max() <= 1e-12 * scale
+    assert np.abs(od - og).max() <= 1e-12 * np.abs(od).max()
+
+
+def test_single_expert_is_dense_swiglu_mlp():
+    """E = 1, k = 1 with renormalisation: the routed weight is 1 and the layer
+    is the dense MLP w2 . (silu(w1 x) * (w3 x)) for every token."""
+    cfg = get_config("toy", E=1, k=1, H=128, F=64)
+    inp = make_inputs(cfg, 10)
+    xb = to_numpy(inp["x"])
+    r = orouter.route(xb, inp["gate"].numpy(), None, 1, "softmax")
+    assert np.all(r["weights"] == 1.0)
+    W = offn.ExpertWeights("bf16", to_numpy(inp["w13"]), to_numpy(inp["w2"]))
+    y, _ = offn.layer(xb, r, W, E=1)
+    xt = inp["x"].to(torch.float64)
+    w13 = inp["w13"][0].to(torch.float64)
+    w2 = inp["w2"][0].to(torch.float64)
+    ref = torch.nn.functional.silu(xt @ w13[:64].T) * (xt @ w13[64:].T)
+    ref = ref @ w2.T
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_block_dequant_matches_torch():
+    g = torch.Generator().manual_seed(7)
+    w = torch.randn((256, 384), generator=g) * 0.02
+    codes, scale = quantize_fp8_block(w)
+    ours = offn.dequant("fp8", codes.numpy(), scale.numpy())
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64)
+    ref = ref * scale.to(torch.float64).repeat_interleave(128, 0).repeat_interleave(128, 1)
+    assert np.array_equal(ours, ref.numpy())
+    # and the stored values approximate the generating weights
+    assert np.abs(ours - w.numpy()).max() <= 0.07 * np.abs(w.numpy()).max()
+
+
+def test_mxfp4_dequant_hand_example():
+    # one row of 32: codes 0..15 twice, scale code 126 (0.5)
+    codes = np.array(list(range(16)) * 2, dtype=np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    vals = offn.dequant("mxfp4", packed, np.array([[126]], dtype=np.uint8))
+    table = [0, .5, 1, 1.5, 2, 3, 4, 6]
+    expect = np.array((table + [-v for v in table]) * 2) * 0.5
+    assert np.array_equal(vals[0], expect)
+
+
+def test_mxfp4_generator_roundtrip_is_nearest():
+    g = torch.Generator().manual_seed(8)
+    w = torch.randn((8, 64), generator=g)
+    packed, e8 = quantize_mxfp4(w)
+    vals = offn.dequant("mxfp4", packed.numpy(), e8.numpy())
+    s = fm.e8m0_decode(e8.numpy()).repeat(32, axis=1)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    full = np.concatenate([-grid[::-1], grid])
+    v = w.numpy() / s
+    best = np.abs(np.clip(v, -6, 6)[..., None] - full).min(axis=-1)
+    assert np.allclose(np.abs(vals / s - np.clip(v, -6, 6)), best, atol=1e-6)
+
+
+@pytest.mark.parametrize("fmt,group", [("fp8", 128), ("mxfp4", 32)])
+def test_activation_quantiser_error_bound(fmt, group):
+    rng = np.random.default_rng(9)
+    v = rng.normal(0, 1, size=(6, 256))
+    v[2, :group] = 0.0  # an all-zero group
+    q = offn.quantize_act(v, fmt)
+    assert np.all(q[2, :group] == 0.0)
+    for c0 in range(0, 256, group):
+        blk, qb = v[:, c0:c0 + group], q[:, c0:c0 + group]
+        amax = np.abs(blk).max(axis=1, keepdims=True)
+        # e4m3 keeps 3 mantissa bits: |error| <= 2^-4 |v| in the normal
+        # range, plus a subnormal floor of half of 2^-9 times the scale
+        s = np.where(amax > 0, amax / 448.0, 1.0) if fmt == "fp8" else \
+            np.array([[fm.pow2_at_least(a / 448.0) if a > 0 else 1.0] for a in amax[:, 0]])
+        assert np.all(np.abs(qb - blk) <= 2.0 ** -4 * np.abs(blk) + 2.0 ** -10 * s + 1e-15)
+        assert np.all(np.abs(qb) <= 448.0 * s * (1 + 1e-15))
