@@ -1,0 +1,162 @@
+// moe_layer (route -> align -> expert FFN on one stream), status strings,
+// the test-only error read-back and the measurement probes.
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+struct LayerLayout {
+  size_t ctrl, ids, w, sorted, bexp, npp, ffn, total;
+};
+
+// The route workspace (control block + logits) sits at offset 0 and its
+// control block doubles as the alignment workspace.
+LayerLayout layer_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
+  LayerLayout L;
+  size_t off = 0;
+  L.ctrl = off;
+  off += align_up(route_workspace_size(T, E), 256);
+  L.ids = off;
+  off += align_up((size_t)T * k * sizeof(int32_t), 256);
+  L.w = off;
+  off += align_up((size_t)T * k * sizeof(float), 256);
+  L.sorted = off;
+  off += align_up((size_t)align_max_padded(T, k, E, block_m) * sizeof(int32_t), 256);
+  L.bexp = off;
+  off += align_up((size_t)align_max_blocks(T, k, E, block_m) * sizeof(int32_t), 256);
+  L.npp = off;
+  off += 256;
+  L.ffn = off;
+  off += align_up(ffn_workspace_size(T, H, E, F, k, block_m, wformat), 256);
+  L.total = off;
+  return L;
+}
+
+__global__ void empty_kernel() {}
+
+__global__ __launch_bounds__(256) void read_kernel(const uint4* p, size_t n16, float* sink) {
+  float acc = 0.f;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) {
+    const uint4 v = p[i];
+    acc += __uint_as_float(v.x ^ v.y ^ v.z ^ v.w);
+  }
+  acc = wave_sum(acc);
+  __shared__ float s[4];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = s[0] + s[1] + s[2] + s[3];
+}
+
+int read_grid(size_t bytes) {
+  const size_t n16 = bytes / 16;
+  size_t g = (n16 + 255) / 256;
+  if (g > 4096) g = 4096;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+int layer_block_m(int T, int k, int E) {
+  const int64_t m = ((int64_t)T * k + E - 1) / E;  // tokens per expert
+  if (m <= 16) return 16;
+  if (m <= 32) return 32;
+  if (m <= 96) return 64;
+  return 128;
+}
+
+}  // namespace moe
+
+extern "C" const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_INVAL: return "MOE_E_INVAL: invalid argument";
+    case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED: unsupported shape or format";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace too small";
+    case MOE_E_HIP: return "MOE_E_HIP: HIP runtime error at launch";
+  }
+  return "unknown moe_status";
+}
+
+extern "C" int moe_layer_block_m(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1) return 16;
+  return moe::layer_block_m(T, k, E);
+}
+
+extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat) {
+  if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1) return 0;
+  if (block_m == 0) block_m = moe::layer_block_m(T, k, E);
+  return moe::layer_layout(T, H, E, F, k, block_m, wformat).total;
+}
+
+extern "C" moe_status moe_layer(const void* x, const float* gate, const float* bias, int wformat,
+                                const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
+                                int T, int H, int E, int F, int k, int n_group, int topk_group, int scoring,
+                                int renormalize, float routed_scale, int block_m, void* y,
+                                int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  using namespace moe;
+  if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1) ? layer_block_m(T, k, E) : 16;
+  // validate everything before enqueuing anything
+  int32_t dummy_i = 0;
+  float dummy_f = 0.f;
+  moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, &dummy_i, &dummy_f);
+  if (st != MOE_OK) return st;
+  st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, &dummy_i, &dummy_f, &dummy_i, &dummy_i, &dummy_i,
+                    T, H, E, F, k, block_m, y);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!workspace) return MOE_E_INVAL;
+  const LayerLayout L = layer_layout(T, H, E, F, k, block_m, wformat);
+  if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
+  char* b = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(b + L.ids);
+  float* w = topk_weights_out ? topk_weights_out : reinterpret_cast<float*>(b + L.w);
+  int32_t* sorted = reinterpret_cast<int32_t*>(b + L.sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(b + L.bexp);
+  int32_t* npp = reinterpret_cast<int32_t*>(b + L.npp);
+
+  st = launch_route(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, ids, w,
+                    nullptr, b + L.ctrl, stream);
+  if (st != MOE_OK) return st;
+  st = launch_align(ids, T, k, E, block_m, sorted, bexp, npp, b + L.ctrl, stream);
+  if (st != MOE_OK) return st;
+  FfnArgs a;
+  a.x = x; a.wformat = wformat;
+  a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
+  a.topk_ids = ids; a.topk_weights = w;
+  a.sorted_ids = sorted; a.block_expert = bexp; a.num_post_padded = npp;
+  a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.y = y;
+  ffn_carve(a, b + L.ffn);
+  return launch_ffn(a, stream);
+}
+
+extern "C" int32_t moe_debug_error(void* workspace, hipStream_t stream) {
+  int32_t v = 0;
+  if (!workspace) return -1;
+  if (hipStreamSynchronize(stream) != hipSuccess) return -1;
+  if (hipMemcpy(&v, workspace, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  const int32_t zero = 0;
+  if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return -1;
+  return v;
+}
+
+extern "C" moe_status moe_probe_empty(hipStream_t stream) {
+  moe::empty_kernel<<<1, 64, 0, stream>>>();
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" size_t moe_probe_read_sink_len(size_t bytes) { return (size_t)moe::read_grid(bytes); }
+
+extern "C" moe_status moe_probe_read(const void* p, size_t bytes, float* sink, hipStream_t stream) {
+  if (!p || !sink || bytes == 0 || bytes % 16) return MOE_E_INVAL;
+  const int g = moe::read_grid(bytes);
+  moe::read_kernel<<<g, 256, 0, stream>>>(static_cast<const uint4*>(p), bytes / 16, sink);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

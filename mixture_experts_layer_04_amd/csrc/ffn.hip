@@ -1,0 +1,181 @@
+// moe_expert_ffn: argument checks, workspace layout, the combine kernel and
+// the per-format dispatch.
+//
+// Combine ([Kernels] "Combine, backward and low precision": a gather per
+// token that sums its k rows in a fixed order is deterministic; [MegaMoE]
+// §3.7: the slots of a token are added as fp32 in slot order and rounded
+// once): one workgroup per token reads the token's k expert-output rows,
+// multiplies each by its routing weight and adds them in slot order in fp32.
+
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+int tile_grid(int64_t n_tiles, int max_wgs) {
+  int64_t g = n_tiles < max_wgs ? n_tiles : max_wgs;
+  g = (g + 7) / 8 * 8;
+  return (int)(g < 8 ? 8 : g);
+}
+
+namespace {
+
+struct FinP {
+  const uint16_t* out;
+  const int32_t* ids;
+  const float* w;
+  uint16_t* y;
+  int H, E, k;
+};
+
+__global__ __launch_bounds__(256) void finalize_kernel(FinP p) {
+  const int t = blockIdx.x;
+  const int32_t* ids = p.ids + (size_t)t * p.k;
+  const float* w = p.w + (size_t)t * p.k;
+  for (int h = threadIdx.x * 8; h < p.H; h += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < p.k; ++j) {
+      const int e = ids[j];
+      if (e < 0 || e >= p.E) continue;
+      const float wj = w[j];
+      const uint4 o = *reinterpret_cast<const uint4*>(p.out + ((size_t)t * p.k + j) * p.H + h);
+      acc[0] = __builtin_fmaf(wj, bf16_lo(o.x), acc[0]);
+      acc[1] = __builtin_fmaf(wj, bf16_hi(o.x), acc[1]);
+      acc[2] = __builtin_fmaf(wj, bf16_lo(o.y), acc[2]);
+      acc[3] = __builtin_fmaf(wj, bf16_hi(o.y), acc[3]);
+      acc[4] = __builtin_fmaf(wj, bf16_lo(o.z), acc[4]);
+      acc[5] = __builtin_fmaf(wj, bf16_hi(o.z), acc[5]);
+      acc[6] = __builtin_fmaf(wj, bf16_lo(o.w), acc[6]);
+      acc[7] = __builtin_fmaf(wj, bf16_hi(o.w), acc[7]);
+    }
+    uint4 v;
+    v.x = pack_bf16x2(acc[0], acc[1]);
+    v.y = pack_bf16x2(acc[2], acc[3]);
+    v.z = pack_bf16x2(acc[4], acc[5]);
+    v.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(p.y + (size_t)t * p.H + h) = v;
+  }
+}
+
+}  // namespace
+
+moe_status launch_finalize(const FfnArgs& a, hipStream_t s) {
+  FinP p;
+  p.out = static_cast<const uint16_t*>(a.out);
+  p.ids = a.topk_ids;
+  p.w = a.topk_weights;
+  p.y = static_cast<uint16_t*>(a.y);
+  p.H = a.H; p.E = a.E; p.k = a.k;
+  finalize_kernel<<<a.T, 256, 0, s>>>(p);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+moe_status ffn_validate(const void* x, int wformat, const void* w13, const void* w13_scale, const void* w2,
+                        const void* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+                        const int32_t* sorted_ids, const int32_t* block_expert,
+                        const int32_t* num_post_padded, int T, int H, int E, int F, int k, int block_m,
+                        const void* y) {
+  if (T < 0 || H < 128 || F < 128 || H % 128 || F % 128) return MOE_E_INVAL;
+  if (E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_E_INVAL;
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_E_INVAL;
+  if ((int64_t)T * k > (1 << 24)) return MOE_E_INVAL;
+  if (wformat != MOE_W_BF16 && wformat != MOE_W_FP8_BLOCK128 && wformat != MOE_W_MXFP4) return MOE_E_INVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !sorted_ids || !block_expert || !num_post_padded || !y)
+    return MOE_E_INVAL;
+  if (wformat != MOE_W_BF16 && (!w13_scale || !w2_scale)) return MOE_E_INVAL;
+  return MOE_OK;
+}
+
+namespace {
+struct Layout {
+  size_t xq, xs, act, act_s, out, total;
+};
+Layout ffn_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
+  Layout L;
+  const size_t mp = (size_t)align_max_padded(T, k, E, block_m);
+  size_t off = 0;
+  const bool q = wformat != MOE_W_BF16;
+  off += kCtrlBytes;  // never written by the FFN; keeps the control block intact
+  L.xq = off;
+  off += q ? align_up((size_t)T * H, 256) : 0;
+  L.xs = off;
+  off += q ? align_up((size_t)T * (H / 32) * sizeof(float), 256) : 0;
+  L.act = off;
+  off += align_up(mp * F * (q ? 1 : 2), 256);
+  L.act_s = off;
+  off += q ? align_up(mp * (F / 32) * sizeof(float), 256) : 0;
+  L.out = off;
+  off += align_up((size_t)T * k * H * 2, 256);
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat) {
+  return ffn_layout(T, H, E, F, k, block_m, wformat).total;
+}
+
+void ffn_carve(FfnArgs& a, void* ws) {
+  const Layout L = ffn_layout(a.T, a.H, a.E, a.F, a.k, a.block_m, a.wformat);
+  char* b = static_cast<char*>(ws);
+  a.xq = b + L.xq;
+  a.xs = b + L.xs;
+  a.act = b + L.act;
+  a.act_s = b + L.act_s;
+  a.out = b + L.out;
+}
+
+moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
+  if (a.T == 0) return MOE_OK;
+  moe_status st;
+  switch (a.wformat) {
+    case MOE_W_BF16:
+      st = launch_gemms_bf16(a, s);
+      break;
+    case MOE_W_FP8_BLOCK128:
+      st = launch_quant_x(a, s);
+      if (st == MOE_OK) st = launch_gemms_fp8(a, s);
+      break;
+    case MOE_W_MXFP4:
+      st = launch_quant_x(a, s);
+      if (st == MOE_OK) st = launch_gemms_mxfp4(a, s);
+      break;
+    default:
+      return MOE_E_INVAL;
+  }
+  if (st != MOE_OK) return st;
+  return launch_finalize(a, s);
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_expert_ffn(const void* x, int wformat, const void* w13, const void* w13_scale,
+                                     const void* w2, const void* w2_scale, const int32_t* topk_ids,
+                                     const float* topk_weights, const int32_t* sorted_ids,
+                                     const int32_t* block_expert, const int32_t* num_post_padded, int T,
+                                     int H, int E, int F, int k, int block_m, void* y, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  using namespace moe;
+  moe_status st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
+                               block_expert, num_post_padded, T, H, E, F, k, block_m, y);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!workspace) return MOE_E_INVAL;
+  if (workspace_bytes < ffn_workspace_size(T, H, E, F, k, block_m, wformat)) return MOE_E_WORKSPACE;
+  FfnArgs a;
+  a.x = x; a.wformat = wformat;
+  a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
+  a.topk_ids = topk_ids; a.topk_weights = topk_weights;
+  a.sorted_ids = sorted_ids; a.block_expert = block_expert; a.num_post_padded = num_post_padded;
+  a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.y = y;
+  ffn_carve(a, workspace);
+  return launch_ffn(a, stream);
+}
+
+extern "C" size_t moe_expert_ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat) {
+  if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1) return 0;
+  return moe::ffn_workspace_size(T, H, E, F, k, block_m, wformat);
+}

@@ -1,0 +1,89 @@
+// Internal (host-side) launchers shared between the entry points.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Every workspace starts with a fixed control block that no other region of
+// any entry point overlaps, so whatever sequence of shapes shares one
+// workspace, the words in it only ever hold what their owners leave there
+// (zero after each call):
+//   [0, 4)            sticky alignment error bits
+//   [256, kCtrlBytes) one counter per router token tile
+constexpr size_t kCtrlBytes = 65536;
+constexpr size_t kCounterOffset = 256;
+constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);
+
+moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
+                          int topk_group, int scoring, const int32_t* ids, const float* w);
+size_t route_workspace_size(int T, int E);
+moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+                        int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
+                        int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream);
+
+moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
+                          const void* block_expert, const void* num_post_padded);
+size_t align_workspace_size();
+int64_t align_max_padded(int T, int k, int E, int block_m);
+int64_t align_max_blocks(int T, int k, int E, int block_m);
+moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream);
+
+// Everything moe_expert_ffn needs, with the workspace already carved.
+struct FfnArgs {
+  const void* x;
+  int wformat;
+  const void* w13;
+  const void* w13_scale;
+  const void* w2;
+  const void* w2_scale;
+  const int32_t* topk_ids;
+  const float* topk_weights;
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_post_padded;
+  int T, H, E, F, k, block_m;
+  void* y;
+  // workspace regions
+  void* xq;        // quantised x (fp8 formats)
+  void* xs;        // its scales
+  void* act;       // SwiGLU output [max_padded, F]
+  void* act_s;     // its scales (fp8 formats)
+  void* out;       // expert outputs [T*k, H] bf16
+};
+
+moe_status ffn_validate(const void* x, int wformat, const void* w13, const void* w13_scale, const void* w2,
+                        const void* w2_scale, const int32_t* topk_ids, const float* topk_weights,
+                        const int32_t* sorted_ids, const int32_t* block_expert,
+                        const int32_t* num_post_padded, int T, int H, int E, int F, int k, int block_m,
+                        const void* y);
+size_t ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat);
+void ffn_carve(FfnArgs& a, void* ws);
+moe_status launch_ffn(const FfnArgs& a, hipStream_t stream);
+
+// per-format GEMM launchers (GEMM1 + SwiGLU, then GEMM2)
+moe_status launch_gemms_bf16(const FfnArgs& a, hipStream_t stream);
+moe_status launch_gemms_fp8(const FfnArgs& a, hipStream_t stream);
+moe_status launch_gemms_mxfp4(const FfnArgs& a, hipStream_t stream);
+moe_status launch_quant_x(const FfnArgs& a, hipStream_t stream);
+moe_status launch_finalize(const FfnArgs& a, hipStream_t stream);
+
+// Grid size for a grid-stride loop over `n_tiles` tiles that are spread over
+// the 8 XCDs in contiguous runs (see xcd_tile()).
+int tile_grid(int64_t n_tiles, int max_wgs);
+
+}  // namespace moe
+
+#ifdef __HIPCC__
+namespace moe {
+// Maps the i-th grid-stride tile index to a logical tile so that XCD x
+// (workgroups are dealt to the XCDs round-robin) handles the contiguous run
+// [x*per, (x+1)*per) of logical tiles; neighbouring logical tiles share a
+// weight tile and so hit the same L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t i, int64_t per) { return (i & 7) * per + (i >> 3); }
+}  // namespace moe
+#endif

@@ -8,4 +8,4 @@ those formats are made, not a step of the layer.
 """
 
 from .configs import CONFIGS, LayerConfig, get_config  # noqa: F401
-from .generate import make_inputs, make_topk_ids, make_weights, make_x, to_numpy  # noqa: F401
+from .generate import make_inputs, make_router_weights, make_topk_ids, make_weights, make_x, to_numpy  # noqa: F401

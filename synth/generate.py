@@ -104,10 +104,16 @@ def _weights(cfg: LayerConfig, device, which, N, K):
     raise ValueError(cfg.wformat)
 
 
-def make_weights(cfg: LayerConfig, device="cpu"):
-    """Router and expert weights of a configuration (independent of T)."""
+def make_router_weights(cfg: LayerConfig, device="cpu"):
+    """Gate [E, H] float32 and selection bias [E] float32 (or None)."""
     gate = _randn((cfg.E, cfg.H), cfg.gate_std, device, cfg.seed, cfg.name, "gate")
     bias = _randn((cfg.E,), cfg.bias_std, device, cfg.seed, cfg.name, "bias") if cfg.has_bias else None
+    return gate, bias
+
+
+def make_weights(cfg: LayerConfig, device="cpu"):
+    """Router and expert weights of a configuration (independent of T)."""
+    gate, bias = make_router_weights(cfg, device)
     w13, w13_scale = _weights(cfg, device, "w13", 2 * cfg.F, cfg.H)
     w2, w2_scale = _weights(cfg, device, "w2", cfg.H, cfg.F)
     return {"gate": gate, "bias": bias, "w13": w13, "w13_scale": w13_scale,

@@ -1,0 +1,124 @@
+"""GPU parity of moe_layer / moe_expert_ffn against the float64 oracle
+(relative Frobenius error within the benchmark spec's tolerance), at small sizes
+on every token (several tiles, ragged tails, every BLOCK_M) and at the full
+layer shapes on sampled tokens in the launch configuration the benchmark
+uses; plus HIP-graph capture and determinism."""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import (LAYER_TOL, bf16_to_f64, check_routing, oracle_layer, oracle_route, rel_fro,
+                     routing_for_layer, say)
+from synth import get_config, make_weights, make_x
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def weights_for(cfg):
+    key = cfg
+    if key not in _CACHE:
+        _CACHE.clear()
+        torch.cuda.empty_cache()
+        _CACHE[key] = make_weights(cfg, "cuda")
+    return _CACHE[key]
+
+
+def run_layer(cfg, W, x, block_m=0):
+    import mixture_experts_layer_04_amd as moe
+    return moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,
+                     cfg.topk_group, cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat,
+                     w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], block_m=block_m, return_routing=True)
+
+
+def check_layer(cfg, T, block_m=0, sample=None, seed=0):
+    say(f"layer {cfg.name} {cfg.wformat} E={cfg.E} H={cfg.H} F={cfg.F} k={cfg.k} T={T} block_m={block_m}")
+    W = weights_for(cfg)
+    x = make_x(cfg, T, "cuda")
+    y, ids, w = run_layer(cfg, W, x, block_m)
+    torch.cuda.synchronize()
+    r = oracle_route(cfg, x, W["gate"], W["bias"])
+    check_routing(cfg, r, ids.cpu().numpy(), w.cpu().numpy())
+    routing = routing_for_layer(cfg, r, ids.cpu().numpy())
+    tokens = None
+    if sample is not None and sample < T:
+        rng = np.random.default_rng(seed)
+        tokens = np.unique(np.concatenate([rng.choice(T, sample - 1, replace=False), [T - 1]]))
+    y_ref = oracle_layer(cfg, x, routing, W, tokens=tokens)
+    got = bf16_to_f64(y)
+    if tokens is not None:
+        got = got[tokens]
+    err = rel_fro(got, y_ref)
+    say(f"  rel. Frobenius error {err:.3e} (tolerance {LAYER_TOL[cfg.wformat]:.0e})")
+    assert np.all(np.isfinite(got))
+    assert err <= LAYER_TOL[cfg.wformat]
+    return x, W, y, ids, w, err
+
+
+SMALL = [
+    ("toy", {}, 16, 0),
+    ("toy", dict(F=256), 100, 16),
+    ("toy", dict(F=256), 100, 32),
+    ("toy", dict(F=256), 300, 64),
+    ("toy", dict(F=256), 300, 128),
+    ("toy", dict(E=16, k=4, H=384, F=256, scoring="sigmoid", has_bias=True), 333, 0),
+    ("toy", dict(E=16, k=4, H=256, F=128, scoring="sigmoid", has_bias=True, n_group=4, topk_group=2,
+                 routed_scale=2.5), 64, 16),
+    ("toy", dict(E=1, k=1, H=128, F=128), 19, 16),
+]
+
+
+@pytest.mark.parametrize("name,over,T,bm", SMALL)
+def test_layer_small_all_tokens(name, over, T, bm):
+    cfg = get_config(name, **over)
+    check_layer(cfg, T, bm)
+
+
+FULL = [("qwen3", 1), ("qwen3", 64), ("qwen3", 4096), ("glm", 1), ("glm", 8), ("glm", 512)]
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_layer_full_size_sampled(name, T):
+    cfg = get_config(name)
+    check_layer(cfg, T, 0, sample=6)
+
+
+def test_expert_ffn_matches_layer():
+    import mixture_experts_layer_04_amd as moe
+    cfg = get_config("toy", F=256)
+    x, W, y, ids, w, _ = check_layer(cfg, 200, 32)
+    s, b, n = moe.align(ids, cfg.E, 32)
+    y2 = moe.expert_ffn(x, W["w13"], W["w2"], ids, w, s, b, n, 32)
+    assert torch.equal(y, y2)
+
+
+def test_layer_graph_capture_and_determinism():
+    import mixture_experts_layer_04_amd as moe
+    cfg = get_config("toy", F=256)
+    W = weights_for(cfg)
+    x = make_x(cfg, 150, "cuda")
+
+    def call(out):
+        return moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, block_m=0, out=out)
+
+    ref = call(None).clone()
+    assert torch.equal(call(None), ref)  # deterministic
+    y_static = torch.empty_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(y_static)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(y_static)
+    for i in range(3):
+        y_static.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_static, ref), f"replay {i} differs"
+        other = call(None)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref)
