@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-GPU MoE-layer forward on MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+resident in HBM: moe_route -> moe_align -> expert FFN (GEMM1 + SwiGLU,
+GEMM2, slot-order combine), the same kernels moe_layer enqueues.  The FFN is
+driven through moe_expert_ffn_stages so that HIP events on the kernels'
+stream bracket the dominant kernel (grouped GEMM1) inside the timed region.
+
+Default workload: the Qwen3-30B-A3B-shaped layer (H 2048, E 128, k 8, F 768,
+softmax top-8, bf16 experts) at T = 4096 tokens.  Printed as one JSON line
+on stdout; diagnostics go to stderr.
+
+Also reported in the same line:
+  roofline      - the GEMM1 kernel against MI355X's published peaks
+  cpu_baseline  - the float64 oracle timed on a bounded token sample
+  decode        - cold-cache (512 MiB flush before each replay) HIP-graph
+                  replays of moe_layer at T = 1 and 64: us/layer and achieved
+                  HBM bandwidth on the weights of the experts actually touched
+  router        - moe_route alone next to the launch floor (empty kernel)
+                  and the bare gate-read kernel, cold
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X published
+MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp4": 10.1e15}  # dense FLOP/s
+METRIC = "MoE layer µs & tokens/s; HBM TB/s % (T≤256), MFMA % (T≥4k); router µs"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_qwen3_T4096_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- accounting
+def expert_bytes(cfg):
+    return cfg.expert_bytes()
+
+
+def w13_bytes(cfg):
+    return expert_bytes(cfg) * 2 // 3 if cfg.wformat == "bf16" else None
+
+
+def gemm1_work(cfg, T, touched):
+    """Algorithmic work of one grouped GEMM1 launch: weight bytes of the
+    experts touched + x read once + SwiGLU output written once; FLOPs
+    2 * T * k * 2F * H (padding rows not counted)."""
+    wbytes = touched * 2 * cfg.F * cfg.H * 2
+    nbytes = wbytes + T * cfg.H * 2 + T * cfg.k * cfg.F * 2
+    flops = 2 * T * cfg.k * 2 * cfg.F * cfg.H
+    return nbytes, flops
+
+
+def layer_flops(cfg, T):
+    return 6 * T * cfg.k * cfg.H * cfg.F
+
+
+def touched_experts(cfg, T):
+    """Expected distinct experts touched by T tokens under uniform routing,
+    E (1 - (1 - k/E)^T) ([MoE] "How many experts does a batch touch?")."""
+    return cfg.E * (1 - (1 - cfg.k / cfg.E) ** T)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("ffn_bf16.hip", "common.h", "launch.h"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_04_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM1 launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on another version of the kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- GPU parts
+def make_problem(cfg, T, device="cuda"):
+    from synth import make_weights, make_x
+    W = make_weights(cfg, device)
+    x = make_x(cfg, T, device)
+    return W, x
+
+
+class Step:
+    """The hot path as its constituent calls, with preallocated buffers."""
+
+    def __init__(self, moe, torch, cfg, W, x, block_m):
+        self.moe, self.torch, self.cfg, self.W, self.x, self.bm = moe, torch, cfg, W, x, block_m
+        T = x.shape[0]
+        dev = x.device
+        self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        need = max(moe.lib().moe_route_workspace_size(T, cfg.E),
+                   moe.lib().moe_align_workspace_size(T, cfg.k, cfg.E),
+                   moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, block_m, 0))
+        self.ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+
+    def route_align(self):
+        c, W = self.cfg, self.W
+        self.ids, self.w = self.moe.route(self.x, W["gate"], W["bias"], c.k, c.scoring, c.n_group, c.topk_group,
+                                          c.renormalize, c.routed_scale, ws=self.ws)
+        self.sid, self.bexp, self.npp = self.moe.align(self.ids, c.E, self.bm, ws=self.ws)
+
+    def ffn(self, stages):
+        W = self.W
+        self.moe.expert_ffn(self.x, W["w13"], W["w2"], self.ids, self.w, self.sid, self.bexp, self.npp, self.bm,
+                            wformat=self.cfg.wformat, w13_scale=W["w13_scale"], w2_scale=W["w2_scale"],
+                            ws=self.ws, stages=stages, out=self.y)
+
+    def __call__(self, ev=None):
+        self.route_align()
+        self.ffn(("quant",))
+        if ev is not None:
+            ev[0].record()
+        self.ffn(("gemm1",))
+        if ev is not None:
+            ev[1].record()
+        self.ffn(("gemm2", "combine"))
+
+
+def time_layer_cold(torch, fn, flush, reps=20):
+    """Median of per-replay event times, with the cache flushed before each."""
+    ts = []
+    for _ in range(reps):
+        flush.zero_()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e) * 1000.0)
+    return statistics.median(ts), min(ts)
+
+
+def graph_of(torch, fn):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def decode_sweep(moe, torch, cfg, W, flush):
+    from synth import make_x
+    out = {}
+    for T in (1, 64):
+        x = make_x(cfg, T, "cuda")
+        y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, 0, cfg.wformat),
+                         dtype=torch.uint8, device="cuda")
+
+        def call():
+            moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,
+                      cfg.topk_group, cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat,
+                      w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], ws=ws, out=y)
+
+        g = graph_of(torch, call)
+        med, best = time_layer_cold(torch, g.replay, flush)
+        ids, _ = moe.route(x, W["gate"], W["bias"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                           cfg.renormalize, cfg.routed_scale)
+        touched = int(torch.unique(ids).numel())
+        nbytes = touched * expert_bytes(cfg)
+        out[f"T{T}"] = {"us_per_layer": round(med, 2), "us_best": round(best, 2), "experts_touched": touched,
+                        "weight_bytes": nbytes, "hbm_TBps": round(nbytes / (med * 1e-6) / 1e12, 3),
+                        "hbm_frac": round(nbytes / (med * 1e-6) / HBM_PEAK, 4),
+                        "tokens_per_s": round(T / (med * 1e-6), 1)}
+        log(f"decode T={T}: {med:.1f} us/layer, {touched} experts, {out[f'T{T}']['hbm_TBps']} TB/s")
+    return out
+
+
+def router_probe(moe, torch, flush):
+    """moe_route alone (cold) beside the empty kernel and the bare read of the
+    gate, for the GLM-5.3-Flash-shaped gate (288 x 4096 fp32) and the Qwen3
+    one, at T = 1."""
+    from synth import get_config, make_router_weights, make_x
+    res = {}
+    empty = graph_of(torch, lambda: moe.probe_empty())
+    res["empty_kernel_us"] = round(time_layer_cold(torch, empty.replay, flush)[0], 2)
+    for name in ("glm", "qwen3"):
+        cfg = get_config(name)
+        gate, bias = make_router_weights(cfg, "cuda")
+        x = make_x(cfg, 1, "cuda")
+        ws = torch.zeros(moe.lib().moe_route_workspace_size(1, cfg.E), dtype=torch.uint8, device="cuda")
+        sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(gate.numel() * 4)), dtype=torch.float32, device="cuda")
+        g_route = graph_of(torch, lambda: moe.route(x, gate, bias, cfg.k, cfg.scoring, ws=ws))
+        g_read = graph_of(torch, lambda: moe.probe_read(gate, sink))
+        r_us = time_layer_cold(torch, g_route.replay, flush)[0]
+        b_us = time_layer_cold(torch, g_read.replay, flush)[0]
+        res[name] = {"route_us_T1": round(r_us, 2), "bare_gate_read_us": round(b_us, 2),
+                     "gate_bytes": gate.numel() * 4, "ratio": round(r_us / b_us, 3)}
+        log(f"router {name}: {r_us:.2f} us vs bare read {b_us:.2f} us")
+    return res
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(cfg, W, x, n_sample):
+    """The oracle as it stands on a bounded sample of the same workload:
+    route + dense-equivalent layer for the first n_sample tokens."""
+    import numpy as np
+    from oracle import ffn as offn
+    from oracle import router as orouter
+    from synth import to_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    xs = to_numpy(x[:n_sample])
+    gate, bias = to_numpy(W["gate"]), to_numpy(W["bias"])
+    Wn = offn.ExpertWeights(cfg.wformat, to_numpy(W["w13"]), to_numpy(W["w2"]),
+                            to_numpy(W["w13_scale"]), to_numpy(W["w2_scale"]))
+    t0 = time.perf_counter()
+    r = orouter.route(xs, gate, bias, cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group, cfg.renormalize,
+                      cfg.routed_scale)
+    y, _ = offn.layer(xs, r, Wn, cfg.E)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(y))
+    return {"value": round(n_sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_sample} of the {x.shape[0]} tokens (router + float64 dense-equivalent layer), "
+                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--T", type=int, default=4096)
+    ap.add_argument("--config", default="qwen3")
+    ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode sweep and router probes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (every expert is local to the "
+              "one GPU). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import mixture_experts_layer_04_amd as moe
+    from synth import get_config
+
+    cfg = get_config(args.config)
+    T = args.T
+    log(f"bench: {cfg.description}, T={T}")
+    W, x = make_problem(cfg, T)
+    bm = moe.layer_block_m(T, cfg.k, cfg.E)
+    step = Step(moe, torch, cfg, W, x, bm)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) / args.steps * 1e3
+    g1_us = statistics.mean(s.elapsed_time(e) for s, e in evs) * 1000.0
+
+    touched = int(torch.unique(step.ids).numel())
+    g1_bytes, g1_flops = gemm1_work(cfg, T, touched)
+    t_hbm, t_mfma = g1_bytes / HBM_PEAK, g1_flops / MFMA_PEAK[cfg.wformat]
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit = g1_bytes / (g1_us * 1e-6) / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = g1_flops / (g1_us * 1e-6) / 1e12, MFMA_PEAK[cfg.wformat] / 1e12, "TFLOP/s"
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
+            "kernel": "grouped GEMM1 + SwiGLU (gemm_tiled_bf16)" if bm > 16 else "grouped GEMM1 + SwiGLU (gemm_stream_bf16)",
+            "kernel_us": round(g1_us, 2), "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops,
+            "mfma_frac": round(g1_flops / (g1_us * 1e-6) / MFMA_PEAK[cfg.wformat], 4),
+            "hbm_frac": round(g1_bytes / (g1_us * 1e-6) / HBM_PEAK, 4)}
+    log(f"step {ms:.3f} ms, GEMM1 {g1_us:.1f} us ({roof['frac']:.3f} of {bound} peak)")
+
+    result = {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE layer (Qwen3-30B-A3B shape), T={T}", "T": T, "H": cfg.H,
+                   "E": cfg.E, "k": cfg.k, "F": cfg.F, "block_m": bm, "weights": cfg.wformat,
+                   "experts_touched": touched},
+        "us_per_layer": round(ms * 1e3, 2),
+        "layer_mfma_frac": round(layer_flops(cfg, T) / (ms * 1e-3) / MFMA_PEAK[cfg.wformat], 4),
+        "roofline": roof,
+    }
+    if not args.no_extras:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        result["decode"] = decode_sweep(moe, torch, cfg, W, flush)
+        result["router"] = router_probe(moe, torch, flush)
+        del flush
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(cfg, W, x, args.cpu_sample)
+        log(f"cpu oracle: {result['cpu_baseline']['value']} tokens/s on {result['cpu_baseline']['cores']} threads")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -196,6 +196,32 @@ moe_status moe_expert_ffn(const void* x, int wformat,
 size_t moe_expert_ffn_workspace_size(int T, int H, int E, int F, int k,
                                      int block_m, int wformat);
 
+/* Measurement hook: the same call as moe_expert_ffn, but only the stages in
+ * `stages` (a bit mask of moe_ffn_stage) are enqueued, in pipeline order.  A
+ * stage reads what the earlier stages left in the workspace, so running one
+ * stage alone is meaningful only after a call that ran the stages before it
+ * with the same arguments and workspace.  Lets a caller bracket a single
+ * kernel with events.  Unknown bits return MOE_E_INVAL. */
+typedef enum moe_ffn_stage {
+  MOE_STAGE_QUANT = 1,    /* activation quantisation (fp8 formats only)   */
+  MOE_STAGE_GEMM1 = 2,    /* grouped GEMM1 + SwiGLU epilogue              */
+  MOE_STAGE_GEMM2 = 4,    /* grouped GEMM2                                */
+  MOE_STAGE_COMBINE = 8,  /* weighted slot-order combine into y           */
+  MOE_STAGE_ALL = 15
+} moe_ffn_stage;
+moe_status moe_expert_ffn_stages(const void* x, int wformat,
+                                 const void* w13, const void* w13_scale,
+                                 const void* w2, const void* w2_scale,
+                                 const int32_t* topk_ids,
+                                 const float* topk_weights,
+                                 const int32_t* sorted_ids,
+                                 const int32_t* block_expert,
+                                 const int32_t* num_post_padded,
+                                 int T, int H, int E, int F, int k, int block_m,
+                                 void* y, void* workspace,
+                                 size_t workspace_bytes, int stages,
+                                 hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * moe_layer - the whole forward: moe_route -> moe_align -> moe_expert_ffn
  * on one stream with one workspace (arguments as above).

@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 SCORING = {"softmax": 0, "sigmoid": 1}
 WFORMAT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
+STAGE = {"quant": 1, "gemm1": 2, "gemm2": 4, "combine": 8, "all": 15}
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -31,6 +32,8 @@ SIGNATURES = {
     "moe_expert_ffn": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                             _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "moe_expert_ffn_stages": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i, _vp]),
     "moe_layer": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),

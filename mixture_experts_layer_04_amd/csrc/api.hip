@@ -130,6 +130,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   a.topk_ids = ids; a.topk_weights = w;
   a.sorted_ids = sorted; a.block_expert = bexp; a.num_post_padded = npp;
   a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.stages = MOE_STAGE_ALL;
   a.y = y;
   ffn_carve(a, b + L.ffn);
   return launch_ffn(a, stream);

@@ -127,37 +127,36 @@ void ffn_carve(FfnArgs& a, void* ws) {
   a.out = b + L.out;
 }
 
+static moe_status launch_gemm(const FfnArgs& a, int which, hipStream_t s) {
+  switch (a.wformat) {
+    case MOE_W_BF16: return launch_gemm_bf16(a, which, s);
+    case MOE_W_FP8_BLOCK128: return launch_gemm_fp8(a, which, s);
+    case MOE_W_MXFP4: return launch_gemm_mxfp4(a, which, s);
+  }
+  return MOE_E_INVAL;
+}
+
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
-  moe_status st;
-  switch (a.wformat) {
-    case MOE_W_BF16:
-      st = launch_gemms_bf16(a, s);
-      break;
-    case MOE_W_FP8_BLOCK128:
-      st = launch_quant_x(a, s);
-      if (st == MOE_OK) st = launch_gemms_fp8(a, s);
-      break;
-    case MOE_W_MXFP4:
-      st = launch_quant_x(a, s);
-      if (st == MOE_OK) st = launch_gemms_mxfp4(a, s);
-      break;
-    default:
-      return MOE_E_INVAL;
-  }
-  if (st != MOE_OK) return st;
-  return launch_finalize(a, s);
+  moe_status st = MOE_OK;
+  if ((a.stages & MOE_STAGE_QUANT) && a.wformat != MOE_W_BF16) st = launch_quant_x(a, s);
+  if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM1)) st = launch_gemm(a, 1, s);
+  if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM2)) st = launch_gemm(a, 2, s);
+  if (st == MOE_OK && (a.stages & MOE_STAGE_COMBINE)) st = launch_finalize(a, s);
+  return st;
 }
 
 }  // namespace moe
 
-extern "C" moe_status moe_expert_ffn(const void* x, int wformat, const void* w13, const void* w13_scale,
-                                     const void* w2, const void* w2_scale, const int32_t* topk_ids,
-                                     const float* topk_weights, const int32_t* sorted_ids,
-                                     const int32_t* block_expert, const int32_t* num_post_padded, int T,
-                                     int H, int E, int F, int k, int block_m, void* y, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
+extern "C" moe_status moe_expert_ffn_stages(const void* x, int wformat, const void* w13, const void* w13_scale,
+                                            const void* w2, const void* w2_scale, const int32_t* topk_ids,
+                                            const float* topk_weights, const int32_t* sorted_ids,
+                                            const int32_t* block_expert, const int32_t* num_post_padded,
+                                            int T, int H, int E, int F, int k, int block_m, void* y,
+                                            void* workspace, size_t workspace_bytes, int stages,
+                                            hipStream_t stream) {
   using namespace moe;
+  if (stages & ~MOE_STAGE_ALL) return MOE_E_INVAL;
   moe_status st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
                                block_expert, num_post_padded, T, H, E, F, k, block_m, y);
   if (st != MOE_OK) return st;
@@ -170,9 +169,21 @@ extern "C" moe_status moe_expert_ffn(const void* x, int wformat, const void* w13
   a.topk_ids = topk_ids; a.topk_weights = topk_weights;
   a.sorted_ids = sorted_ids; a.block_expert = block_expert; a.num_post_padded = num_post_padded;
   a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.stages = stages;
   a.y = y;
   ffn_carve(a, workspace);
   return launch_ffn(a, stream);
+}
+
+extern "C" moe_status moe_expert_ffn(const void* x, int wformat, const void* w13, const void* w13_scale,
+                                     const void* w2, const void* w2_scale, const int32_t* topk_ids,
+                                     const float* topk_weights, const int32_t* sorted_ids,
+                                     const int32_t* block_expert, const int32_t* num_post_padded, int T,
+                                     int H, int E, int F, int k, int block_m, void* y, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return moe_expert_ffn_stages(x, wformat, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
+                               block_expert, num_post_padded, T, H, E, F, k, block_m, y, workspace,
+                               workspace_bytes, MOE_STAGE_ALL, stream);
 }
 
 extern "C" size_t moe_expert_ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat) {

@@ -290,17 +290,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_bf16(GemmP p) {
 }
 
 template <int BM>
-moe_status launch_tiled(const GemmP& p, int64_t max_tiles1, int64_t max_tiles2, hipStream_t s) {
-  gemm_tiled_bf16<BM, true><<<tile_grid(max_tiles1, 1024), 256, 0, s>>>(p);
-  MOE_CHECK_LAUNCH();
-  gemm_tiled_bf16<BM, false><<<tile_grid(max_tiles2, 1024), 256, 0, s>>>(p);
+moe_status launch_tiled(const GemmP& p, int which, int64_t max_tiles1, int64_t max_tiles2, hipStream_t s) {
+  if (which == 1)
+    gemm_tiled_bf16<BM, true><<<tile_grid(max_tiles1, 1024), 256, 0, s>>>(p);
+  else
+    gemm_tiled_bf16<BM, false><<<tile_grid(max_tiles2, 1024), 256, 0, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
 
 }  // namespace
 
-moe_status launch_gemms_bf16(const FfnArgs& a, hipStream_t s) {
+moe_status launch_gemm_bf16(const FfnArgs& a, int which, hipStream_t s) {
   GemmP p;
   p.x = static_cast<const uint16_t*>(a.x);
   p.w13 = static_cast<const uint16_t*>(a.w13);
@@ -314,15 +315,16 @@ moe_status launch_gemms_bf16(const FfnArgs& a, hipStream_t s) {
   const int64_t mb = align_max_blocks(a.T, a.k, a.E, a.block_m);
   switch (a.block_m) {
     case 16: {
-      gemm_stream_bf16<true><<<tile_grid(mb * (a.F / 16), 2048), 256, 0, s>>>(p);
-      MOE_CHECK_LAUNCH();
-      gemm_stream_bf16<false><<<tile_grid(mb * (a.H / 16), 2048), 256, 0, s>>>(p);
+      if (which == 1)
+        gemm_stream_bf16<true><<<tile_grid(mb * (a.F / 16), 2048), 256, 0, s>>>(p);
+      else
+        gemm_stream_bf16<false><<<tile_grid(mb * (a.H / 16), 2048), 256, 0, s>>>(p);
       MOE_CHECK_LAUNCH();
       return MOE_OK;
     }
-    case 32: return launch_tiled<32>(p, mb * (a.F / 64), mb * (a.H / 128), s);
-    case 64: return launch_tiled<64>(p, mb * (a.F / 64), mb * (a.H / 128), s);
-    case 128: return launch_tiled<128>(p, mb * (a.F / 64), mb * (a.H / 128), s);
+    case 32: return launch_tiled<32>(p, which, mb * (a.F / 64), mb * (a.H / 128), s);
+    case 64: return launch_tiled<64>(p, which, mb * (a.F / 64), mb * (a.H / 128), s);
+    case 128: return launch_tiled<128>(p, which, mb * (a.F / 64), mb * (a.H / 128), s);
   }
   return MOE_E_INVAL;
 }

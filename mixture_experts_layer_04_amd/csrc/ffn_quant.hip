@@ -4,6 +4,6 @@
 
 namespace moe {
 moe_status launch_quant_x(const FfnArgs&, hipStream_t) { return MOE_E_UNSUPPORTED; }
-moe_status launch_gemms_fp8(const FfnArgs&, hipStream_t) { return MOE_E_UNSUPPORTED; }
-moe_status launch_gemms_mxfp4(const FfnArgs&, hipStream_t) { return MOE_E_UNSUPPORTED; }
+moe_status launch_gemm_fp8(const FfnArgs&, int, hipStream_t) { return MOE_E_UNSUPPORTED; }
+moe_status launch_gemm_mxfp4(const FfnArgs&, int, hipStream_t) { return MOE_E_UNSUPPORTED; }
 }  // namespace moe

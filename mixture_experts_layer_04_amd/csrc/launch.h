@@ -47,6 +47,7 @@ struct FfnArgs {
   const int32_t* block_expert;
   const int32_t* num_post_padded;
   int T, H, E, F, k, block_m;
+  int stages;      // bit mask of MOE_STAGE_* to run
   void* y;
   // workspace regions
   void* xq;        // quantised x (fp8 formats)
@@ -65,10 +66,10 @@ size_t ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wf
 void ffn_carve(FfnArgs& a, void* ws);
 moe_status launch_ffn(const FfnArgs& a, hipStream_t stream);
 
-// per-format GEMM launchers (GEMM1 + SwiGLU, then GEMM2)
-moe_status launch_gemms_bf16(const FfnArgs& a, hipStream_t stream);
-moe_status launch_gemms_fp8(const FfnArgs& a, hipStream_t stream);
-moe_status launch_gemms_mxfp4(const FfnArgs& a, hipStream_t stream);
+// per-format GEMM launchers; `which` is 1 for GEMM1 (+SwiGLU), 2 for GEMM2
+moe_status launch_gemm_bf16(const FfnArgs& a, int which, hipStream_t stream);
+moe_status launch_gemm_fp8(const FfnArgs& a, int which, hipStream_t stream);
+moe_status launch_gemm_mxfp4(const FfnArgs& a, int which, hipStream_t stream);
 moe_status launch_quant_x(const FfnArgs& a, hipStream_t stream);
 moe_status launch_finalize(const FfnArgs& a, hipStream_t stream);
 

@@ -11,7 +11,7 @@ stream.  The workspace is a zero-initialised byte tensor cached per device
 
 import torch
 
-from ._lib import SCORING, WFORMAT, check, lib
+from ._lib import SCORING, STAGE, WFORMAT, check, lib
 
 _WS = {}
 
@@ -99,20 +99,25 @@ def _dims(x, w13, w2, wformat):
 
 
 def expert_ffn(x, w13, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded, block_m,
-               wformat="bf16", w13_scale=None, w2_scale=None, ws=None):
-    """moe_expert_ffn -> y bf16 [T, H]."""
+               wformat="bf16", w13_scale=None, w2_scale=None, ws=None, stages=None, out=None):
+    """moe_expert_ffn -> y bf16 [T, H].  ``stages`` (names from
+    _lib.STAGE, or an int mask) selects moe_expert_ffn_stages instead."""
     _check_cuda(x, w13, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded,
                 w13_scale, w2_scale)
     T, H, E, F = _dims(x, w13, w2, wformat)
     k = topk_ids.shape[1]
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if out is None else out
     wf = WFORMAT[wformat]
     need = lib().moe_expert_ffn_workspace_size(T, H, E, F, k, block_m, wf)
     ws = workspace(x.device, need) if ws is None else ws
-    check(lib().moe_expert_ffn(_ptr(x), wf, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
-                               _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert),
-                               _ptr(num_post_padded), T, H, E, F, k, block_m, _ptr(y), _ptr(ws), ws.numel(),
-                               _stream(x.device)), "moe_expert_ffn")
+    args = [_ptr(x), wf, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
+            _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert),
+            _ptr(num_post_padded), T, H, E, F, k, block_m, _ptr(y), _ptr(ws), ws.numel()]
+    if stages is None:
+        check(lib().moe_expert_ffn(*args, _stream(x.device)), "moe_expert_ffn")
+    else:
+        mask = stages if isinstance(stages, int) else sum(STAGE[s] for s in stages)
+        check(lib().moe_expert_ffn_stages(*args, mask, _stream(x.device)), "moe_expert_ffn_stages")
     return y
 
 
