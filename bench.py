@@ -114,9 +114,10 @@ class Step:
         T = x.shape[0]
         dev = x.device
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
-        need = max(moe.lib().moe_route_workspace_size(T, cfg.E),
+        need = max(moe.lib().moe_route_workspace_size(T, cfg.H, cfg.E),
                    moe.lib().moe_align_workspace_size(T, cfg.k, cfg.E),
-                   moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, block_m, 0))
+                   moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, block_m,
+                                                           {"bf16": 0, "fp8": 1, "mxfp4": 2}[cfg.wformat]))
         self.ws = torch.zeros(need, dtype=torch.uint8, device=dev)
 
     def route_align(self):
@@ -211,7 +212,7 @@ def router_probe(moe, torch, flush):
         cfg = get_config(name)
         gate, bias = make_router_weights(cfg, "cuda")
         x = make_x(cfg, 1, "cuda")
-        ws = torch.zeros(moe.lib().moe_route_workspace_size(1, cfg.E), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(moe.lib().moe_route_workspace_size(1, cfg.H, cfg.E), dtype=torch.uint8, device="cuda")
         sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(gate.numel() * 4)), dtype=torch.float32, device="cuda")
         g_route = graph_of(torch, lambda: moe.route(x, gate, bias, cfg.k, cfg.scoring, ws=ws))
         g_read = graph_of(torch, lambda: moe.probe_read(gate, sink))

@@ -117,10 +117,11 @@ const char* moe_status_str(moe_status s);
  *  topk_weights float32 [T, k] out: their weights
  *  logits_out float32 [T, E] optional out (NULL allowed): the fp32 logits
  *
- * Arithmetic: logits accumulate bf16(x) * fp32(gate) in fp32 in one fixed
- * order for every T (a token's logits do not depend on the batch it is in,
- * [Router] §9); scores, keys and weights are fp32.
- * Constraints: 0 <= T <= 261120, H >= 8 and a multiple of 8,
+ * Arithmetic: logits accumulate bf16(x) * fp32(gate) to fp32 accuracy
+ * (the gate split exactly into three bf16 planes on matrix cores) in one
+ * fixed order for every T: a token's logits and choice do not depend on the
+ * batch it is in ([Router] §9).  Scores, keys and weights are fp32.
+ * Constraints: 0 <= T <= 261120, H >= 128 and a multiple of 128,
  * 1 <= k <= E <= 1024, k <= 16; n_group divides E, E/n_group >= 2 when n_group > 1,
  * 1 <= topk_group <= n_group, k <= topk_group * E / n_group.
  * ------------------------------------------------------------------------ */
@@ -130,7 +131,7 @@ moe_status moe_route(const void* x, const float* gate, const float* bias,
                      int32_t* topk_ids, float* topk_weights, float* logits_out,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
-size_t moe_route_workspace_size(int T, int E);
+size_t moe_route_workspace_size(int T, int H, int E);
 
 /* ------------------------------------------------------------------------
  * moe_align - block alignment ([MoE] "vLLM's Triton path: align, then
@@ -180,8 +181,9 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
  * rows are gathered through sorted_ids / k; blocks at or past the padded
  * length exit without work.  The SwiGLU output and the expert outputs are
  * bf16 in the workspace (fp8 with scales for the quantised formats).
- * Constraints: H and F multiples of 128; block_m in {16, 32, 64, 128};
- * k <= 16; E <= 1024.
+ * Constraints: H and F multiples of 128 (bf16) or of 512 (fp8 formats,
+ * else MOE_E_UNSUPPORTED); block_m in {16, 32, 64, 128}; k <= 16;
+ * E <= 1024.
  * ------------------------------------------------------------------------ */
 moe_status moe_expert_ffn(const void* x, int wformat,
                           const void* w13, const void* w13_scale,

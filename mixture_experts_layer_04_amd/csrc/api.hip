@@ -18,7 +18,7 @@ LayerLayout layer_layout(int T, int H, int E, int F, int k, int block_m, int wfo
   LayerLayout L;
   size_t off = 0;
   L.ctrl = off;
-  off += align_up(route_workspace_size(T, E), 256);
+  off += align_up(route_workspace_size(T, H, E), 256);
   L.ids = off;
   off += align_up((size_t)T * k * sizeof(int32_t), 256);
   L.w = off;

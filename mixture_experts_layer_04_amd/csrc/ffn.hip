@@ -85,6 +85,7 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
   if (!x || !w13 || !w2 || !topk_ids || !topk_weights || !sorted_ids || !block_expert || !num_post_padded || !y)
     return MOE_E_INVAL;
   if (wformat != MOE_W_BF16 && (!w13_scale || !w2_scale)) return MOE_E_INVAL;
+  if (wformat != MOE_W_BF16 && (H % 512 != 0 || F % 512 != 0)) return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -20,7 +20,7 @@ constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);
 
 moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
                           int topk_group, int scoring, const int32_t* ids, const float* w);
-size_t route_workspace_size(int T, int E);
+size_t route_workspace_size(int T, int H, int E);
 moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream);

@@ -1,20 +1,36 @@
-// Router: gate logits + scoring + (group limit) + top-k + renormalisation in
-// one launch.
+// Router: gate logits + scoring + (group limit) + top-k + renormalisation
+// (one launch at decode, two at prefill).
 //
 // [Router] §1.1 (three steps), §1.3 (rank key = score + bias, weight = score),
-// §5.3 (one row per wave, k rounds, lowest id wins ties), §8.1 (the GEMV
-// wants expert-parallel blocks, the top-k wants row-parallel waves) and §9
-// (a token's logits must not depend on its batch).
+// §2 (fp32 logits and bias), §5.3 (one row per wave, k rounds, lowest id wins
+// ties), §8.1 (the GEMV wants expert-parallel blocks, the top-k wants
+// row-parallel waves) and §9 (a token's logits must not depend on its batch).
 //
-// Layout of the work: blocks tile (expert tile x token tile).  Each wave owns
-// EPW experts and computes their fp32 dot products with TPB tokens; lane l
-// accumulates the 8-element chunks c = l, l+64, ... of H with fmaf in a
-// fixed order, then a butterfly sums the 64 lanes.  The per-(token, expert)
-// arithmetic is therefore identical for every T and tile shape.  After its
-// logits are stored, each block bumps an agent-scope counter of its token
-// tile; the block that arrives last (there is no waiting) runs the selection
-// for the tile's tokens, one wave per token, with the E logits held in VGPRs
-// (slot s of lane l is expert s*64 + l), and resets the counter to zero.
+// Logit arithmetic (identical for every T and both layouts below, so a
+// token's logits and choice are bit-identical whatever batch it is in):
+//  * the fp32 gate value g is split exactly into three bf16 planes,
+//    g = hi + mid + lo (hi: g with its low 16 bits cleared; mid: the same for
+//    the remainder; lo: the last <= 8 significant bits), and x is bf16, so
+//    every product x * plane is exact in fp32 and v_mfma_f32_16x16x32_bf16
+//    accumulates bf16(x) * fp32(gate) to fp32 accuracy;
+//  * K is cut into chunks of 128; P_c = MFMA chain over chunk c from zero
+//    (4 K-steps, each hi, mid, lo in that order);
+//  * G_j = P_4j + P_4j+1 + P_4j+2 + P_4j+3 (left to right), and
+//    logit = G_0 + G_1 + ... (left to right).
+//
+// Layouts:
+//  * small T (decode): a workgroup owns 16 experts x one group (4 chunks, one
+//    per wave) x one 16-token tile, splits its gate values in registers, sums
+//    its 4 chunk partials into G_j and stores them.  One agent-scope
+//    acquire-release counter per token tile elects the workgroup that arrives
+//    last (nobody waits); it adds the G_j, then runs the selection for the
+//    tile's tokens, one wave per token, with the E logits in VGPRs (slot s of
+//    lane l is expert s*64 + l), and resets the counter.
+//  * large T (prefill, T > 256, where a second launch is cheap next to the
+//    layer): a tiled logits kernel (64 tokens x 64 experts per workgroup,
+//    each gate value split once per 64 tokens into LDS planes) writes fp32
+//    logits, then a row-parallel kernel runs the same selection, one wave per
+//    token.
 
 #include "common.h"
 #include "launch.h"
@@ -23,85 +39,72 @@ namespace moe {
 
 namespace {
 
+constexpr int KCH = 128;          // K chunk
+constexpr int CPG = 4;            // chunks per group
+constexpr int SMALL_T_MAX = 256;  // largest T routed with the decode layout
+constexpr int PROW = 104;         // LDS plane row (bf16): hi[32] mid[32] lo[32] pad[8]
+
 struct RouteParams {
   const uint16_t* x;
   const float* gate;
   const float* bias;
-  float* logits;
+  float* part;        // decode layout: group sums [NG][T][E]
+  float* logits_out;  // optional [T][E]
   unsigned* counters;
   int32_t* ids;
   float* weights;
   int T, H, E, k, n_group, topk_group, scoring, renorm;
   float scale;
-  int n_etiles;
+  int NF, NC, NG;
 };
 
-template <int TPB, int EPW>
-__device__ __forceinline__ void gemv_tile(const RouteParams& p, int ttile, int etile) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int t0 = ttile * TPB;
-  const int e0 = etile * (4 * EPW) + wave * EPW;
-  const float* g[EPW];
-  const uint16_t* xr[TPB];
-#pragma unroll
-  for (int i = 0; i < EPW; ++i) g[i] = p.gate + (size_t)min(e0 + i, p.E - 1) * p.H;
-#pragma unroll
-  for (int j = 0; j < TPB; ++j) xr[j] = p.x + (size_t)min(t0 + j, p.T - 1) * p.H;
-
-  float acc[TPB][EPW];
-#pragma unroll
-  for (int j = 0; j < TPB; ++j)
-#pragma unroll
-    for (int i = 0; i < EPW; ++i) acc[j][i] = 0.f;
-
-  const int nchunk = p.H >> 3;
-#pragma unroll 2
-  for (int c = lane; c < nchunk; c += kWave) {
-    float gv[EPW][8];
-#pragma unroll
-    for (int i = 0; i < EPW; ++i) {
-      const float4* gp = reinterpret_cast<const float4*>(g[i] + (size_t)c * 8);
-      const float4 a = gp[0];
-      const float4 b = gp[1];
-      gv[i][0] = a.x; gv[i][1] = a.y; gv[i][2] = a.z; gv[i][3] = a.w;
-      gv[i][4] = b.x; gv[i][5] = b.y; gv[i][6] = b.z; gv[i][7] = b.w;
-    }
-#pragma unroll
-    for (int j = 0; j < TPB; ++j) {
-      uint4 xv = *reinterpret_cast<const uint4*>(xr[j] + (size_t)c * 8);
-      float xf[8] = {bf16_lo(xv.x), bf16_hi(xv.x), bf16_lo(xv.y), bf16_hi(xv.y),
-                     bf16_lo(xv.z), bf16_hi(xv.z), bf16_lo(xv.w), bf16_hi(xv.w)};
-#pragma unroll
-      for (int i = 0; i < EPW; ++i)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc[j][i] = __builtin_fmaf(xf[q], gv[i][q], acc[j][i]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < TPB; ++j)
-#pragma unroll
-    for (int i = 0; i < EPW; ++i) {
-      float v = wave_sum(acc[j][i]);
-      if (lane == 0 && t0 + j < p.T && e0 + i < p.E) p.logits[(size_t)(t0 + j) * p.E + e0 + i] = v;
-    }
+// g = hi + mid + lo exactly, each a bf16 (returned as the upper 16 bits).
+__device__ __forceinline__ void split3(float g, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t h = __float_as_uint(g) & 0xFFFF0000u;
+  const float r = g - __uint_as_float(h);
+  const uint32_t m = __float_as_uint(r) & 0xFFFF0000u;
+  const float l = r - __uint_as_float(m);
+  hi = h >> 16;
+  mid = m >> 16;
+  lo = __float_as_uint(l) >> 16;
 }
 
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// 8 consecutive fp32 gate values -> the three bf16x8 MFMA operands
+__device__ __forceinline__ void split8(const float4& g0, const float4& g1, bf16x8_t& bh, bf16x8_t& bm,
+                                       bf16x8_t& bl) {
+  const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  uint32_t h[8], m[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) split3(g[i], h[i], m[i], l[i]);
+  bh = as_bf16x8(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  bm = as_bf16x8(m[0] | (m[1] << 16), m[2] | (m[3] << 16), m[4] | (m[5] << 16), m[6] | (m[7] << 16));
+  bl = as_bf16x8(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+
+__device__ __forceinline__ f32x4_t mfma3(const bf16x8_t& a, const bf16x8_t& bh, const bf16x8_t& bm,
+                                         const bf16x8_t& bl, f32x4_t acc) {
+  acc = mfma_16x16x32_bf16(a, bh, acc);
+  acc = mfma_16x16x32_bf16(a, bm, acc);
+  acc = mfma_16x16x32_bf16(a, bl, acc);
+  return acc;
+}
+
+// Selection for one token from its E fp32 logits (l[s] = logit of expert
+// s*64 + lane, -inf past E); writes ids / weights of token t.
 template <int SLOTS>
-__device__ __forceinline__ void select_token(const RouteParams& p, int t) {
+__device__ __forceinline__ void select_token(const RouteParams& p, int t, const float (&l)[SLOTS]) {
   const int lane = threadIdx.x & 63;
-  const float* lg = p.logits + (size_t)t * p.E;
   float key[SLOTS], sc[SLOTS];
   bool ok[SLOTS];
   const float NEG_INF = -__builtin_inff();
-
-  float l[SLOTS];
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int e = s * kWave + lane;
-    ok[s] = e < p.E;
-    l[s] = ok[s] ? lg[e] : NEG_INF;
-  }
+  for (int s = 0; s < SLOTS; ++s) ok[s] = s * kWave + lane < p.E;
+
   if (p.scoring == MOE_SOFTMAX) {
     float m = NEG_INF;
 #pragma unroll
@@ -203,70 +206,260 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t) {
   }
 }
 
-template <int TPB, int EPW, int SLOTS>
-__global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
-  const int etile = blockIdx.x;
+// ---------------------------------------------------------------------------
+// Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token tiles.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void route_small(RouteParams p) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int f = blockIdx.x % p.NF;
+  const int j = blockIdx.x / p.NF;
   const int ttile = blockIdx.y;
-  gemv_tile<TPB, EPW>(p, ttile, etile);
-
+  const int t0 = ttile * 16;
+  const int c = j * CPG + wave;
+  __shared__ float red[CPG][16][17];
   __shared__ int s_last;
-  __threadfence();  // this thread's logits are visible at agent scope
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (c < p.NC) {
+    const int e = min(f * 16 + r, p.E - 1);
+    const float* grow = p.gate + (size_t)e * p.H + c * KCH + q * 8;
+    const int t = t0 + r;
+    const bool tv = t < p.T;
+    const uint16_t* xrow = p.x + (size_t)(tv ? t : 0) * p.H + c * KCH + q * 8;
+    float4 g0[4], g1[4];
+    bf16x8_t a[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      g0[s] = *reinterpret_cast<const float4*>(grow + 32 * s);
+      g1[s] = *reinterpret_cast<const float4*>(grow + 32 * s + 4);
+      a[s] = *reinterpret_cast<const bf16x8_t*>(xrow + 32 * s);
+      if (!tv) a[s] = bf16x8_t{};
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t bh, bm, bl;
+      split8(g0[s], g1[s], bh, bm, bl);
+      acc = mfma3(a[s], bh, bm, bl, acc);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][4 * q + i][r] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+    const int nc = min(CPG, p.NC - j * CPG);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = lane * 4 + i;  // 256 entries of the 16 x 16 tile
+      const int tl = idx >> 4;
+      const int el = idx & 15;
+      float gsum = red[0][tl][el];
+      for (int w = 1; w < nc; ++w) gsum += red[w][tl][el];
+      const int t = t0 + tl;
+      const int e = f * 16 + el;
+      if (t < p.T && e < p.E) p.part[((size_t)j * p.T + t) * p.E + e] = gsum;
+    }
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(p.counters + ttile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == (unsigned)(p.n_etiles - 1);
+    const int last = prev == (unsigned)(gridDim.x - 1);
     if (last) __hip_atomic_store(p.counters + ttile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // acquire: see every block's logits
-  const int wave = threadIdx.x >> 6;
-  for (int j = wave; j < TPB; j += 4) {
-    const int t = ttile * TPB + j;
-    if (t < p.T) select_token<SLOTS>(p, t);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every wave sees all group sums
+  for (int tl = wave; tl < 16; tl += 4) {
+    const int t = t0 + tl;
+    if (t >= p.T) break;
+    float l[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const int e = s * kWave + lane;
+      float v = -__builtin_inff();
+      if (e < p.E) {
+        v = p.part[(size_t)t * p.E + e];
+        for (int jj = 1; jj < p.NG; ++jj) v += p.part[((size_t)jj * p.T + t) * p.E + e];
+        if (p.logits_out) p.logits_out[(size_t)t * p.E + e] = v;
+      }
+      l[s] = v;
+    }
+    select_token<SLOTS>(p, t, l);
   }
 }
 
-template <int TPB, int EPW>
-moe_status launch_route_tpb(const RouteParams& p0, hipStream_t stream) {
-  RouteParams p = p0;
-  p.n_etiles = ceil_div(p.E, 4 * EPW);
-  dim3 grid(p.n_etiles, ceil_div(p.T, TPB));
-  const int slots = ceil_div(p.E, kWave);
-  if (slots <= 1)
-    route_kernel<TPB, EPW, 1><<<grid, 256, 0, stream>>>(p);
-  else if (slots <= 2)
-    route_kernel<TPB, EPW, 2><<<grid, 256, 0, stream>>>(p);
-  else if (slots <= 4)
-    route_kernel<TPB, EPW, 4><<<grid, 256, 0, stream>>>(p);
-  else if (slots <= 5)
-    route_kernel<TPB, EPW, 5><<<grid, 256, 0, stream>>>(p);
-  else if (slots <= 8)
-    route_kernel<TPB, EPW, 8><<<grid, 256, 0, stream>>>(p);
-  else
-    route_kernel<TPB, EPW, 16><<<grid, 256, 0, stream>>>(p);
+// ---------------------------------------------------------------------------
+// Prefill layout, first kernel: logits of a 64-token x 64-expert tile.
+// 4 waves as 2 x 2, each 32 tokens x 32 experts (2 x 2 fragments).  Per
+// 32-wide K step the 256 threads split the tile's 64 x 32 gate values once
+// into LDS planes (so each gate value is split once per 64 tokens) while the
+// next step's values are already in flight.
+constexpr int LT = 64;  // tokens per tile
+constexpr int LE = 64;  // experts per tile
+
+__global__ __launch_bounds__(256) void route_logits_tiled(RouteParams p, float* logits) {
+  __shared__ __attribute__((aligned(16))) uint16_t planes[LE * PROW];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int r = lane & 15;
+  const int q = lane >> 4;
+  const int t0 = blockIdx.x * LT;
+  const int e0 = blockIdx.y * LE;
+  const int nsteps = p.H / 32;
+
+  // this thread's two float4 pieces of each K step: expert row (tid >> 3) and
+  // (tid >> 3) + 32, K offset (tid & 7) * 4
+  const int se = tid >> 3;
+  const int sk = (tid & 7) * 4;
+  const bool sv0 = e0 + se < p.E;
+  const bool sv1 = e0 + se + 32 < p.E;
+  const float* g0p = p.gate + (size_t)min(e0 + se, p.E - 1) * p.H + sk;
+  const float* g1p = p.gate + (size_t)min(e0 + se + 32, p.E - 1) * p.H + sk;
+  const uint16_t* xr[2];
+  bool tv[2];
+#pragma unroll
+  for (int tf = 0; tf < 2; ++tf) {
+    const int t = t0 + wm * 32 + tf * 16 + r;
+    tv[tf] = t < p.T;
+    xr[tf] = p.x + (size_t)(tv[tf] ? t : 0) * p.H + q * 8;
+  }
+
+  f32x4_t part[2][2], grp[2][2], tot[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      part[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      grp[a][b] = part[a][b];
+      tot[a][b] = part[a][b];
+    }
+
+  float4 ng0 = *reinterpret_cast<const float4*>(g0p);
+  float4 ng1 = *reinterpret_cast<const float4*>(g1p);
+  bf16x8_t na[2];
+#pragma unroll
+  for (int tf = 0; tf < 2; ++tf) na[tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf]);
+
+  for (int st = 0; st < nsteps; ++st) {
+    const float4 g0 = sv0 ? ng0 : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 g1 = sv1 ? ng1 : make_float4(0.f, 0.f, 0.f, 0.f);
+    bf16x8_t a[2];
+#pragma unroll
+    for (int tf = 0; tf < 2; ++tf) a[tf] = tv[tf] ? na[tf] : bf16x8_t{};
+    __syncthreads();  // the previous step's planes are consumed
+    {
+      uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+      uint16_t* row = planes + se * PROW + sk;
+      split3(g0.x, h0, m0, l0); split3(g0.y, h1, m1, l1); split3(g0.z, h2, m2, l2); split3(g0.w, h3, m3, l3);
+      *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
+      *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+      row += 32 * PROW;
+      split3(g1.x, h0, m0, l0); split3(g1.y, h1, m1, l1); split3(g1.z, h2, m2, l2); split3(g1.w, h3, m3, l3);
+      *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
+      *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    }
+    if (st + 1 < nsteps) {  // prefetch the next step
+      const int kb = (st + 1) * 32;
+      ng0 = *reinterpret_cast<const float4*>(g0p + kb);
+      ng1 = *reinterpret_cast<const float4*>(g1p + kb);
+#pragma unroll
+      for (int tf = 0; tf < 2; ++tf) na[tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ef = 0; ef < 2; ++ef) {
+      const uint16_t* pr = planes + (wn * 32 + ef * 16 + r) * PROW + q * 8;
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pr);
+      const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(pr + 32);
+      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pr + 64);
+#pragma unroll
+      for (int tf = 0; tf < 2; ++tf) part[tf][ef] = mfma3(a[tf], bh, bm, bl, part[tf][ef]);
+    }
+    if ((st & 3) == 3 || st == nsteps - 1) {  // end of a chunk
+      const int c = st >> 2;
+      const bool first_in_group = (c % CPG) == 0;
+      const bool end_of_group = (c % CPG) == CPG - 1 || st == nsteps - 1;
+      const bool first_group = c < CPG;
+#pragma unroll
+      for (int tf = 0; tf < 2; ++tf)
+#pragma unroll
+        for (int ef = 0; ef < 2; ++ef) {
+          grp[tf][ef] = first_in_group ? part[tf][ef] : grp[tf][ef] + part[tf][ef];
+          part[tf][ef] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (end_of_group) tot[tf][ef] = first_group ? grp[tf][ef] : tot[tf][ef] + grp[tf][ef];
+        }
+    }
+  }
+#pragma unroll
+  for (int tf = 0; tf < 2; ++tf)
+#pragma unroll
+    for (int ef = 0; ef < 2; ++ef)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int t = t0 + wm * 32 + tf * 16 + 4 * q + ii;
+        const int e = e0 + wn * 32 + ef * 16 + r;
+        if (t < p.T && e < p.E) logits[(size_t)t * p.E + e] = tot[tf][ef][ii];
+      }
+}
+
+// Prefill layout, second kernel: one wave per token selects from its logits.
+template <int SLOTS>
+__global__ __launch_bounds__(256) void route_select(RouteParams p, const float* logits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;
+  float l[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int e = s * kWave + lane;
+    l[s] = e < p.E ? logits[(size_t)t * p.E + e] : -__builtin_inff();
+  }
+  select_token<SLOTS>(p, t, l);
+}
+
+bool use_large(int T, int E) { (void)E; return T > SMALL_T_MAX; }
+
+template <int SLOTS>
+moe_status launch_slots(const RouteParams& p, hipStream_t stream) {
+  if (use_large(p.T, p.E)) {
+    float* logits = p.logits_out ? p.logits_out : p.part;
+    route_logits_tiled<<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE)), 256, 0, stream>>>(p, logits);
+    MOE_CHECK_LAUNCH();
+    route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p, logits);
+  } else {
+    dim3 grid(p.NF * p.NG, ceil_div(p.T, 16));
+    route_small<SLOTS><<<grid, 256, 0, stream>>>(p);
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
 
 }  // namespace
 
-size_t route_workspace_size(int T, int E) { return kCtrlBytes + align_up((size_t)T * E * sizeof(float), 256); }
-
-static int route_tokens_per_tile(int T) { return T <= 1 ? 1 : (T <= 4 ? 4 : 16); }
+size_t route_workspace_size(int T, int H, int E) {
+  const size_t per_token = use_large(T, E) ? (size_t)E : (size_t)ceil_div(H, KCH * CPG) * E;
+  return kCtrlBytes + align_up(per_token * T * sizeof(float), 256);
+}
 
 moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
                           int topk_group, int scoring, const int32_t* ids, const float* w) {
-  if (T < 0 || H < 8 || H % 8 != 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_E_INVAL;
+  if (T < 0 || H < 128 || H % 128 != 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_E_INVAL;
   if (scoring != MOE_SOFTMAX && scoring != MOE_SIGMOID) return MOE_E_INVAL;
   if (n_group < 1 || n_group > 64 || E % n_group != 0) return MOE_E_INVAL;
   if (n_group > 1 && (E / n_group < 2)) return MOE_E_INVAL;
   if (topk_group < 1 || topk_group > n_group) return MOE_E_INVAL;
   if ((int64_t)k > (int64_t)topk_group * (E / n_group)) return MOE_E_INVAL;
   if (T > 0 && (!x || !gate || !ids || !w)) return MOE_E_INVAL;
-  if (ceil_div(T, route_tokens_per_tile(T)) > kMaxCounters) return MOE_E_INVAL;
+  if (ceil_div(T, 16) > kMaxCounters) return MOE_E_INVAL;
   return MOE_OK;
 }
 
@@ -279,7 +472,8 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
   p.gate = gate;
   p.bias = bias;
   char* base = static_cast<char*>(ws);
-  p.logits = logits_out ? logits_out : reinterpret_cast<float*>(base + kCtrlBytes);
+  p.part = reinterpret_cast<float*>(base + kCtrlBytes);
+  p.logits_out = logits_out;
   p.counters = reinterpret_cast<unsigned*>(base + kCounterOffset);
   p.ids = ids;
   p.weights = weights;
@@ -287,12 +481,16 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
   p.n_group = n_group; p.topk_group = topk_group;
   p.scoring = scoring; p.renorm = renormalize != 0;
   p.scale = routed_scale;
-  p.n_etiles = 1;
-  switch (route_tokens_per_tile(T)) {
-    case 1: return launch_route_tpb<1, 1>(p, stream);
-    case 4: return launch_route_tpb<4, 1>(p, stream);
-    default: return launch_route_tpb<16, 2>(p, stream);
-  }
+  p.NF = ceil_div(E, 16);
+  p.NC = H / KCH;
+  p.NG = ceil_div(p.NC, CPG);
+  const int slots = ceil_div(E, kWave);
+  if (slots <= 1) return launch_slots<1>(p, stream);
+  if (slots <= 2) return launch_slots<2>(p, stream);
+  if (slots <= 4) return launch_slots<4>(p, stream);
+  if (slots <= 5) return launch_slots<5>(p, stream);
+  if (slots <= 8) return launch_slots<8>(p, stream);
+  return launch_slots<16>(p, stream);
 }
 
 }  // namespace moe
@@ -307,12 +505,12 @@ extern "C" moe_status moe_route(const void* x, const float* gate, const float* b
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!workspace) return MOE_E_INVAL;
-  if (workspace_bytes < route_workspace_size(T, E)) return MOE_E_WORKSPACE;
+  if (workspace_bytes < route_workspace_size(T, H, E)) return MOE_E_WORKSPACE;
   return launch_route(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                       topk_ids, topk_weights, logits_out, workspace, stream);
 }
 
-extern "C" size_t moe_route_workspace_size(int T, int E) {
-  if (T < 0 || E < 1) return 0;
-  return moe::route_workspace_size(T, E);
+extern "C" size_t moe_route_workspace_size(int T, int H, int E) {
+  if (T < 0 || H < 1 || E < 1) return 0;
+  return moe::route_workspace_size(T, H, E);
 }

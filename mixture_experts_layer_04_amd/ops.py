@@ -67,7 +67,7 @@ def route(x, gate, bias, k, scoring="softmax", n_group=1, topk_group=1, renormal
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
-    need = lib().moe_route_workspace_size(T, E)
+    need = lib().moe_route_workspace_size(T, H, E)
     ws = workspace(x.device, need) if ws is None else ws
     check(lib().moe_route(_ptr(x), _ptr(gate), _ptr(bias), T, H, E, k, n_group, topk_group,
                           SCORING[scoring], int(bool(renormalize)), float(routed_scale),

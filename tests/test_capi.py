@@ -51,10 +51,10 @@ def test_status_strings(L):
 
 
 def test_route_argument_checks(L):
-    def call(T=4, H=64, E=8, k=2, ng=1, tg=1, scoring=0, ws=FAKE, nbytes=1 << 20):
+    def call(T=4, H=128, E=8, k=2, ng=1, tg=1, scoring=0, ws=FAKE, nbytes=1 << 20):
         return L.moe_route(FAKE, FAKE, None, T, H, E, k, ng, tg, scoring, 1, 1.0, FAKE, FAKE, None, ws, nbytes, None)
     assert call(T=-1) == 1
-    assert call(H=60) == 1            # H not a multiple of 8
+    assert call(H=192) == 1           # H not a multiple of 128
     assert call(k=0) == 1
     assert call(k=9) == 1             # k > E
     assert call(E=2000, k=2) == 1     # E > 1024
@@ -65,7 +65,7 @@ def test_route_argument_checks(L):
     assert call(ws=None) == 1
     assert call(nbytes=16) == 3       # workspace too small
     assert call(T=261121) == 1        # more token tiles than router counters
-    assert L.moe_route_workspace_size(1, 8) >= 65536  # control block first
+    assert L.moe_route_workspace_size(1, 128, 8) >= 65536  # control block first
     assert call(T=0) == 0             # empty batch is a no-op
 
 
