@@ -73,7 +73,7 @@ def touched_experts(cfg, T):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("ffn_bf16.hip", "common.h", "launch.h"):
+    for f in ("ffn_gemm.hip", "common.h", "launch.h"):
         with open(os.path.join(ROOT, "mixture_experts_layer_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -263,6 +263,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=2048)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode sweep and router probes")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device to device once (a kernel of known traffic that calibrates "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every expert is local to the "
@@ -275,6 +278,12 @@ def main():
 
     cfg = get_config(args.config)
     T = args.T
+    if args.copy_probe:
+        src = torch.ones(args.copy_probe << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"bench: {cfg.description}, T={T}")
     W, x = make_problem(cfg, T)
     bm = moe.layer_block_m(T, cfg.k, cfg.E)
@@ -303,7 +312,7 @@ def main():
         achieved, peak, unit = g1_flops / (g1_us * 1e-6) / 1e12, MFMA_PEAK[cfg.wformat] / 1e12, "TFLOP/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
-            "kernel": "grouped GEMM1 + SwiGLU (gemm_tiled_bf16)" if bm > 16 else "grouped GEMM1 + SwiGLU (gemm_stream_bf16)",
+            "kernel": "grouped GEMM1 + SwiGLU (gemm_tiled)" if bm > 16 else "grouped GEMM1 + SwiGLU (gemm_stream)",
             "kernel_us": round(g1_us, 2), "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops,
             "mfma_frac": round(g1_flops / (g1_us * 1e-6) / MFMA_PEAK[cfg.wformat], 4),
             "hbm_frac": round(g1_bytes / (g1_us * 1e-6) / HBM_PEAK, 4)}

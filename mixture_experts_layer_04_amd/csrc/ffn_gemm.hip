@@ -39,9 +39,9 @@
 //    into VGPRs (a weight element is used once); the quarters are reduced in
 //    LDS in a fixed order before the epilogue.
 //  * BLOCK_M >= 32 ("tiled", prefill): 2 x 2 waves, A (BLOCK_M rows) and B
-//    tiles double-buffered in LDS, 128 bytes of K per row per step, the next
-//    step's global loads in flight while the current step is multiplied; one
-//    barrier per step.
+//    tiles copied straight into a 3-stage LDS ring two K steps (128 bytes of
+//    K per row each) ahead of the multiply; one barrier per step; the output
+//    tile leaves through LDS as whole rows.
 // Tiles are visited in a grid-stride loop bounded by the padded length read
 // on the device (no workgroup is launched for blocks that do not exist), in
 // an order that keeps the blocks sharing a weight tile on one XCD.
@@ -198,18 +198,59 @@ __device__ __forceinline__ int a_row_index(const GemmP& p, int blk, int bm, int 
 // columns).  Waves 2 x 2: wave (wm, wn) owns rows [wm*BM/2, +BM/2) and weight
 // rows: GEMM1 gate [wn*BNW/4, +BNW/4) and up [BNW/2 + wn*BNW/4, +BNW/4);
 // GEMM2 [wn*BNW/2, +BNW/2).
-template <int F, bool G1, int BM, int BNW>
+//
+// K steps of 128 bytes per row are copied global -> LDS with
+// global_load_lds_dwordx4 (no VGPR staging) into a ring of NS stages, NS - 1
+// steps ahead of the multiply; one barrier per step.  Inside a stage a row's
+// 16-byte chunk c sits at slot c ^ f(row) (f(row) = (row / (16 / chunks per
+// row)) mod chunks per row), so the 16 rows one MFMA operand read touches
+// fall in 16 different bank groups.  The epilogue stages the output tile in
+// LDS and writes whole rows with 16-byte stores.
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
+__device__ __forceinline__ void g2lds16(const uint8_t* g, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gvoid_t*)g, (lvoid_t*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds_dst) {
+  __builtin_amdgcn_global_load_lds((gvoid_t*)g, (lvoid_t*)lds_dst, 4, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for the copy pipeline: each wave has already waited for
+// its own copies of the step (wait_vm), so no memory fence is needed, and a
+// fence would also wait for the copies still in flight for later steps.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int CPR>
+__device__ __forceinline__ int swz(int c, int row) {
+  return c ^ ((row / (16 / CPR)) & (CPR - 1));
+}
+
+template <int F, bool G1, int BM, int BNW, int NS>
 __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
   using T = Tr<F>;
-  constexpr int LDA = 128 + 16;                 // LDS bytes per A row
-  constexpr int LDB = T::BROW + 16;             // LDS bytes per B row
-  constexpr int ASZ = BM * LDA;
-  constexpr int BSZ = BNW * LDB;
+  constexpr int CPRB = T::BROW / 16;   // 16-byte chunks per B row and step
+  constexpr int ASZ = BM * 128;
+  constexpr int BSZ = BNW * T::BROW;
   constexpr int FM = BM / 32;
   constexpr int FN = BNW / 32;
-  constexpr int A_CH = BM * 8 / 256;            // 16-byte pieces per thread
-  constexpr int B_PR = T::BROW / 16;            // pieces per B row
-  constexpr int B_CH = BNW * B_PR / 256;
+  constexpr int LA = BM / 32;          // A copy instructions per wave per step
+  constexpr int LB = BNW * CPRB / 256; // B copy instructions per wave per step
+  // scales (FP8, MX): one 4-byte word per tile row (A: the row's scale(s) of
+  // the step, B: the weight row's) copied with the data; every wave issues
+  // the same number of copies, the slots past BM + BNW are never read
+  constexpr int LSC = (F == F_BF16) ? 0 : (BM + BNW + 255) / 256;
+  constexpr int LS = LA + LB + LSC;
+  constexpr int SCSZ = LSC * 256 * 4;
+  constexpr int SSZ = ASZ + BSZ + SCSZ;
+  constexpr int D = NS - 1;            // steps in flight ahead of the multiply
+  static_assert(LS * (D > 1 ? D - 1 : 1) <= 63, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -219,18 +260,29 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
   const int wn = wave & 1;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int K = G1 ? p.H : p.F;                 // in elements
-  const int N = G1 ? p.F : p.H;                 // output columns
+  const int K = G1 ? p.H : p.F;
+  const int N = G1 ? p.F : p.H;
   const int BNO = G1 ? BNW / 2 : BNW;
   const int ntn = N / BNO;
   const int nblk = *p.npp / BM;
   const int64_t n_valid = (int64_t)nblk * ntn;
   const int64_t per = (n_valid + 7) >> 3;
   const int nk = K / T::KSTEP;
-  const int rowbytes_a = K * T::AB;             // bytes per A row in global memory
+  const int rowbytes_a = K * T::AB;
   const int rowbytes_b = (F == F_MX) ? K / 2 : K * T::AB;
   const uint8_t* asrc = G1 ? p.x : p.act;
   const uint8_t* wsrc = G1 ? p.w13 : p.w2;
+  const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
+
+  // tile-local weight row of fragment fn of this wave
+  auto frag_lrow = [&](int fn) {
+    return G1 ? (fn < FN / 2 ? wn * (BNW / 4) + fn * 16 : BNW / 2 + wn * (BNW / 4) + (fn - FN / 2) * 16)
+              : wn * (BNW / 2) + fn * 16;
+  };
+  auto weight_row = [&](int nt, int lrow) {
+    if (G1) return lrow < BNW / 2 ? nt * (BNW / 2) + lrow : p.F + nt * (BNW / 2) + (lrow - BNW / 2);
+    return nt * BNW + lrow;
+  };
 
   for (int64_t it = blockIdx.x; it < 8 * per; it += gridDim.x) {
     const int64_t L = xcd_tile(it, per);
@@ -239,69 +291,66 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
     const int nt = (int)(L / nblk);
     const int e = p.block_expert[blk];
 
-    // global sources of this thread's pieces
-    const uint8_t* ap[A_CH];
-    bool av[A_CH];
+    // per-lane global sources of the copy instructions
+    const uint8_t* ag[LA];
 #pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch >> 3;
+    for (int i = 0; i < LA; ++i) {
+      const int row = wave * (BM / 4) + 8 * i + (lane >> 3);
       bool v;
-      const int src = a_row_index<G1>(p, blk, BM, row, v);
-      av[c] = v;
-      ap[c] = asrc + (size_t)src * rowbytes_a + (ch & 7) * 16;
+      const int src = a_row_index<G1>(p, blk, BM, row, v);  // padding rows read token 0; never used
+      ag[i] = asrc + (size_t)src * rowbytes_a + 16 * swz<8>(lane & 7, row);
     }
-    const uint8_t* bp[B_CH];
+    const uint8_t* bg[LB];
 #pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int ch = tid + 256 * c;
-      const int row = ch / B_PR;
-      int wrow;
-      if (G1)
-        wrow = row < BNW / 2 ? nt * (BNW / 2) + row : p.F + nt * (BNW / 2) + (row - BNW / 2);
-      else
-        wrow = nt * BNW + row;
-      const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
-      bp[c] = wsrc + ((size_t)e * erows + wrow) * rowbytes_b + (ch % B_PR) * 16;
+    for (int i = 0; i < LB; ++i) {
+      const int row = (wave * LB + i) * (64 / CPRB) + lane / CPRB;
+      bg[i] = wsrc + ((size_t)e * erows + weight_row(nt, row)) * rowbytes_b + 16 * swz<CPRB>(lane % CPRB, row);
     }
-
-    // rows of this wave's fragments (for the epilogue and the scales)
-    int arow_src[FM][4];
-    bool arow_ok[FM][4];
+    // scale words: slot q = (i * 4 + wave) * 64 + lane of copy i; q < BM: A
+    // row q, q < BM + BNW: B row q - BM.  Per step the source advances by
+    // sc_step bytes.
+    const uint8_t* scg[LSC > 0 ? LSC : 1];
+    int sc_step[LSC > 0 ? LSC : 1];
+    if (F != F_BF16) {
+      const int kblocks = K / 128;  // FP8: one fp32 scale per 128 K; MX: 4 e8m0 per 128 K
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bool v;
-        arow_src[fm][i] = a_row_index<G1>(p, blk, BM, wm * (BM / 2) + fm * 16 + 4 * g + i, v);
-        arow_ok[fm][i] = v;
+      for (int i = 0; i < LSC; ++i) {
+        const int q = (i * 4 + wave) * 64 + lane;
+        if (q < BM) {
+          bool v;
+          const int src = a_row_index<G1>(p, blk, BM, q, v);
+          if (F == F_FP8) {
+            scg[i] = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s) + ((size_t)src * kblocks) * 4;
+            sc_step[i] = 4;
+          } else {
+            scg[i] = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s) + (size_t)src * (K / 32);
+            sc_step[i] = 4;
+          }
+        } else {
+          const int lrow = q < BM + BNW ? q - BM : 0;
+          const int wr = weight_row(nt, lrow);
+          if (F == F_FP8) {
+            scg[i] = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s) +
+                     (((size_t)e * (erows / 128) + wr / 128) * kblocks) * 4;
+            sc_step[i] = 4;
+          } else {
+            scg[i] = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s) + ((size_t)e * erows + wr) * (K / 32);
+            sc_step[i] = 4;
+          }
+        }
       }
-    // MX: the A scale of lane (r, g) is that of row r of each fragment
-    int mx_arow[FM];
-    bool mx_aok[FM];
-    if (F == F_MX) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        bool v;
-        mx_arow[fm] = a_row_index<G1>(p, blk, BM, wm * (BM / 2) + fm * 16 + r, v);
-        mx_aok[fm] = v;
-      }
     }
-    // weight row of fragment fn, column r (for MX B scales) and the first
-    // weight row of each fragment (for FP8 block scales)
-    int frow[FN];
+    // copy step s into ring slot `slot`
+    auto issue = [&](int s, int slot) {
+      uint8_t* st = lds + slot * SSZ;
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      int lrow;  // row inside the tile
-      if (G1)
-        lrow = fn < FN / 2 ? wn * (BNW / 4) + fn * 16 : BNW / 2 + wn * (BNW / 4) + (fn - FN / 2) * 16;
-      else
-        lrow = wn * (BNW / 2) + fn * 16;
-      if (G1)
-        frow[fn] = lrow < BNW / 2 ? nt * (BNW / 2) + lrow : p.F + nt * (BNW / 2) + (lrow - BNW / 2);
-      else
-        frow[fn] = nt * BNW + lrow;
-    }
+      for (int i = 0; i < LA; ++i) g2lds16(ag[i] + (size_t)s * 128, st + (wave * (BM / 4) + 8 * i) * 128);
+#pragma unroll
+      for (int i = 0; i < LB; ++i)
+        g2lds16(bg[i] + (size_t)s * T::BROW, st + ASZ + (wave * LB + i) * (64 / CPRB) * T::BROW);
+#pragma unroll
+      for (int i = 0; i < LSC; ++i) g2lds4(scg[i] + (size_t)s * sc_step[i], st + ASZ + BSZ + (i * 4 + wave) * 256);
+    };
 
     f32x4_t acc[FM][FN];
 #pragma unroll
@@ -309,115 +358,93 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[A_CH], rb[B_CH];
-    auto gload = [&](int s) {
-      const int offa = s * 128;
-      const int offb = s * T::BROW;
+    __syncthreads();  // the previous tile is done with LDS
+    // Every step issues exactly one step of copies (the last D - 1 steps copy
+    // step nk - 1 again into ring slots that no later step reads), so the
+    // number of copies in flight is always (D - 1) * LS at the wait below and
+    // the compiler's own waits for the scale loads stay exact.
 #pragma unroll
-      for (int c = 0; c < A_CH; ++c) ra[c] = *reinterpret_cast<const uint4*>(ap[c] + offa);
-#pragma unroll
-      for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const uint4*>(bp[c] + offb);
-    };
-    auto sstore = [&](int buf) {
-      uint8_t* As = lds + buf * (ASZ + BSZ);
-      uint8_t* Bs = As + ASZ;
-#pragma unroll
-      for (int c = 0; c < A_CH; ++c) {
-        const int ch = tid + 256 * c;
-        uint4 v = ra[c];
-        if (!av[c]) v = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(As + (ch >> 3) * LDA + (ch & 7) * 16) = v;
-      }
-#pragma unroll
-      for (int c = 0; c < B_CH; ++c) {
-        const int ch = tid + 256 * c;
-        *reinterpret_cast<uint4*>(Bs + (ch / B_PR) * LDB + (ch % B_PR) * 16) = rb[c];
-      }
-    };
-
-    __syncthreads();  // the previous tile's last reads of LDS are done
-    gload(0);
-    sstore(0);
-    if (nk > 1) gload(1);
-    __syncthreads();
+    for (int s = 0; s < D; ++s) issue(s < nk ? s : nk - 1, s % NS);
 
     for (int s = 0; s < nk; ++s) {
-      if (s + 1 < nk) sstore((s + 1) & 1);
-      if (s + 2 < nk) gload(s + 2);
-      const uint8_t* As = lds + (s & 1) * (ASZ + BSZ);
+      wait_vm<(D - 1) * LS>();
+      barrier_no_fence();
+      issue(s + D < nk ? s + D : nk - 1, (s + D) % NS);
+
+      const uint8_t* As = lds + (s % NS) * SSZ;
       const uint8_t* Bs = As + ASZ;
+      const uint8_t* Ss = Bs + BSZ;  // scale words of the step
       if (F == F_BF16) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8_t af[FM], bfr[FN];
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm) af[fm] = ld_bf16_op(As + (wm * (BM / 2) + fm * 16 + r) * LDA, ks, g);
+          for (int fm = 0; fm < FM; ++fm) {
+            const int rr = wm * (BM / 2) + fm * 16 + r;
+            af[fm] = *reinterpret_cast<const bf16x8_t*>(As + rr * 128 + 16 * swz<8>(ks * 4 + g, rr));
+          }
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
-            const int lrow = G1 ? (fn < FN / 2 ? wn * (BNW / 4) + fn * 16 : BNW / 2 + wn * (BNW / 4) + (fn - FN / 2) * 16)
-                                : wn * (BNW / 2) + fn * 16;
-            bfr[fn] = ld_bf16_op(Bs + (lrow + r) * LDB, ks, g);
+            const int rr = frag_lrow(fn) + r;
+            bfr[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + rr * 128 + 16 * swz<8>(ks * 4 + g, rr));
           }
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn]);
         }
-      } else if (F == F_FP8) {
-        // fp32 block scales of this 128-wide K block
-        const float* xsf = static_cast<const float*>(G1 ? p.xs : p.act_s);
-        const int kblocks = K / 128;
+      } else {
+        i32x8_t af[FM];
         float as_[FM][4];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) as_[fm][i] = xsf[(size_t)arow_src[fm][i] * kblocks + s];
-        const float* wsf = static_cast<const float*>(G1 ? p.w13_s : p.w2_s);
-        const size_t erows_blk = G1 ? (size_t)(2 * p.F / 128) : (size_t)(p.H / 128);
-        i32x8_t af[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) af[fm] = ld_f8_op(As + (wm * (BM / 2) + fm * 16 + r) * LDA, g);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int lrow = G1 ? (fn < FN / 2 ? wn * (BNW / 4) + fn * 16 : BNW / 2 + wn * (BNW / 4) + (fn - FN / 2) * 16)
-                              : wn * (BNW / 2) + fn * 16;
-          const i32x8_t bfr = ld_f8_op(Bs + (lrow + r) * LDB, g);
-          const float wsc = wsf[((size_t)e * erows_blk + frow[fn] / 128) * kblocks + s];
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
-            const f32x4_t t = mfma_f8(af[fm], bfr);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[fm][fn][i] = __builtin_fmaf(t[i], as_[fm][i] * wsc, acc[fm][fn][i]);
-          }
-        }
-      } else {  // F_MX
-        const uint8_t* xse = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s);
-        const uint8_t* wse = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s);
-        const int sblocks = K / 32;
-        const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
-        i32x8_t af[FM];
         int sa[FM];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-          af[fm] = ld_f8_op(As + (wm * (BM / 2) + fm * 16 + r) * LDA, g);
-          sa[fm] = mx_aok[fm] ? (int)xse[(size_t)mx_arow[fm] * sblocks + s * 4 + g] : 127;
+          if (F == F_FP8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              as_[fm][i] = reinterpret_cast<const float*>(Ss)[wm * (BM / 2) + fm * 16 + 4 * g + i];
+          } else {
+            sa[fm] = (int)Ss[(wm * (BM / 2) + fm * 16 + r) * 4 + g];
+          }
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int rr = wm * (BM / 2) + fm * 16 + r;
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(As + rr * 128 + 16 * swz<8>(g, rr));
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(As + rr * 128 + 16 * swz<8>(4 + g, rr));
+          af[fm] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          const int lrow = G1 ? (fn < FN / 2 ? wn * (BNW / 4) + fn * 16 : BNW / 2 + wn * (BNW / 4) + (fn - FN / 2) * 16)
-                              : wn * (BNW / 2) + fn * 16;
-          const i32x8_t bfr = ld_f4_op(Bs + (lrow + r) * LDB, g);
-          const int sb = (int)wse[((size_t)e * erows + frow[fn] + r) * sblocks + s * 4 + g];
+          const int rr = frag_lrow(fn) + r;
+          if (F == F_FP8) {
+            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(Bs + rr * 128 + 16 * swz<8>(g, rr));
+            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(Bs + rr * 128 + 16 * swz<8>(4 + g, rr));
+            const i32x8_t bfr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const float wsc = reinterpret_cast<const float*>(Ss)[BM + frag_lrow(fn)];
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = mfma_mx(af[fm], bfr, acc[fm][fn], sa[fm], sb);
+            for (int fm = 0; fm < FM; ++fm) {
+              const f32x4_t t = mfma_f8(af[fm], bfr);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[fm][fn][i] = __builtin_fmaf(t[i], as_[fm][i] * wsc, acc[fm][fn][i]);
+            }
+          } else {
+            const i32x4_t v = *reinterpret_cast<const i32x4_t*>(Bs + rr * 64 + 16 * swz<4>(g, rr));
+            const i32x8_t bfr = {v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+            const int sb = (int)Ss[(BM + rr) * 4 + g];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = mfma_mx(af[fm], bfr, acc[fm][fn], sa[fm], sb);
+          }
         }
       }
-      __syncthreads();
     }
+    __syncthreads();  // every wave is done reading the stage buffers
 
     // ---------------------------------------------------------------- epilogue
     if (G1) {
-      constexpr int FA = FN / 2;  // SwiGLU fragments of this wave
+      constexpr int FA = FN / 2;
+      constexpr int BNA = BNW / 2;
       float v[FM][FA][4];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -425,22 +452,19 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
         for (int fa = 0; fa < FA; ++fa)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[fm][fa][i] = swiglu(acc[fm][fa][i], acc[fm][fa + FA][i]);
-      const int col0 = nt * (BNW / 2) + wn * (BNW / 4);  // first SwiGLU column of this wave
+      const int lcol0 = wn * (BNA / 2);  // first tile column of this wave
       if (F == F_BF16) {
-        uint16_t* act = reinterpret_cast<uint16_t*>(p.act);
+        uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BM][BNA]
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = blk * BM + wm * (BM / 2) + fm * 16 + 4 * g + i;
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int fa = 0; fa < FA; ++fa)
-              act[(size_t)row * p.F + col0 + fa * 16 + r] = (uint16_t)f32_to_bf16_bits(v[fm][fa][i]);
-          }
+              st[(wm * (BM / 2) + fm * 16 + 4 * g + i) * BNA + lcol0 + fa * 16 + r] =
+                  (uint16_t)f32_to_bf16_bits(v[fm][fa][i]);
       } else if (F == F_FP8) {
-        // amax over the tile's BNW/2 = 128 columns of each row (two waves)
-        float* xch = reinterpret_cast<float*>(lds);  // [2][BM]
-        float m[FM][4];
+        float* xch = reinterpret_cast<float*>(lds + BM * BNA);  // [2][BM] after the byte tile
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -450,7 +474,6 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
             for (int fa = 0; fa < FA; ++fa) mm = fmaxf(mm, fabsf(v[fm][fa][i]));
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
-            m[fm][i] = mm;
             if (r == 0) xch[wn * BM + wm * (BM / 2) + fm * 16 + 4 * g + i] = mm;
           }
         __syncthreads();
@@ -463,20 +486,18 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
             const float amax = fmaxf(xch[lr], xch[BM + lr]);
             const float sc = amax > 0.f ? amax / 448.f : 1.f;
             const float inv = 1.f / sc;
-            const int row = blk * BM + lr;
-            if (wn == 0 && r == 0) act_s[(size_t)row * (p.F / 128) + nt] = sc;
+            if (wn == 0 && r == 0) act_s[(size_t)(blk * BM + lr) * (p.F / 128) + nt] = sc;
 #pragma unroll
             for (int fa = 0; fa < FA; ++fa)
-              p.act[(size_t)row * p.F + col0 + fa * 16 + r] = (uint8_t)to_e4m3(clamp448(v[fm][fa][i] * inv));
+              lds[lr * BNA + lcol0 + fa * 16 + r] = (uint8_t)to_e4m3(clamp448(v[fm][fa][i] * inv));
           }
-        __syncthreads();
       } else {  // F_MX: groups of 32 columns = fragment pairs of this wave
         uint8_t* act_s = static_cast<uint8_t*>(p.act_s);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int row = blk * BM + wm * (BM / 2) + fm * 16 + 4 * g + i;
+            const int lr = wm * (BM / 2) + fm * 16 + 4 * g + i;
 #pragma unroll
             for (int gp = 0; gp < FA / 2; ++gp) {
               float mm = fmaxf(fabsf(v[fm][2 * gp][i]), fabsf(v[fm][2 * gp + 1][i]));
@@ -484,27 +505,43 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
               for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
               const uint32_t c = e8m0_at_least(mm / 448.f);
               const float inv = e8m0_inv(c);
-              const int col = col0 + gp * 32;
-              if (r == 0) act_s[(size_t)row * (p.F / 32) + col / 32] = (uint8_t)c;
-              p.act[(size_t)row * p.F + col + r] = (uint8_t)to_e4m3(clamp448(v[fm][2 * gp][i] * inv));
-              p.act[(size_t)row * p.F + col + 16 + r] = (uint8_t)to_e4m3(clamp448(v[fm][2 * gp + 1][i] * inv));
+              const int lc = lcol0 + gp * 32;
+              if (r == 0) act_s[(size_t)(blk * BM + lr) * (p.F / 32) + (nt * BNA + lc) / 32] = (uint8_t)c;
+              lds[lr * BNA + lc + r] = (uint8_t)to_e4m3(clamp448(v[fm][2 * gp][i] * inv));
+              lds[lr * BNA + lc + 16 + r] = (uint8_t)to_e4m3(clamp448(v[fm][2 * gp + 1][i] * inv));
             }
           }
       }
+      __syncthreads();
+      // whole rows of the tile to act (BNA columns of 2 or 1 bytes)
+      constexpr int RB = BNA * T::AB;  // bytes per tile row
+      constexpr int CH = RB / 16;
+      for (int idx = tid; idx < BM * CH; idx += 256) {
+        const int lr = idx / CH;
+        const int c = idx % CH;
+        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * RB + c * 16);
+        *reinterpret_cast<uint4*>(p.act + ((size_t)(blk * BM + lr) * p.F + nt * BNA) * T::AB + c * 16) = val;
+      }
     } else {
+      uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BM][BNW]
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!arow_ok[fm][i]) continue;
-          const int row = blk * BM + wm * (BM / 2) + fm * 16 + 4 * g + i;
-          const int sid = p.sorted_ids[row];
-          if (sid >= p.A) continue;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
-            p.out[(size_t)sid * p.H + nt * BNW + wn * (BNW / 2) + fn * 16 + r] =
+            st[(wm * (BM / 2) + fm * 16 + 4 * g + i) * BNW + wn * (BNW / 2) + fn * 16 + r] =
                 (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
-        }
+      __syncthreads();
+      constexpr int CH = BNW * 2 / 16;
+      for (int idx = tid; idx < BM * CH; idx += 256) {
+        const int lr = idx / CH;
+        const int c = idx % CH;
+        const int sid = p.sorted_ids[blk * BM + lr];
+        if (sid >= p.A) continue;
+        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNW * 2 + c * 16);
+        *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
+      }
     }
   }
 }
@@ -681,11 +718,12 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmP p) {
   }
 }
 
-template <int F, bool G1, int BM, int BNW>
+template <int F, bool G1, int BM, int BNW, int NS>
 moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   using T = Tr<F>;
-  const size_t lds = 2 * ((size_t)BM * (128 + 16) + (size_t)BNW * (T::BROW + 16));
-  gemm_tiled<F, G1, BM, BNW><<<tile_grid(max_tiles, 512), 256, lds, s>>>(p);
+  const size_t sc = (F == F_BF16) ? 0 : (size_t)((BM + BNW + 255) / 256) * 1024;
+  const size_t lds = (size_t)NS * ((size_t)BM * 128 + (size_t)BNW * T::BROW + sc);
+  gemm_tiled<F, G1, BM, BNW, NS><<<tile_grid(max_tiles, 512), 256, lds, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -719,9 +757,9 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   }
   const int64_t t1 = mb * (a.F / 128), t2 = mb * (a.H / 128);
   switch (a.block_m) {
-    case 32: return which == 1 ? launch_tiled_one<F, true, 32, 256>(p, t1, s) : launch_tiled_one<F, false, 32, 128>(p, t2, s);
-    case 64: return which == 1 ? launch_tiled_one<F, true, 64, 256>(p, t1, s) : launch_tiled_one<F, false, 64, 128>(p, t2, s);
-    case 128: return which == 1 ? launch_tiled_one<F, true, 128, 256>(p, t1, s) : launch_tiled_one<F, false, 128, 128>(p, t2, s);
+    case 32: return which == 1 ? launch_tiled_one<F, true, 32, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 32, 128, 3>(p, t2, s);
+    case 64: return which == 1 ? launch_tiled_one<F, true, 64, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 64, 128, 3>(p, t2, s);
+    case 128: return which == 1 ? launch_tiled_one<F, true, 128, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 128, 128, 3>(p, t2, s);
   }
   return MOE_E_INVAL;
 }
