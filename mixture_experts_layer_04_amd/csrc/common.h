@@ -58,6 +58,33 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Wave reductions on DPP row operations (quad xor 1, quad xor 2, half-row
+// mirror, row mirror; afterwards every lane of a 16-lane row holds the row's
+// result) and v_readlane of the four rows.  The order of operations is fixed
+// (so sums are deterministic) and the result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__device__ __forceinline__ float wave_max_u(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_u(float v) {
+  v = v + dpp_f32<0xB1>(v);
+  v = v + dpp_f32<0x4E>(v);
+  v = v + dpp_f32<0x141>(v);
+  v = v + dpp_f32<0x140>(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {

@@ -28,25 +28,31 @@ struct FinP {
   int H, E, k;
 };
 
+template <int KT>  // = k
 __global__ __launch_bounds__(256) void finalize_kernel(FinP p) {
+  constexpr int KM = KT;
   const int t = blockIdx.x;
   const int32_t* ids = p.ids + (size_t)t * p.k;
   const float* w = p.w + (size_t)t * p.k;
   for (int h = threadIdx.x * 8; h < p.H; h += 256 * 8) {
+    // all k rows in flight at once, then added in slot order
+    uint4 o[KM];
+#pragma unroll
+    for (int j = 0; j < KM; ++j) o[j] = *reinterpret_cast<const uint4*>(p.out + ((size_t)t * KM + j) * p.H + h);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < p.k; ++j) {
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
       const int e = ids[j];
       if (e < 0 || e >= p.E) continue;
       const float wj = w[j];
-      const uint4 o = *reinterpret_cast<const uint4*>(p.out + ((size_t)t * p.k + j) * p.H + h);
-      acc[0] = __builtin_fmaf(wj, bf16_lo(o.x), acc[0]);
-      acc[1] = __builtin_fmaf(wj, bf16_hi(o.x), acc[1]);
-      acc[2] = __builtin_fmaf(wj, bf16_lo(o.y), acc[2]);
-      acc[3] = __builtin_fmaf(wj, bf16_hi(o.y), acc[3]);
-      acc[4] = __builtin_fmaf(wj, bf16_lo(o.z), acc[4]);
-      acc[5] = __builtin_fmaf(wj, bf16_hi(o.z), acc[5]);
-      acc[6] = __builtin_fmaf(wj, bf16_lo(o.w), acc[6]);
-      acc[7] = __builtin_fmaf(wj, bf16_hi(o.w), acc[7]);
+      acc[0] = __builtin_fmaf(wj, bf16_lo(o[j].x), acc[0]);
+      acc[1] = __builtin_fmaf(wj, bf16_hi(o[j].x), acc[1]);
+      acc[2] = __builtin_fmaf(wj, bf16_lo(o[j].y), acc[2]);
+      acc[3] = __builtin_fmaf(wj, bf16_hi(o[j].y), acc[3]);
+      acc[4] = __builtin_fmaf(wj, bf16_lo(o[j].z), acc[4]);
+      acc[5] = __builtin_fmaf(wj, bf16_hi(o[j].z), acc[5]);
+      acc[6] = __builtin_fmaf(wj, bf16_lo(o[j].w), acc[6]);
+      acc[7] = __builtin_fmaf(wj, bf16_hi(o[j].w), acc[7]);
     }
     uint4 v;
     v.x = pack_bf16x2(acc[0], acc[1]);
@@ -66,7 +72,14 @@ moe_status launch_finalize(const FfnArgs& a, hipStream_t s) {
   p.w = a.topk_weights;
   p.y = static_cast<uint16_t*>(a.y);
   p.H = a.H; p.E = a.E; p.k = a.k;
-  finalize_kernel<<<a.T, 256, 0, s>>>(p);
+  switch (a.k) {
+#define MOE_FIN(K) \
+  case K: finalize_kernel<K><<<a.T, 256, 0, s>>>(p); break;
+    MOE_FIN(1) MOE_FIN(2) MOE_FIN(3) MOE_FIN(4) MOE_FIN(5) MOE_FIN(6) MOE_FIN(7) MOE_FIN(8)
+    MOE_FIN(9) MOE_FIN(10) MOE_FIN(11) MOE_FIN(12) MOE_FIN(13) MOE_FIN(14) MOE_FIN(15) MOE_FIN(16)
+#undef MOE_FIN
+    default: return MOE_E_INVAL;
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -91,7 +104,7 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
 
 namespace {
 struct Layout {
-  size_t xq, xs, act, act_s, out, total;
+  size_t xq, xs, act, act_s, act32, out, total;
 };
 Layout ffn_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
   Layout L;
@@ -107,6 +120,8 @@ Layout ffn_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
   off += align_up(mp * F * (q ? 1 : 2), 256);
   L.act_s = off;
   off += q ? align_up(mp * (F / 32) * sizeof(float), 256) : 0;
+  L.act32 = off;
+  off += (q && block_m == 16) ? align_up(mp * F * sizeof(float), 256) : 0;
   L.out = off;
   off += align_up((size_t)T * k * H * 2, 256);
   L.total = off;
@@ -125,6 +140,7 @@ void ffn_carve(FfnArgs& a, void* ws) {
   a.xs = b + L.xs;
   a.act = b + L.act;
   a.act_s = b + L.act_s;
+  a.act32 = b + L.act32;
   a.out = b + L.out;
 }
 

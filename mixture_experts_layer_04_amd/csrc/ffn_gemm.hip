@@ -34,10 +34,13 @@
 //  * the 16x16 fp32 result: lane l holds rows 4g .. 4g+3 of column l % 16.
 //
 // Two tile families:
-//  * BLOCK_M = 16 ("stream", decode): the weights are the traffic.  The 4
-//    waves of a workgroup split K into quarters and load operands straight
-//    into VGPRs (a weight element is used once); the quarters are reduced in
-//    LDS in a fixed order before the epilogue.
+//  * BLOCK_M = 16 ("stream", decode): the weights are the traffic.  Small
+//    tiles (16 or 32 weight rows) spread the weight bytes evenly over the
+//    CUs; the 8 waves of a workgroup split K, each loading several MFMA
+//    steps of operands straight into VGPRs before multiplying them (a weight
+//    element is used once); the partial tiles are added in LDS in a fixed
+//    order.  For FP8 / MX the fp32 SwiGLU rows are requantised by a second,
+//    row-parallel kernel.
 //  * BLOCK_M >= 32 ("tiled", prefill): 2 x 2 waves, A (BLOCK_M rows) and B
 //    tiles copied straight into a 3-stage LDS ring two K steps (128 bytes of
 //    K per row each) ahead of the multiply; one barrier per step; the output
@@ -45,6 +48,8 @@
 // Tiles are visited in a grid-stride loop bounded by the padded length read
 // on the device (no workgroup is launched for blocks that do not exist), in
 // an order that keeps the blocks sharing a weight tile on one XCD.
+
+#include <cmath>
 
 #include "common.h"
 #include "launch.h"
@@ -67,6 +72,7 @@ struct GemmP {
   const int32_t* npp;
   uint8_t* act;           // [max_padded, F] bf16 or e4m3
   void* act_s;            // fp32 [max_padded, F/128] (FP8) or e8m0 [max_padded, F/32] (MX)
+  float* act32;           // BLOCK_M 16, FP8 / MX: fp32 SwiGLU rows [max_padded, F]
   uint16_t* out;          // [T*k, H] bf16
   int H, F, k, A;
 };
@@ -547,33 +553,88 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
 }
 
 // ---------------------------------------------------------------------------
-// Stream kernel (BLOCK_M = 16).  Tile: 16 rows x BNA SwiGLU columns (GEMM1:
-// BNA gate + BNA up weight rows; BNA = 16 / 128 / 32 for BF16 / FP8 / MX so
-// that a requantisation group lies inside one tile) or 16 rows x 16 output
-// columns (GEMM2).  The 4 waves split K into quarters.
-template <int F, bool G1>
-__global__ __launch_bounds__(256) void gemm_stream(GemmP p) {
-  using T = Tr<F>;
-  constexpr int BM = 16;
-  constexpr int BNA = G1 ? T::BNA_STREAM : 16;   // output columns per tile
-  constexpr int FN = G1 ? 2 * BNA / 16 : 1;       // weight fragments per wave
-  constexpr int NCOL = FN * 16;                   // weight rows per tile
-  extern __shared__ float red_lds[];              // [4][BM][NCOL + 1]
-  auto red = reinterpret_cast<float(*)[BM][NCOL + 1]>(red_lds);
-  const int wave = threadIdx.x >> 6;
+// Stream kernel (BLOCK_M = 16, decode).  A weight element is used by at most
+// the 16 rows of one block, so the kernel is a weight stream: what decides
+// its speed is that every CU gets an even share of the weight bytes and keeps
+// enough of them in flight.
+//
+// Tile: 16 padded rows x NC = 16 * FN weight rows.  GEMM1: FN = 1 holds 8
+// gate rows (C columns 0-7) and the matching 8 up rows (C columns 8-15); an
+// even FN holds FN/2 fragments of gate rows, then FN/2 of up rows; either way
+// SwiGLU column j of the tile takes gate column j and up column NC/2 + j.
+// GEMM2: NC output columns.  The 8 waves of a workgroup split the K steps
+// (one MFMA each) into 8 near-equal contiguous runs; a wave issues the loads
+// of S steps at once, then multiplies them (the other waves of the SIMD keep
+// the memory pipe busy meanwhile).  A rows of padding slots are not loaded.
+// The 8 partial tiles are added in LDS in wave order.  GEMM1 writes SwiGLU
+// rows as bf16 (BF16) or fp32 (FP8, MX: their requantisation groups span
+// several tiles, so requant_act_kernel quantises the rows afterwards).
+template <int F>
+struct SOp;
+template <>
+struct SOp<F_BF16> {
+  using A = bf16x8_t;
+  using B = bf16x8_t;
+  static constexpr int SK = 32;  // K elements per MFMA step
+  static constexpr int S = 8;    // steps loaded at once
+};
+template <>
+struct SOp<F_FP8> {
+  using A = i32x8_t;
+  using B = i32x8_t;
+  static constexpr int SK = 128;
+  static constexpr int S = 4;
+};
+template <>
+struct SOp<F_MX> {
+  using A = i32x8_t;
+  using B = i32x4_t;
+  static constexpr int SK = 128;
+  static constexpr int S = 4;
+};
+
+// Steps loaded at once: SOp::S, halved for FP8 with 4 fragments (VGPRs).
+template <int F, int FN>
+constexpr int stream_steps() {
+  return (F == F_FP8 && FN == 4) ? SOp<F>::S / 2 : SOp<F>::S;
+}
+
+template <int F, int FN, int S>
+struct SChunk {
+  typename SOp<F>::A a[S];
+  typename SOp<F>::B b[FN][S];
+  float as[S][4];   // FP8: A scales of C rows 4g .. 4g+3
+  float ws[FN][S];  // FP8: weight block scale of this lane's C column
+  int sa[S];        // MX: e8m0 of A row r, K block g
+  int sb[FN][S];    // MX: e8m0 of weight row r, K block g
+};
+
+constexpr int kStreamWaves = 8;
+
+template <int F, bool G1, int FN>
+__global__ __launch_bounds__(512) void gemm_stream(GemmP p) {
+  using O = SOp<F>;
+  constexpr int SK = O::SK, S = stream_steps<F, FN>();
+  constexpr int NC = FN * 16;                // weight rows (C columns) per tile
+  constexpr int BNO = G1 ? NC / 2 : NC;      // output columns per tile
+  static_assert(!G1 || FN == 1 || FN % 2 == 0, "GEMM1 needs FN = 1 or even");
+  extern __shared__ float red_lds[];         // [kStreamWaves][16][NC + 1]
+  auto red = reinterpret_cast<float(*)[16][NC + 1]>(red_lds);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int K = G1 ? p.H : p.F;
   const int N = G1 ? p.F : p.H;
-  const int ntn = N / BNA;
-  const int nblk = *p.npp / BM;
+  const int ntn = N / BNO;
+  const int nblk = *p.npp / 16;
   const int64_t n_valid = (int64_t)nblk * ntn;
   const int64_t per = (n_valid + 7) >> 3;
-  const int kq = K / 4;                         // elements per wave
-  const int nsteps = kq / T::KSTEP;
-  const int rowbytes_a = K * T::AB;
-  const int rowbytes_b = (F == F_MX) ? K / 2 : K * T::AB;
+  const int ks = K / SK;                                  // MFMA steps over K
+  const int st0 = wave * ks / kStreamWaves;               // this wave's steps [st0, st1)
+  const int nst = (wave + 1) * ks / kStreamWaves - st0;
+  const int rowbytes_a = K * (F == F_BF16 ? 2 : 1);
+  const int rowbytes_b = (F == F_MX) ? K / 2 : K * (F == F_BF16 ? 2 : 1);
   const uint8_t* asrc = G1 ? p.x : p.act;
   const uint8_t* wsrc = G1 ? p.w13 : p.w2;
   const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
@@ -584,77 +645,103 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmP p) {
     const int blk = (int)(L / ntn);
     const int nt = (int)(L % ntn);
     const int e = p.block_expert[blk];
-    bool aval;
-    const int asrc_row = a_row_index<G1>(p, blk, BM, r, aval);
-    const uint8_t* arow = asrc + (size_t)asrc_row * rowbytes_a;
-    int wrow[FN];
+    const int sid = p.sorted_ids[blk * 16 + r];
+    const bool aval = sid < p.A;
+    const int arow_i = G1 ? (aval ? sid / p.k : 0) : blk * 16 + r;
+    const uint8_t* arow = asrc + (size_t)arow_i * rowbytes_a;
+    size_t wr[FN];  // weight row (in [E * erows]) of this lane's C column, per fragment
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-      if (G1)
-        wrow[fn] = fn < FN / 2 ? nt * BNA + fn * 16 : p.F + nt * BNA + (fn - FN / 2) * 16;
+      int lrow;
+      if (G1 && FN == 1)
+        lrow = r < 8 ? nt * 8 + r : p.F + nt * 8 + (r - 8);
+      else if (G1)
+        lrow = fn < FN / 2 ? nt * BNO + fn * 16 + r : p.F + nt * BNO + (fn - FN / 2) * 16 + r;
       else
-        wrow[fn] = nt * 16;
+        lrow = nt * NC + fn * 16 + r;
+      wr[fn] = (size_t)e * erows + lrow;
     }
+    // FP8: A rows of the C rows 4g .. 4g+3 (their scales)
+    int orow[4];
+    bool ook[4];
+    if (F == F_FP8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s4 = p.sorted_ids[blk * 16 + 4 * g + i];
+        ook[i] = s4 < p.A;
+        orow[i] = G1 ? (ook[i] ? s4 / p.k : 0) : blk * 16 + 4 * g + i;
+      }
+    }
+
     f32x4_t acc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int k0 = wave * kq;  // first K element of this wave
 
-    if (F == F_BF16) {
-      for (int kk = 0; kk < kq; kk += 32) {
-        bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + (size_t)(k0 + kk + 8 * g) * 2);
-        if (!aval) a = bf16x8_t{};
+    for (int c0 = 0; c0 < nst; c0 += S) {
+      SChunk<F, FN, S> ch;
+      // ---- issue the loads of steps c0 .. c0 + S - 1
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const uint8_t* b = wsrc + ((size_t)e * erows + wrow[fn] + r) * rowbytes_b + (size_t)(k0 + kk + 8 * g) * 2;
-          acc[fn] = mfma_16x16x32_bf16(a, *reinterpret_cast<const bf16x8_t*>(b), acc[fn]);
+      for (int s = 0; s < S; ++s) {
+        if (c0 + s >= nst) break;
+        const int kb = st0 + c0 + s;  // global step index
+        if constexpr (F == F_BF16) {
+          if (aval)
+            ch.a[s] = *reinterpret_cast<const bf16x8_t*>(arow + (size_t)kb * 64 + g * 16);
+          else
+            ch.a[s] = bf16x8_t{};
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            ch.b[fn][s] = *reinterpret_cast<const bf16x8_t*>(wsrc + wr[fn] * rowbytes_b + (size_t)kb * 64 + g * 16);
+        } else if constexpr (F == F_FP8) {
+          const float* xsf = static_cast<const float*>(G1 ? p.xs : p.act_s);
+          const float* wsf = static_cast<const float*>(G1 ? p.w13_s : p.w2_s);
+          const int kblocks = K / 128;
+          if (aval)
+            ch.a[s] = ld_f8_op(arow + (size_t)kb * 128, g);
+          else
+            ch.a[s] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ch.as[s][i] = ook[i] ? xsf[(size_t)orow[i] * kblocks + kb] : 0.f;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            ch.b[fn][s] = ld_f8_op(wsrc + wr[fn] * rowbytes_b + (size_t)kb * 128, g);
+            const size_t wsrow = (wr[fn] / erows) * (erows / 128) + (wr[fn] % erows) / 128;
+            ch.ws[fn][s] = wsf[wsrow * kblocks + kb];
+          }
+        } else {
+          const uint8_t* xse = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s);
+          const uint8_t* wse = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s);
+          const int sblocks = K / 32;
+          if (aval) {
+            ch.a[s] = ld_f8_op(arow + (size_t)kb * 128, g);
+            ch.sa[s] = (int)xse[(size_t)arow_i * sblocks + kb * 4 + g];
+          } else {
+            ch.a[s] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            ch.sa[s] = 127;
+          }
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            ch.b[fn][s] = *reinterpret_cast<const i32x4_t*>(wsrc + wr[fn] * rowbytes_b + (size_t)kb * 64 + g * 16);
+            ch.sb[fn][s] = (int)wse[wr[fn] * sblocks + kb * 4 + g];
+          }
         }
       }
-    } else if (F == F_FP8) {
-      const float* xsf = static_cast<const float*>(G1 ? p.xs : p.act_s);
-      const float* wsf = static_cast<const float*>(G1 ? p.w13_s : p.w2_s);
-      const int kblocks = K / 128;
-      const size_t erows_blk = erows / 128;
-      // A row scales of this lane's 4 output rows
-      int orow[4];
-      bool ook[4];
+      // ---- multiply them, in K order
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bool v;
-        orow[i] = a_row_index<G1>(p, blk, BM, 4 * g + i, v);
-        ook[i] = v;
-      }
-      for (int st = 0; st < nsteps; ++st) {
-        const int kb = k0 / 128 + st;
-        i32x8_t a = ld_f8_op(arow + (size_t)kb * 128, g);
-        if (!aval) a = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        float as_[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) as_[i] = ook[i] ? xsf[(size_t)orow[i] * kblocks + kb] : 0.f;
+      for (int s = 0; s < S; ++s) {
+        if (c0 + s >= nst) break;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          const uint8_t* b = wsrc + ((size_t)e * erows + wrow[fn] + r) * rowbytes_b + (size_t)kb * 128;
-          const f32x4_t t = mfma_f8(a, ld_f8_op(b, g));
-          const float wsc = wsf[((size_t)e * erows_blk + wrow[fn] / 128) * kblocks + kb];
+          if constexpr (F == F_BF16) {
+            acc[fn] = mfma_16x16x32_bf16(ch.a[s], ch.b[fn][s], acc[fn]);
+          } else if constexpr (F == F_FP8) {
+            const f32x4_t t = mfma_f8(ch.a[s], ch.b[fn][s]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[fn][i] = __builtin_fmaf(t[i], as_[i] * wsc, acc[fn][i]);
-        }
-      }
-    } else {  // F_MX
-      const uint8_t* xse = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s);
-      const uint8_t* wse = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s);
-      const int sblocks = K / 32;
-      for (int st = 0; st < nsteps; ++st) {
-        const int kb = k0 / 128 + st;
-        i32x8_t a = ld_f8_op(arow + (size_t)kb * 128, g);
-        const int sa = aval ? (int)xse[(size_t)asrc_row * sblocks + kb * 4 + g] : 127;
-        if (!aval) a = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const size_t wr = (size_t)e * erows + wrow[fn] + r;
-          const i32x8_t b = ld_f4_op(wsrc + wr * rowbytes_b + (size_t)kb * 64, g);
-          const int sb = (int)wse[wr * sblocks + kb * 4 + g];
-          acc[fn] = mfma_mx(a, b, acc[fn], sa, sb);
+            for (int i = 0; i < 4; ++i) acc[fn][i] = __builtin_fmaf(t[i], ch.as[s][i] * ch.ws[fn][s], acc[fn][i]);
+          } else {
+            const i32x4_t v = ch.b[fn][s];
+            acc[fn] = mfma_mx(ch.a[s], i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0}, acc[fn], ch.sa[s], ch.sb[fn][s]);
+          }
         }
       }
     }
@@ -665,57 +752,112 @@ __global__ __launch_bounds__(256) void gemm_stream(GemmP p) {
       for (int i = 0; i < 4; ++i) red[wave][4 * g + i][fn * 16 + r] = acc[fn][i];
     __syncthreads();
 
-    // epilogue: 256 threads, 16 per row; each thread BNA / 16 columns
-    {
-      const int row = threadIdx.x >> 4;
-      const int c16 = threadIdx.x & 15;
+    // ---- epilogue: the 8 partial tiles added in wave order; valid rows only
+    for (int idx = threadIdx.x; idx < 16 * BNO; idx += 64 * kStreamWaves) {
+      const int row = idx / BNO;
+      const int col = idx % BNO;
+      const int rsid = p.sorted_ids[blk * 16 + row];
+      if (rsid >= p.A) continue;
       if (G1) {
-        constexpr int CPT = BNA / 16;  // SwiGLU columns per thread
-        float v[CPT];
-        float mm = 0.f;
+        float gs = red[0][row][col], us = red[0][row][BNO + col];
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-          const int col = c16 * CPT + j;  // column inside the tile
-          float gs = red[0][row][col], us = red[0][row][BNA + col];
-#pragma unroll
-          for (int w = 1; w < 4; ++w) {
-            gs += red[w][row][col];
-            us += red[w][row][BNA + col];
-          }
-          v[j] = swiglu(gs, us);
-          mm = fmaxf(mm, fabsf(v[j]));
+        for (int w = 1; w < kStreamWaves; ++w) {
+          gs += red[w][row][col];
+          us += red[w][row][BNO + col];
         }
-        const size_t prow = (size_t)blk * BM + row;
-        const int colg = nt * BNA + c16 * CPT;
-        if (F == F_BF16) {
-          reinterpret_cast<uint16_t*>(p.act)[prow * p.F + colg] = (uint16_t)f32_to_bf16_bits(v[0]);
-        } else {
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
-          float inv;
-          if (F == F_FP8) {
-            const float sc = mm > 0.f ? mm / 448.f : 1.f;
-            inv = 1.f / sc;
-            if (c16 == 0) static_cast<float*>(p.act_s)[prow * (p.F / 128) + nt] = sc;
-          } else {
-            const uint32_t c = e8m0_at_least(mm / 448.f);
-            inv = e8m0_inv(c);
-            if (c16 == 0) static_cast<uint8_t*>(p.act_s)[prow * (p.F / 32) + nt] = (uint8_t)c;
-          }
-#pragma unroll
-          for (int j = 0; j < CPT; ++j) p.act[prow * p.F + colg + j] = (uint8_t)to_e4m3(clamp448(v[j] * inv));
-        }
+        const float v = swiglu(gs, us);
+        const size_t o = (size_t)(blk * 16 + row) * p.F + nt * BNO + col;
+        if (F == F_BF16)
+          reinterpret_cast<uint16_t*>(p.act)[o] = (uint16_t)f32_to_bf16_bits(v);
+        else
+          p.act32[o] = v;
       } else {
-        float s0 = red[0][row][c16];
-        s0 += red[1][row][c16];
-        s0 += red[2][row][c16];
-        s0 += red[3][row][c16];
-        const int sid = p.sorted_ids[blk * BM + row];
-        if (sid < p.A) p.out[(size_t)sid * p.H + nt * 16 + c16] = (uint16_t)f32_to_bf16_bits(s0);
+        float s0 = red[0][row][col];
+#pragma unroll
+        for (int w = 1; w < kStreamWaves; ++w) s0 += red[w][row][col];
+        p.out[(size_t)rsid * p.H + nt * NC + col] = (uint16_t)f32_to_bf16_bits(s0);
       }
     }
     __syncthreads();
   }
+}
+
+// Requantisation of the fp32 SwiGLU rows the stream GEMM1 wrote (FP8: e4m3
+// with scale amax/448 per 128 columns; MX: e4m3 with the e8m0 scale
+// pow2_at_least(amax/448) per 32), valid padded rows only.  One workgroup per
+// row, each thread 8 consecutive columns.
+template <int F>
+__global__ __launch_bounds__(256) void requant_act_kernel(GemmP p) {
+  const int lane = threadIdx.x & 63;
+  const int nrows = *p.npp;
+  for (int row = blockIdx.x; row < nrows; row += gridDim.x) {
+    if (p.sorted_ids[row] >= p.A) continue;
+    for (int c = threadIdx.x * 8; c < p.F; c += 256 * 8) {
+      const float4 v0 = *reinterpret_cast<const float4*>(p.act32 + (size_t)row * p.F + c);
+      const float4 v1 = *reinterpret_cast<const float4*>(p.act32 + (size_t)row * p.F + c + 4);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+      constexpr int GL = (F == F_FP8) ? 16 : 4;  // lanes per scale group
+#pragma unroll
+      for (int off = 1; off < GL; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      float inv;
+      if (F == F_FP8) {
+        const float sc = m > 0.f ? m / 448.f : 1.f;
+        inv = 1.f / sc;
+        if ((lane & 15) == 0) static_cast<float*>(p.act_s)[(size_t)row * (p.F / 128) + c / 128] = sc;
+      } else {
+        const uint32_t code = e8m0_at_least(m / 448.f);
+        inv = e8m0_inv(code);
+        if ((lane & 3) == 0) static_cast<uint8_t*>(p.act_s)[(size_t)row * (p.F / 32) + c / 32] = (uint8_t)code;
+      }
+      uint2 q;
+      q.x = pack4_e4m3(clamp448(f[0] * inv), clamp448(f[1] * inv), clamp448(f[2] * inv), clamp448(f[3] * inv));
+      q.y = pack4_e4m3(clamp448(f[4] * inv), clamp448(f[5] * inv), clamp448(f[6] * inv), clamp448(f[7] * inv));
+      *reinterpret_cast<uint2*>(p.act + (size_t)row * p.F + c) = q;
+    }
+  }
+}
+
+// Fragments per tile for the stream kernels: the widest tile (fewest re-reads
+// of the A rows) that still leaves >= 2048 tiles (8 per CU) for the expected
+// number of experts touched, E (1 - (1 - k/E)^T).
+int stream_fn(int T, int k, int E, int N, bool g1) {
+  const double touched = E * (1.0 - std::pow(1.0 - (double)k / E, (double)T));
+  const int fns[3] = {4, 2, 1};
+  for (int fn : fns) {
+    const int bno = g1 ? fn * 8 : fn * 16;
+    if (N % bno == 0 && touched * (N / bno) >= 2048.0) return fn;
+  }
+  return 1;
+}
+
+// Workgroups of `kernel` that fit on the current device at once (CUs x
+// occupancy), as a multiple of 8.  `cache` (one per kernel, indexed by
+// device) keeps the answer.
+int resident_wgs(const void* kernel, int threads, size_t lds, int* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    cache[dev] = (cus * per_cu + 7) / 8 * 8;
+  }
+  return cache[dev];
+}
+
+template <int F, bool G1, int FN>
+void launch_stream_one(const GemmP& p, int64_t max_blocks, int N, hipStream_t s) {
+  constexpr int BNO = G1 ? FN * 8 : FN * 16;
+  const size_t lds = (size_t)kStreamWaves * 16 * (FN * 16 + 1) * sizeof(float);
+  // every workgroup resident at once: a workgroup that finds no tile exits
+  // at once instead of holding a slot that a tile could use
+  static int cache[64] = {0};
+  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_stream<F, G1, FN>), 64 * kStreamWaves, lds, cache);
+  gemm_stream<F, G1, FN><<<tile_grid(max_blocks * (N / BNO), wgs), 64 * kStreamWaves, lds, s>>>(p);
 }
 
 template <int F, bool G1, int BM, int BNW, int NS>
@@ -743,16 +885,28 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   p.npp = a.num_post_padded;
   p.act = static_cast<uint8_t*>(a.act);
   p.act_s = a.act_s;
+  p.act32 = static_cast<float*>(a.act32);
   p.out = static_cast<uint16_t*>(a.out);
   p.H = a.H; p.F = a.F; p.k = a.k; p.A = a.T * a.k;
   const int64_t mb = align_max_blocks(a.T, a.k, a.E, a.block_m);
   if (a.block_m == 16) {
-    constexpr int NCOL1 = 2 * Tr<F>::BNA_STREAM;
-    if (which == 1)
-      gemm_stream<F, true><<<tile_grid(mb * (a.F / Tr<F>::BNA_STREAM), 2048), 256, 4 * 16 * (NCOL1 + 1) * 4, s>>>(p);
-    else
-      gemm_stream<F, false><<<tile_grid(mb * (a.H / 16), 2048), 256, 4 * 16 * (16 + 1) * 4, s>>>(p);
-    MOE_CHECK_LAUNCH();
+    const int N = which == 1 ? a.F : a.H;
+    const int fn = stream_fn(a.T, a.k, a.E, N, which == 1);
+    if (which == 1) {
+      if (fn == 4) launch_stream_one<F, true, 4>(p, mb, N, s);
+      else if (fn == 2) launch_stream_one<F, true, 2>(p, mb, N, s);
+      else launch_stream_one<F, true, 1>(p, mb, N, s);
+      MOE_CHECK_LAUNCH();
+      if (F != F_BF16) {
+        requant_act_kernel<F><<<tile_grid(align_max_padded(a.T, a.k, a.E, 16), 4096), 256, 0, s>>>(p);
+        MOE_CHECK_LAUNCH();
+      }
+    } else {
+      if (fn == 4) launch_stream_one<F, false, 4>(p, mb, N, s);
+      else if (fn == 2) launch_stream_one<F, false, 2>(p, mb, N, s);
+      else launch_stream_one<F, false, 1>(p, mb, N, s);
+      MOE_CHECK_LAUNCH();
+    }
     return MOE_OK;
   }
   const int64_t t1 = mb * (a.F / 128), t2 = mb * (a.H / 128);

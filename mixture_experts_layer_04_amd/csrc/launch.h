@@ -54,6 +54,7 @@ struct FfnArgs {
   void* xs;        // its scales
   void* act;       // SwiGLU output [max_padded, F]
   void* act_s;     // its scales (fp8 formats)
+  void* act32;     // BLOCK_M 16 with fp8 formats: fp32 SwiGLU rows before requantisation
   void* out;       // expert outputs [T*k, H] bf16
 };
 

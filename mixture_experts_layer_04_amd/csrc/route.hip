@@ -95,7 +95,9 @@ __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t& a, const bf16x8_t& bh, 
 }
 
 // Selection for one token from its E fp32 logits (l[s] = logit of expert
-// s*64 + lane, -inf past E); writes ids / weights of token t.
+// s*64 + lane, -inf past E); writes ids / weights of token t.  Every
+// arg-max is a wave max of the keys (DPP) followed by one ballot per slot
+// for the lowest expert id holding that key.
 template <int SLOTS>
 __device__ __forceinline__ void select_token(const RouteParams& p, int t, const float (&l)[SLOTS]) {
   const int lane = threadIdx.x & 63;
@@ -109,14 +111,14 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
     float m = NEG_INF;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) m = fmaxf(m, l[s]);
-    m = wave_max(m);
+    m = wave_max_u(m);
     float part = 0.f;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       sc[s] = ok[s] ? expf(l[s] - m) : 0.f;
       part += sc[s];
     }
-    const float inv = 1.f / wave_sum(part);
+    const float inv = 1.f / wave_sum_u(part);
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       sc[s] = sc[s] * inv;
@@ -133,70 +135,77 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
   }
 
   if (p.n_group > 1) {
-    // group score = sum of the two largest rank keys of the group
+    // group score = sum of the two largest rank keys of the group (a tie at
+    // the top counts twice)
     const int gsize = p.E / p.n_group;
+    int grp[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) grp[s] = ok[s] ? (s * kWave + lane) / gsize : -1;
     float my_gs = NEG_INF;
     for (int g = 0; g < p.n_group; ++g) {
-      float t1 = NEG_INF, t2 = NEG_INF;
+      float v = NEG_INF;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s)
+        if (grp[s] == g) v = fmaxf(v, key[s]);
+      const float t1 = wave_max_u(v);
+      int drop = -1;  // lowest expert of the group holding t1
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
-        const int e = s * kWave + lane;
-        if (ok[s] && e / gsize == g) {
-          const float v = key[s];
-          if (v > t1) { t2 = t1; t1 = v; } else if (v > t2) { t2 = v; }
-        }
+        const uint64_t b = __ballot(grp[s] == g && key[s] == t1);
+        if (drop < 0 && b != 0) drop = s * kWave + __ffsll((unsigned long long)b) - 1;
       }
+      float v2 = NEG_INF;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float o1 = __shfl_xor(t1, off, kWave);
-        const float o2 = __shfl_xor(t2, off, kWave);
-        const float n1 = fmaxf(t1, o1);
-        const float n2 = fmaxf(fminf(t1, o1), fmaxf(t2, o2));
-        t1 = n1; t2 = n2;
-      }
+      for (int s = 0; s < SLOTS; ++s)
+        if (grp[s] == g && s * kWave + lane != drop) v2 = fmaxf(v2, key[s]);
+      const float t2 = wave_max_u(v2);
       if (lane == g) my_gs = t1 + t2;
     }
     // keep the topk_group best groups, lowest group id on ties
     uint64_t kept = 0;
     bool g_used = lane >= p.n_group;
     for (int r = 0; r < p.topk_group; ++r) {
-      uint64_t v = g_used ? 0ull
-                          : (((uint64_t)f32_order_key(my_gs) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)lane));
-      v = wave_max_u64(v);
-      const int g = (int)(0xFFFFFFFFu - (uint32_t)v);
+      const float m = wave_max_u(g_used ? NEG_INF : my_gs);
+      const uint64_t b = __ballot(!g_used && my_gs == m);
+      const int g = b != 0 ? __ffsll((unsigned long long)b) - 1 : 0;
       kept |= 1ull << g;
       if (lane == g) g_used = true;
     }
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const int e = s * kWave + lane;
-      if (ok[s] && !((kept >> (e / gsize)) & 1ull)) ok[s] = false;
-    }
+    for (int s = 0; s < SLOTS; ++s)
+      if (ok[s] && !((kept >> grp[s]) & 1ull)) ok[s] = false;
   }
 
-  // k rounds of wave arg-max on (key descending, id ascending)
+  // k rounds of arg-max on (key descending, id ascending)
   int sel_id = 0;
   float sel_s = 0.f;
   for (int j = 0; j < p.k; ++j) {
-    uint64_t best = 0;
-    float best_s = 0.f;
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const uint32_t e = (uint32_t)(s * kWave + lane);
-      const uint64_t v = ((uint64_t)f32_order_key(key[s]) << 32) | (0xFFFFFFFFu - e);
-      if (ok[s] && v > best) { best = v; best_s = sc[s]; }
-    }
-    const uint64_t w = wave_max_u64(best);
-    const int id = (int)(0xFFFFFFFFu - (uint32_t)w);
-    const float s_w = __shfl(best_s, id & 63, kWave);
+    float v = NEG_INF;
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s)
-      if (s * kWave + lane == id) ok[s] = false;
+      if (ok[s]) v = fmaxf(v, key[s]);
+    const float m = wave_max_u(v);
+    int id = -1;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      const uint64_t b = __ballot(ok[s] && key[s] == m);
+      if (id < 0 && b != 0) id = s * kWave + __ffsll((unsigned long long)b) - 1;
+    }
+    if (id < 0) id = 0;  // not reached: at least k experts stay allowed
+    const int sl = id >> 6, ln = id & 63;
+    float sv = sc[0];
+#pragma unroll
+    for (int s = 1; s < SLOTS; ++s)
+      if (s == sl) sv = sc[s];
+    const float s_w = readlane_f32(sv, ln);
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+      if (s == sl && lane == ln) ok[s] = false;
     if (lane == j) { sel_id = id; sel_s = s_w; }
   }
   float wgt = sel_s;
   if (p.renorm) {
-    const float sum = wave_sum(lane < p.k ? sel_s : 0.f);
+    const float sum = wave_sum_u(lane < p.k ? sel_s : 0.f);
     wgt = sel_s / (sum + 1e-20f);
   }
   wgt *= p.scale;
