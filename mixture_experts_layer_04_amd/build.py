@@ -25,7 +25,12 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-I", INCLUDE, "-I", CSRC,
+    "-munsafe-fp-atomics",
+    # matrix-core accumulators in VGPRs: in the AGPR form the register
+    # allocator copies the tiled GEMMs' accumulators between the two files on
+    # every K step
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-I", INCLUDE, "-I", CSRC,
 ]
 
 

@@ -101,6 +101,31 @@ struct Tr<F_MX> {
   static constexpr int BNA_STREAM = 32;
 };
 
+// MFMA operand types and K per instruction of each format.
+template <int F>
+struct SOp;
+template <>
+struct SOp<F_BF16> {
+  using A = bf16x8_t;
+  using B = bf16x8_t;
+  static constexpr int SK = 32;  // K elements per MFMA step
+  static constexpr int S = 8;    // steps loaded at once
+};
+template <>
+struct SOp<F_FP8> {
+  using A = i32x8_t;
+  using B = i32x8_t;
+  static constexpr int SK = 128;
+  static constexpr int S = 4;
+};
+template <>
+struct SOp<F_MX> {
+  using A = i32x8_t;
+  using B = i32x4_t;
+  static constexpr int SK = 128;
+  static constexpr int S = 4;
+};
+
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
 // e4m3 (OCP) of v, v already within [-448, 448]; round to nearest even
@@ -569,30 +594,6 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
 // The 8 partial tiles are added in LDS in wave order.  GEMM1 writes SwiGLU
 // rows as bf16 (BF16) or fp32 (FP8, MX: their requantisation groups span
 // several tiles, so requant_act_kernel quantises the rows afterwards).
-template <int F>
-struct SOp;
-template <>
-struct SOp<F_BF16> {
-  using A = bf16x8_t;
-  using B = bf16x8_t;
-  static constexpr int SK = 32;  // K elements per MFMA step
-  static constexpr int S = 8;    // steps loaded at once
-};
-template <>
-struct SOp<F_FP8> {
-  using A = i32x8_t;
-  using B = i32x8_t;
-  static constexpr int SK = 128;
-  static constexpr int S = 4;
-};
-template <>
-struct SOp<F_MX> {
-  using A = i32x8_t;
-  using B = i32x4_t;
-  static constexpr int SK = 128;
-  static constexpr int S = 4;
-};
-
 // Steps loaded at once: SOp::S, halved for FP8 with 4 fragments (VGPRs).
 template <int F, int FN>
 constexpr int stream_steps() {

@@ -99,7 +99,8 @@ __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t& a, const bf16x8_t& bh, 
 // arg-max is a wave max of the keys (DPP) followed by one ballot per slot
 // for the lowest expert id holding that key.
 template <int SLOTS>
-__device__ __forceinline__ void select_token(const RouteParams& p, int t, const float (&l)[SLOTS]) {
+__device__ __forceinline__ void select_token(const RouteParams& p, int t, const float (&l)[SLOTS],
+                                             const float (&bv)[SLOTS]) {
   const int lane = threadIdx.x & 63;
   float key[SLOTS], sc[SLOTS];
   bool ok[SLOTS];
@@ -128,9 +129,9 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int e = s * kWave + lane;
+      (void)e;
       sc[s] = 1.f / (1.f + expf(-l[s]));
-      const float b = (p.bias != nullptr && ok[s]) ? p.bias[e] : 0.f;
-      key[s] = ok[s] ? sc[s] + b : NEG_INF;
+      key[s] = ok[s] ? sc[s] + bv[s] : NEG_INF;
     }
   }
 
@@ -176,31 +177,35 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
       if (ok[s] && !((kept >> grp[s]) & 1ull)) ok[s] = false;
   }
 
-  // k rounds of arg-max on (key descending, id ascending)
+  // k rounds of arg-max on (key descending, id ascending); an expert that is
+  // not allowed or already taken has key -inf (every allowed key is finite)
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s)
+    if (!ok[s]) key[s] = NEG_INF;
   int sel_id = 0;
   float sel_s = 0.f;
   for (int j = 0; j < p.k; ++j) {
-    float v = NEG_INF;
+    float v = key[0];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
-      if (ok[s]) v = fmaxf(v, key[s]);
+    for (int s = 1; s < SLOTS; ++s) v = fmaxf(v, key[s]);
     const float m = wave_max_u(v);
-    int id = -1;
+    int id = 0;
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const uint64_t b = __ballot(ok[s] && key[s] == m);
-      if (id < 0 && b != 0) id = s * kWave + __ffsll((unsigned long long)b) - 1;
+    for (int s = SLOTS - 1; s >= 0; --s) {  // the lowest slot with a hit wins
+      const uint64_t b = __ballot(key[s] == m);
+      if (b != 0) id = s * kWave + __ffsll((unsigned long long)b) - 1;
     }
-    if (id < 0) id = 0;  // not reached: at least k experts stay allowed
     const int sl = id >> 6, ln = id & 63;
     float sv = sc[0];
 #pragma unroll
     for (int s = 1; s < SLOTS; ++s)
       if (s == sl) sv = sc[s];
     const float s_w = readlane_f32(sv, ln);
+    if (lane == ln) {
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s)
-      if (s == sl && lane == ln) ok[s] = false;
+      for (int s = 0; s < SLOTS; ++s)
+        if (s == sl) key[s] = NEG_INF;
+    }
     if (lane == j) { sel_id = id; sel_s = s_w; }
   }
   float wgt = sel_s;
@@ -212,6 +217,17 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
   if (lane < p.k) {
     p.ids[(size_t)t * p.k + lane] = sel_id;
     p.weights[(size_t)t * p.k + lane] = wgt;
+  }
+}
+
+// Selection bias of the lane's experts (0 without a bias or past E).
+template <int SLOTS>
+__device__ __forceinline__ void load_bias(const RouteParams& p, float (&bv)[SLOTS]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int e = s * kWave + lane;
+    bv[s] = (p.bias != nullptr && e < p.E) ? p.bias[e] : 0.f;
   }
 }
 
@@ -285,19 +301,39 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p) {
   for (int tl = wave; tl < 16; tl += 4) {
     const int t = t0 + tl;
     if (t >= p.T) break;
+    float bv[SLOTS];
+    load_bias<SLOTS>(p, bv);
+    // logit = G_0 + G_1 + ... in order; the group sums are loaded 8 groups
+    // at a time (all in flight together) and then added
     float l[SLOTS];
+    int ec[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      ec[s] = min(s * kWave + lane, p.E - 1);
+      l[s] = p.part[(size_t)t * p.E + ec[s]];
+    }
+    for (int j0 = 1; j0 < p.NG; j0 += 8) {
+      float pv[8][SLOTS];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = min(j0 + u, p.NG - 1);
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) pv[u][s] = p.part[((size_t)jj * p.T + t) * p.E + ec[s]];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (j0 + u < p.NG) {
+#pragma unroll
+          for (int s = 0; s < SLOTS; ++s) l[s] += pv[u][s];
+        }
+    }
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
       const int e = s * kWave + lane;
-      float v = -__builtin_inff();
-      if (e < p.E) {
-        v = p.part[(size_t)t * p.E + e];
-        for (int jj = 1; jj < p.NG; ++jj) v += p.part[((size_t)jj * p.T + t) * p.E + e];
-        if (p.logits_out) p.logits_out[(size_t)t * p.E + e] = v;
-      }
-      l[s] = v;
+      if (e >= p.E) l[s] = -__builtin_inff();
+      else if (p.logits_out) p.logits_out[(size_t)t * p.E + e] = l[s];
     }
-    select_token<SLOTS>(p, t, l);
+    select_token<SLOTS>(p, t, l, bv);
   }
 }
 
@@ -426,13 +462,14 @@ __global__ __launch_bounds__(256) void route_select(RouteParams p, const float* 
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
-  float l[SLOTS];
+  float l[SLOTS], bv[SLOTS];
+  load_bias<SLOTS>(p, bv);
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     const int e = s * kWave + lane;
     l[s] = e < p.E ? logits[(size_t)t * p.E + e] : -__builtin_inff();
   }
-  select_token<SLOTS>(p, t, l);
+  select_token<SLOTS>(p, t, l, bv);
 }
 
 bool use_large(int T, int E) { (void)E; return T > SMALL_T_MAX; }
