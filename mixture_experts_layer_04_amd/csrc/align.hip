@@ -58,12 +58,25 @@ __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
   int* my = cnt + wave * E;
   for (int e = lane; e < E; e += 64) my[e] = 0;
   bool bad = false;
-  for (int a = a_begin + lane; a < a_end; a += 64) {
-    const int id = p.ids[a];
-    if (id >= 0 && id < E)
-      atomicAdd(&my[id], 1);
-    else if (id != -1)
-      bad = true;
+  // ids are read CH per lane at a time (all loads in flight together)
+  constexpr int CH = 16;
+  for (int a0 = a_begin; a0 < a_end; a0 += 64 * CH) {
+    int idv[CH];
+    const int nc = min(CH, (a_end - a0 + 63) >> 6);  // sub-chunks of 64 holding ids
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int a = a0 + 64 * c + lane;
+      idv[c] = (c < nc && a < a_end) ? p.ids[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c >= nc) break;
+      const int id = idv[c];
+      if (id >= 0 && id < E)
+        atomicAdd(&my[id], 1);
+      else if (id != -1)
+        bad = true;
+    }
   }
   if (__ballot(bad) != 0ull && lane == 0) atomicOr(p.err, 1);
   __syncthreads();
@@ -134,22 +147,33 @@ __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
 
   // stable placement
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int a0 = a_begin; a0 < a_end; a0 += 64) {
-    const int a = a0 + lane;
-    int id = (a < a_end) ? p.ids[a] : -1;
-    const bool valid = id >= 0 && id < E;
-    if (!valid) id = 0;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < p.nbits; ++b) {
-      const bool bit = (id >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+  for (int a1 = a_begin; a1 < a_end; a1 += 64 * CH) {
+    int idv[CH];
+    const int nc = min(CH, (a_end - a1 + 63) >> 6);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int a = a1 + 64 * c + lane;
+      idv[c] = (c < nc && a < a_end) ? p.ids[a] : -1;
     }
-    if (valid) {
-      const int rank = __popcll(m & lt);
-      const int pos = my[id] + rank;
-      p.sorted_ids[pos] = a;
-      if (rank == 0) my[id] += __popcll(m);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {  // 64 consecutive assignments at a time, in order
+      if (c >= nc) break;
+      const int a = a1 + 64 * c + lane;
+      int id = idv[c];
+      const bool valid = id >= 0 && id < E;
+      if (!valid) id = 0;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < p.nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const int rank = __popcll(m & lt);
+        const int pos = my[id] + rank;
+        p.sorted_ids[pos] = a;
+        if (rank == 0) my[id] += __popcll(m);
+      }
     }
   }
 }

@@ -231,6 +231,41 @@ __device__ __forceinline__ void load_bias(const RouteParams& p, float (&bv)[SLOT
   }
 }
 
+// logit of token t = G_0 + G_1 + ... (left to right) from the group sums
+// part[j][t][e]; -inf past E; also stored to logits_out if requested.  The
+// group sums are loaded 8 groups at a time (all in flight together).
+template <int SLOTS>
+__device__ __forceinline__ void sum_groups(const RouteParams& p, int t, float (&l)[SLOTS]) {
+  const int lane = threadIdx.x & 63;
+  int ec[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    ec[s] = min(s * kWave + lane, p.E - 1);
+    l[s] = p.part[(size_t)t * p.E + ec[s]];
+  }
+  for (int j0 = 1; j0 < p.NG; j0 += 8) {
+    float pv[8][SLOTS];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int jj = min(j0 + u, p.NG - 1);
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) pv[u][s] = p.part[((size_t)jj * p.T + t) * p.E + ec[s]];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < p.NG) {
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) l[s] += pv[u][s];
+      }
+  }
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const int e = s * kWave + lane;
+    if (e >= p.E) l[s] = -__builtin_inff();
+    else if (p.logits_out) p.logits_out[(size_t)t * p.E + e] = l[s];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token tiles.
 template <int SLOTS>
@@ -303,50 +338,24 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p) {
     if (t >= p.T) break;
     float bv[SLOTS];
     load_bias<SLOTS>(p, bv);
-    // logit = G_0 + G_1 + ... in order; the group sums are loaded 8 groups
-    // at a time (all in flight together) and then added
     float l[SLOTS];
-    int ec[SLOTS];
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      ec[s] = min(s * kWave + lane, p.E - 1);
-      l[s] = p.part[(size_t)t * p.E + ec[s]];
-    }
-    for (int j0 = 1; j0 < p.NG; j0 += 8) {
-      float pv[8][SLOTS];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int jj = min(j0 + u, p.NG - 1);
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s) pv[u][s] = p.part[((size_t)jj * p.T + t) * p.E + ec[s]];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (j0 + u < p.NG) {
-#pragma unroll
-          for (int s = 0; s < SLOTS; ++s) l[s] += pv[u][s];
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const int e = s * kWave + lane;
-      if (e >= p.E) l[s] = -__builtin_inff();
-      else if (p.logits_out) p.logits_out[(size_t)t * p.E + e] = l[s];
-    }
+    sum_groups<SLOTS>(p, t, l);
     select_token<SLOTS>(p, t, l, bv);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Prefill layout, first kernel: logits of a 64-token x 64-expert tile.
+// Prefill layout, first kernel: the group sum G_j of a 64-token x 64-expert
+// tile for one K group j (4 chunks of 128), written to part[j][t][e].
 // 4 waves as 2 x 2, each 32 tokens x 32 experts (2 x 2 fragments).  Per
 // 32-wide K step the 256 threads split the tile's 64 x 32 gate values once
-// into LDS planes (so each gate value is split once per 64 tokens) while the
-// next step's values are already in flight.
+// into LDS planes (each gate value is split once per 64 tokens); the gate
+// and x values of the next PF steps are in flight meanwhile.
 constexpr int LT = 64;  // tokens per tile
 constexpr int LE = 64;  // experts per tile
+constexpr int PF = 4;   // steps loaded ahead
 
-__global__ __launch_bounds__(256) void route_logits_tiled(RouteParams p, float* logits) {
+__global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t planes[LE * PROW];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -357,7 +366,9 @@ __global__ __launch_bounds__(256) void route_logits_tiled(RouteParams p, float* 
   const int q = lane >> 4;
   const int t0 = blockIdx.x * LT;
   const int e0 = blockIdx.y * LE;
-  const int nsteps = p.H / 32;
+  const int j = blockIdx.z;                     // K group
+  const int k0 = j * KCH * CPG;                 // first K of the group
+  const int nsteps = min(KCH * CPG, p.H - k0) / 32;
 
   // this thread's two float4 pieces of each K step: expert row (tid >> 3) and
   // (tid >> 3) + 32, K offset (tid & 7) * 4
@@ -365,83 +376,84 @@ __global__ __launch_bounds__(256) void route_logits_tiled(RouteParams p, float* 
   const int sk = (tid & 7) * 4;
   const bool sv0 = e0 + se < p.E;
   const bool sv1 = e0 + se + 32 < p.E;
-  const float* g0p = p.gate + (size_t)min(e0 + se, p.E - 1) * p.H + sk;
-  const float* g1p = p.gate + (size_t)min(e0 + se + 32, p.E - 1) * p.H + sk;
+  const float* g0p = p.gate + (size_t)min(e0 + se, p.E - 1) * p.H + k0 + sk;
+  const float* g1p = p.gate + (size_t)min(e0 + se + 32, p.E - 1) * p.H + k0 + sk;
   const uint16_t* xr[2];
   bool tv[2];
 #pragma unroll
   for (int tf = 0; tf < 2; ++tf) {
     const int t = t0 + wm * 32 + tf * 16 + r;
     tv[tf] = t < p.T;
-    xr[tf] = p.x + (size_t)(tv[tf] ? t : 0) * p.H + q * 8;
+    xr[tf] = p.x + (size_t)(tv[tf] ? t : 0) * p.H + k0 + q * 8;
   }
 
-  f32x4_t part[2][2], grp[2][2], tot[2][2];
+  f32x4_t part[2][2], grp[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       part[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       grp[a][b] = part[a][b];
-      tot[a][b] = part[a][b];
     }
 
-  float4 ng0 = *reinterpret_cast<const float4*>(g0p);
-  float4 ng1 = *reinterpret_cast<const float4*>(g1p);
-  bf16x8_t na[2];
+  // register ring of PF steps (past the last step: the last step again)
+  float4 rg0[PF], rg1[PF];
+  bf16x8_t rx[PF][2];
+  auto load = [&](int st, int slot) {
+    const int kb = min(st, nsteps - 1) * 32;
+    rg0[slot] = *reinterpret_cast<const float4*>(g0p + kb);
+    rg1[slot] = *reinterpret_cast<const float4*>(g1p + kb);
 #pragma unroll
-  for (int tf = 0; tf < 2; ++tf) na[tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf]);
+    for (int tf = 0; tf < 2; ++tf) rx[slot][tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
+  };
+#pragma unroll
+  for (int u = 0; u < PF; ++u) load(u, u);
 
-  for (int st = 0; st < nsteps; ++st) {
-    const float4 g0 = sv0 ? ng0 : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 g1 = sv1 ? ng1 : make_float4(0.f, 0.f, 0.f, 0.f);
-    bf16x8_t a[2];
+  for (int s0 = 0; s0 < nsteps; s0 += PF) {
 #pragma unroll
-    for (int tf = 0; tf < 2; ++tf) a[tf] = tv[tf] ? na[tf] : bf16x8_t{};
-    __syncthreads();  // the previous step's planes are consumed
-    {
-      uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
-      uint16_t* row = planes + se * PROW + sk;
-      split3(g0.x, h0, m0, l0); split3(g0.y, h1, m1, l1); split3(g0.z, h2, m2, l2); split3(g0.w, h3, m3, l3);
-      *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-      *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
-      *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-      row += 32 * PROW;
-      split3(g1.x, h0, m0, l0); split3(g1.y, h1, m1, l1); split3(g1.z, h2, m2, l2); split3(g1.w, h3, m3, l3);
-      *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-      *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
-      *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-    }
-    if (st + 1 < nsteps) {  // prefetch the next step
-      const int kb = (st + 1) * 32;
-      ng0 = *reinterpret_cast<const float4*>(g0p + kb);
-      ng1 = *reinterpret_cast<const float4*>(g1p + kb);
+    for (int u = 0; u < PF; ++u) {
+      const int st = s0 + u;
+      if (st >= nsteps) break;
+      const float4 g0 = sv0 ? rg0[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 g1 = sv1 ? rg1[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      bf16x8_t a[2];
 #pragma unroll
-      for (int tf = 0; tf < 2; ++tf) na[tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
-    }
-    __syncthreads();
+      for (int tf = 0; tf < 2; ++tf) a[tf] = tv[tf] ? rx[u][tf] : bf16x8_t{};
+      load(st + PF, u);
+      __syncthreads();  // the previous step's planes are consumed
+      {
+        uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+        uint16_t* row = planes + se * PROW + sk;
+        split3(g0.x, h0, m0, l0); split3(g0.y, h1, m1, l1); split3(g0.z, h2, m2, l2); split3(g0.w, h3, m3, l3);
+        *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
+        *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+        row += 32 * PROW;
+        split3(g1.x, h0, m0, l0); split3(g1.y, h1, m1, l1); split3(g1.z, h2, m2, l2); split3(g1.w, h3, m3, l3);
+        *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
+        *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+      }
+      __syncthreads();
 #pragma unroll
-    for (int ef = 0; ef < 2; ++ef) {
-      const uint16_t* pr = planes + (wn * 32 + ef * 16 + r) * PROW + q * 8;
-      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pr);
-      const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(pr + 32);
-      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pr + 64);
+      for (int ef = 0; ef < 2; ++ef) {
+        const uint16_t* pr = planes + (wn * 32 + ef * 16 + r) * PROW + q * 8;
+        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pr);
+        const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(pr + 32);
+        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pr + 64);
 #pragma unroll
-      for (int tf = 0; tf < 2; ++tf) part[tf][ef] = mfma3(a[tf], bh, bm, bl, part[tf][ef]);
-    }
-    if ((st & 3) == 3 || st == nsteps - 1) {  // end of a chunk
-      const int c = st >> 2;
-      const bool first_in_group = (c % CPG) == 0;
-      const bool end_of_group = (c % CPG) == CPG - 1 || st == nsteps - 1;
-      const bool first_group = c < CPG;
+        for (int tf = 0; tf < 2; ++tf) part[tf][ef] = mfma3(a[tf], bh, bm, bl, part[tf][ef]);
+      }
+      if ((st & 3) == 3 || st == nsteps - 1) {  // end of a chunk: G_j += P_c (P_c from zero)
+        const bool first = st < 4;
 #pragma unroll
-      for (int tf = 0; tf < 2; ++tf)
+        for (int tf = 0; tf < 2; ++tf)
 #pragma unroll
-        for (int ef = 0; ef < 2; ++ef) {
-          grp[tf][ef] = first_in_group ? part[tf][ef] : grp[tf][ef] + part[tf][ef];
-          part[tf][ef] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (end_of_group) tot[tf][ef] = first_group ? grp[tf][ef] : tot[tf][ef] + grp[tf][ef];
-        }
+          for (int ef = 0; ef < 2; ++ef) {
+            grp[tf][ef] = first ? part[tf][ef] : grp[tf][ef] + part[tf][ef];
+            part[tf][ef] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+      }
     }
   }
 #pragma unroll
@@ -452,23 +464,19 @@ __global__ __launch_bounds__(256) void route_logits_tiled(RouteParams p, float* 
       for (int ii = 0; ii < 4; ++ii) {
         const int t = t0 + wm * 32 + tf * 16 + 4 * q + ii;
         const int e = e0 + wn * 32 + ef * 16 + r;
-        if (t < p.T && e < p.E) logits[(size_t)t * p.E + e] = tot[tf][ef][ii];
+        if (t < p.T && e < p.E) p.part[((size_t)j * p.T + t) * p.E + e] = grp[tf][ef][ii];
       }
 }
 
 // Prefill layout, second kernel: one wave per token selects from its logits.
 template <int SLOTS>
-__global__ __launch_bounds__(256) void route_select(RouteParams p, const float* logits) {
+__global__ __launch_bounds__(256) void route_select(RouteParams p) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;
   float l[SLOTS], bv[SLOTS];
   load_bias<SLOTS>(p, bv);
-#pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int e = s * kWave + lane;
-    l[s] = e < p.E ? logits[(size_t)t * p.E + e] : -__builtin_inff();
-  }
+  sum_groups<SLOTS>(p, t, l);
   select_token<SLOTS>(p, t, l, bv);
 }
 
@@ -477,10 +485,9 @@ bool use_large(int T, int E) { (void)E; return T > SMALL_T_MAX; }
 template <int SLOTS>
 moe_status launch_slots(const RouteParams& p, hipStream_t stream) {
   if (use_large(p.T, p.E)) {
-    float* logits = p.logits_out ? p.logits_out : p.part;
-    route_logits_tiled<<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE)), 256, 0, stream>>>(p, logits);
+    route_logits_group<<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE), p.NG), 256, 0, stream>>>(p);
     MOE_CHECK_LAUNCH();
-    route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p, logits);
+    route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
   } else {
     dim3 grid(p.NF * p.NG, ceil_div(p.T, 16));
     route_small<SLOTS><<<grid, 256, 0, stream>>>(p);
@@ -492,7 +499,7 @@ moe_status launch_slots(const RouteParams& p, hipStream_t stream) {
 }  // namespace
 
 size_t route_workspace_size(int T, int H, int E) {
-  const size_t per_token = use_large(T, E) ? (size_t)E : (size_t)ceil_div(H, KCH * CPG) * E;
+  const size_t per_token = (size_t)ceil_div(H, KCH * CPG) * E;  // group sums [NG][T][E]
   return kCtrlBytes + align_up(per_token * T * sizeof(float), 256);
 }
 
