@@ -14,9 +14,10 @@ on stdout; diagnostics go to stderr.
 Also reported in the same line:
   roofline      - the GEMM1 kernel against MI355X's published peaks
   cpu_baseline  - the float64 oracle timed on a bounded token sample
-  decode        - cold-cache (512 MiB flush before each replay) HIP-graph
-                  replays of moe_layer at T = 1 and 64: us/layer and achieved
-                  HBM bandwidth on the weights of the experts actually touched
+  decode        - cold-cache moe_layer at decode sizes (Qwen3 T = 1, 64;
+                  GLM T = 1, 8; DeepSeek-V3 T = 1; DeepSeek-V4 T = 512):
+                  us/layer and achieved HBM bandwidth on the weights of the
+                  experts actually touched
   router        - moe_route alone next to the launch floor (empty kernel)
                   and the bare gate-read kernel, cold
 """
@@ -143,81 +144,100 @@ class Step:
         self.ffn(("gemm2", "combine"))
 
 
-def time_layer_cold(torch, fn, flush, reps=20):
-    """Median of per-replay event times, with the cache flushed before each."""
-    ts = []
-    for _ in range(reps):
-        flush.zero_()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
+class ColdTimer:
+    """GPU time of fn() with cold caches: each sample is preceded by a read of
+    1 GiB (it evicts the L2s and the 256 MB last-level cache; a write would
+    leave dirty lines whose write-back then overlaps the timed work), and is
+    the event-pair time around fn() minus the median event-pair time around
+    nothing measured the same way (the event overhead, about 4 us)."""
+
+    def __init__(self, moe, torch):
+        self.moe, self.torch = moe, torch
+        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        self.sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(1 << 30)), dtype=torch.float32,
+                                device="cuda")
+        self.base = None
+
+    def raw(self, fn, reps):
+        torch = self.torch
+        ts = []
+        for _ in range(reps):
+            self.moe.probe_read(self.buf, self.sink)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e) * 1000.0)
+        return statistics.median(ts)
+
+    def __call__(self, fn, reps=20):
+        if self.base is None:
+            self.base = self.raw(lambda: None, 30)
         fn()
-        e.record()
-        torch.cuda.synchronize()
-        ts.append(s.elapsed_time(e) * 1000.0)
-    return statistics.median(ts), min(ts)
+        self.torch.cuda.synchronize()
+        return max(self.raw(fn, reps) - self.base, 0.01)
 
 
-def graph_of(torch, fn):
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        fn()
-    torch.cuda.synchronize()
-    return g
+DECODE_CASES = (("qwen3", 1), ("qwen3", 64), ("glm", 1), ("glm", 8), ("dsv3", 1), ("dsv4", 512))
 
 
-def decode_sweep(moe, torch, cfg, W, flush):
-    from synth import make_x
+def decode_sweep(moe, torch, timer, qwen3_weights):
+    """Cold moe_layer at decode sizes: us per layer and the HBM rate on the
+    weights of the experts actually touched (distinct experts x expert bytes,
+    scales included)."""
+    from synth import get_config, make_weights, make_x
     out = {}
-    for T in (1, 64):
+    cache = {"qwen3": qwen3_weights} if qwen3_weights is not None else {}
+    for name, T in DECODE_CASES:
+        cfg = get_config(name)
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[name] = make_weights(cfg, "cuda")
+        W = cache[name]
         x = make_x(cfg, T, "cuda")
         y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
         ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, 0, cfg.wformat),
                          dtype=torch.uint8, device="cuda")
-
         def call():
             moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,
                       cfg.topk_group, cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat,
                       w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], ws=ws, out=y)
 
-        g = graph_of(torch, call)
-        med, best = time_layer_cold(torch, g.replay, flush)
-        ids, _ = moe.route(x, W["gate"], W["bias"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
-                           cfg.renormalize, cfg.routed_scale)
-        touched = int(torch.unique(ids).numel())
+        us = timer(call)
+        r_ids, _ = moe.route(x, W["gate"], W["bias"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                             cfg.renormalize, cfg.routed_scale)
+        touched = int(torch.unique(r_ids).numel())
         nbytes = touched * expert_bytes(cfg)
-        out[f"T{T}"] = {"us_per_layer": round(med, 2), "us_best": round(best, 2), "experts_touched": touched,
-                        "weight_bytes": nbytes, "hbm_TBps": round(nbytes / (med * 1e-6) / 1e12, 3),
-                        "hbm_frac": round(nbytes / (med * 1e-6) / HBM_PEAK, 4),
-                        "tokens_per_s": round(T / (med * 1e-6), 1)}
-        log(f"decode T={T}: {med:.1f} us/layer, {touched} experts, {out[f'T{T}']['hbm_TBps']} TB/s")
+        key = f"{name}_T{T}"
+        out[key] = {"us_per_layer": round(us, 2), "experts_touched": touched, "weight_bytes": nbytes,
+                    "weights": cfg.wformat, "hbm_TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+                    "hbm_frac": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
+                    "tokens_per_s": round(T / (us * 1e-6), 1)}
+        log(f"decode {key}: {us:.1f} us/layer, {touched} experts, {out[key]['hbm_TBps']} TB/s "
+            f"({out[key]['hbm_frac']:.3f} of peak)")
+    cache.clear()
+    torch.cuda.empty_cache()
     return out
 
 
-def router_probe(moe, torch, flush):
-    """moe_route alone (cold) beside the empty kernel and the bare read of the
-    gate, for the GLM-5.3-Flash-shaped gate (288 x 4096 fp32) and the Qwen3
-    one, at T = 1."""
+def router_probe(moe, torch, timer):
+    """moe_route alone at T = 1 next to the bare read of its gate weight
+    (moe_probe_read, the same bytes) and an empty kernel, all cold."""
     from synth import get_config, make_router_weights, make_x
-    res = {}
-    empty = graph_of(torch, lambda: moe.probe_empty())
-    res["empty_kernel_us"] = round(time_layer_cold(torch, empty.replay, flush)[0], 2)
-    for name in ("glm", "qwen3"):
+    res = {"empty_kernel_us": round(timer(lambda: moe.probe_empty()), 2)}
+    for name in ("glm", "qwen3", "dsv3"):
         cfg = get_config(name)
         gate, bias = make_router_weights(cfg, "cuda")
         x = make_x(cfg, 1, "cuda")
         ws = torch.zeros(moe.lib().moe_route_workspace_size(1, cfg.H, cfg.E), dtype=torch.uint8, device="cuda")
-        sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(gate.numel() * 4)), dtype=torch.float32, device="cuda")
-        g_route = graph_of(torch, lambda: moe.route(x, gate, bias, cfg.k, cfg.scoring, ws=ws))
-        g_read = graph_of(torch, lambda: moe.probe_read(gate, sink))
-        r_us = time_layer_cold(torch, g_route.replay, flush)[0]
-        b_us = time_layer_cold(torch, g_read.replay, flush)[0]
+        sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(gate.numel() * 4)), dtype=torch.float32,
+                           device="cuda")
+        r_us = timer(lambda: moe.route(x, gate, bias, cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                                       cfg.renormalize, cfg.routed_scale, ws=ws))
+        b_us = timer(lambda: moe.probe_read(gate, sink))
         res[name] = {"route_us_T1": round(r_us, 2), "bare_gate_read_us": round(b_us, 2),
                      "gate_bytes": gate.numel() * 4, "ratio": round(r_us / b_us, 3)}
         log(f"router {name}: {r_us:.2f} us vs bare read {b_us:.2f} us")
@@ -248,8 +268,9 @@ def cpu_baseline(cfg, W, x, n_sample):
     dt = time.perf_counter() - t0
     assert np.all(np.isfinite(y))
     return {"value": round(n_sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n_sample} of the {x.shape[0]} tokens (router + float64 dense-equivalent layer), "
-                      f"{dt:.1f} s", "seconds": round(dt, 2)}
+            "sample": (f"first {n_sample} of the {x.shape[0]} tokens" if n_sample < x.shape[0] else
+                       f"all {n_sample} tokens") + f" (router + float64 dense-equivalent layer), {dt:.1f} s",
+            "seconds": round(dt, 2)}
 
 
 # ---------------------------------------------------------------- main
@@ -260,7 +281,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--T", type=int, default=4096)
     ap.add_argument("--config", default="qwen3")
-    ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: all T)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode sweep and router probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -322,7 +343,7 @@ def main():
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{cfg.name} MoE layer (Qwen3-30B-A3B shape), T={T}", "T": T, "H": cfg.H,
+        "config": {"workload": f"{cfg.description}, T={T}", "T": T, "H": cfg.H,
                    "E": cfg.E, "k": cfg.k, "F": cfg.F, "block_m": bm, "weights": cfg.wformat,
                    "experts_touched": touched},
         "us_per_layer": round(ms * 1e3, 2),
@@ -330,12 +351,14 @@ def main():
         "roofline": roof,
     }
     if not args.no_extras:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        result["decode"] = decode_sweep(moe, torch, cfg, W, flush)
-        result["router"] = router_probe(moe, torch, flush)
-        del flush
+        timer = ColdTimer(moe, torch)
+        result["router"] = router_probe(moe, torch, timer)
+        result["decode"] = decode_sweep(moe, torch, timer, W if cfg.name == "qwen3" else None)
+        result["cold_timing"] = ("median event-pair time after a 1 GiB read, minus the empty event-pair "
+                                 f"time ({timer.base:.2f} us)")
+        del timer
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, W, x, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, W, x, args.cpu_sample if args.cpu_sample > 0 else T)
         log(f"cpu oracle: {result['cpu_baseline']['value']} tokens/s on {result['cpu_baseline']['cores']} threads")
     print(json.dumps(result), flush=True)
     return 0
