@@ -60,11 +60,16 @@ int read_grid(size_t bytes) {
 
 }  // namespace
 
+// Block size for T tokens: with fewer than 2 rows per expert on average most
+// blocks hold a single row and the 16-row weight-stream kernel is fastest;
+// from 2 rows on, the tiled kernels' 128-column tiles (activation rows read
+// once per 256 weight rows) win, at the smallest block that the expected
+// rows per expert fill.
 int layer_block_m(int T, int k, int E) {
-  const int64_t m = ((int64_t)T * k + E - 1) / E;  // tokens per expert
-  if (m <= 16) return 16;
-  if (m <= 32) return 32;
-  if (m <= 96) return 64;
+  const double m = (double)T * k / E;  // rows per expert
+  if (m < 2.0) return 16;
+  if (m <= 32.0) return 32;
+  if (m <= 96.0) return 64;
   return 128;
 }
 

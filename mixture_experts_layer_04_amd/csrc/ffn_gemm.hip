@@ -610,10 +610,18 @@ struct SChunk {
   int sb[FN][S];    // MX: e8m0 of weight row r, K block g
 };
 
-constexpr int kStreamWaves = 8;
+// Waves per stream workgroup and (0: chosen per shape) fragments per tile;
+// compile-time tuning knobs.
+#ifndef MOE_STREAM_WAVES
+#define MOE_STREAM_WAVES 4
+#endif
+#ifndef MOE_STREAM_FN
+#define MOE_STREAM_FN 0
+#endif
+constexpr int kStreamWaves = MOE_STREAM_WAVES;
 
 template <int F, bool G1, int FN>
-__global__ __launch_bounds__(512) void gemm_stream(GemmP p) {
+__global__ __launch_bounds__(64 * kStreamWaves) void gemm_stream(GemmP p) {
   using O = SOp<F>;
   constexpr int SK = O::SK, S = stream_steps<F, FN>();
   constexpr int NC = FN * 16;                // weight rows (C columns) per tile
@@ -825,6 +833,7 @@ __global__ __launch_bounds__(256) void requant_act_kernel(GemmP p) {
 // of the A rows) that still leaves >= 2048 tiles (8 per CU) for the expected
 // number of experts touched, E (1 - (1 - k/E)^T).
 int stream_fn(int T, int k, int E, int N, bool g1) {
+  if (MOE_STREAM_FN != 0) return MOE_STREAM_FN;
   const double touched = E * (1.0 - std::pow(1.0 - (double)k / E, (double)T));
   const int fns[3] = {4, 2, 1};
   for (int fn : fns) {

@@ -111,6 +111,8 @@ def test_block_m_choice(L):
     # tile height follows the tokens per expert ([Kernels] "The fused expert
     # GEMM", last paragraph): small at decode, large at prefill
     assert L.moe_layer_block_m(1, 8, 128) == 16
-    assert L.moe_layer_block_m(64, 8, 256) == 16
+    assert L.moe_layer_block_m(64, 8, 256) == 32
+    assert L.moe_layer_block_m(63, 8, 256) == 16
+    assert L.moe_layer_block_m(8, 8, 288) == 16
     assert L.moe_layer_block_m(4096, 8, 128) == 128
     assert L.moe_layer_block_m(2048, 8, 256) == 64
