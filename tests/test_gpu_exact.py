@@ -1,0 +1,128 @@
+"""Exact-arithmetic parity of moe_expert_ffn (bf16, fp8, MXFP4 weights).
+
+The inputs are built so that every value the path produces is exactly
+representable and every sum is exact in fp32, whatever the order:
+
+* x holds small integers (-4..4), a column of 8, a column of 2, and 448 in
+  every 32nd column (so each 1x128 and 1x32 activation group has amax 448 and
+  the fp8 / MX activation scale is exactly 1);
+* each gate row has 4 at the column of 8: g = 32 for every token, and
+  silu(32) rounds to 32 in fp32;
+* each up row has +-1 at three integer columns (|u| <= 12), except every 32nd
+  SwiGLU column, whose up row (1.5 at the 8-column, 1 at the 2-column) gives
+  u = 14, i.e. act = 448 = the e4m3 maximum, so the requantisation scales of
+  the SwiGLU output are exactly 1 as well; every act = 32 u is on the e4m3
+  grid;
+* each w2 row has +-1 at two non-448 SwiGLU columns (|out| <= 768, a multiple
+  of 32: exact in bf16);
+* routing weights are 0.25 or 0.5 (k = 2): y is a multiple of 8 below 768.
+
+The weight values are on the bf16, e4m3 and e2m1 grids with unit scales, so
+the GPU result must equal the exact value (the float64 oracle rounded to the
+nearest integer, all outputs being multiples of 8; a zero may come out as
+-0) for every BLOCK_M and tile shape.  Together with the random-input parity tests
+this pins the gather through sorted_ids, the gate / up row pairing, the
+SwiGLU column, the GEMM2 scatter to the assignment slot and the slot-order
+combine: a transposed operand, a wrong row or a shifted column changes the
+exact result.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import say
+from oracle import ffn as offn
+from oracle import formats as fm
+from synth import make_topk_ids, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+_E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+
+
+def _encode_e2m1(w):
+    """float32 [N, K] on the e2m1 grid -> packed uint8 [N, K/2] (element 2j in
+    the low nibble of byte j)."""
+    a = np.abs(w)
+    codes = np.vectorize(lambda v: _E2M1_CODE[float(v)])(a).astype(np.uint8)
+    codes |= ((w < 0) & (a > 0)).astype(np.uint8) << 3
+    return codes[:, 0::2] | (codes[:, 1::2] << 4)
+
+
+def build(E, H, F, T, k, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-4, 5, size=(T, H)).astype(np.float32)
+    x[:, 1] = 8.0
+    x[:, 2] = 2.0
+    x[:, ::32] = 448.0
+    free_h = np.array([h for h in range(H) if h % 32 != 0 and h not in (1, 2)])
+    free_f = np.array([f for f in range(F) if f % 32 != 0])
+    w13 = np.zeros((E, 2 * F, H), dtype=np.float32)
+    w2 = np.zeros((E, H, F), dtype=np.float32)
+    for e in range(E):
+        w13[e, :F, 1] = 4.0
+        for f in range(F):
+            if f % 32 == 0:
+                w13[e, F + f, 1] = 1.5
+                w13[e, F + f, 2] = 1.0
+            else:
+                cols = rng.choice(free_h, 3, replace=False)
+                w13[e, F + f, cols] = rng.choice([-1.0, 1.0], 3)
+        for h in range(H):
+            cols = rng.choice(free_f, 2, replace=False)
+            w2[e, h, cols] = rng.choice([-1.0, 1.0], 2)
+    ids = make_topk_ids(T, k, E, seed=seed)
+    w = rng.choice([0.25, 0.5], size=(T, k)).astype(np.float32)
+    return x, w13, w2, ids, w
+
+
+def to_device(fmt, x, w13, w2):
+    """Stored tensors of each format (unit scales)."""
+    xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+    E, N13, H = w13.shape
+    F = w2.shape[2]
+    if fmt == "bf16":
+        return xd, torch.from_numpy(w13).to(torch.bfloat16).cuda(), None, \
+            torch.from_numpy(w2).to(torch.bfloat16).cuda(), None
+    if fmt == "fp8":
+        c13 = torch.from_numpy(w13).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+        c2 = torch.from_numpy(w2).to(torch.float8_e4m3fn).view(torch.uint8).cuda()
+        s13 = torch.ones((E, N13 // 128, H // 128), dtype=torch.float32, device="cuda")
+        s2 = torch.ones((E, H // 128, F // 128), dtype=torch.float32, device="cuda")
+        return xd, c13, s13, c2, s2
+    p13 = np.stack([_encode_e2m1(w13[e]) for e in range(E)])
+    p2 = np.stack([_encode_e2m1(w2[e]) for e in range(E)])
+    s13 = torch.full((E, N13, H // 32), 127, dtype=torch.uint8, device="cuda")
+    s2 = torch.full((E, H, F // 32), 127, dtype=torch.uint8, device="cuda")
+    return xd, torch.from_numpy(p13).cuda(), s13, torch.from_numpy(p2).cuda(), s2
+
+
+CASES = [("bf16", 256, 256, bm, T) for bm, T in ((16, 5), (16, 300), (32, 300), (64, 300), (128, 300))] + \
+        [(f, 512, 512, bm, T) for f in ("fp8", "mxfp4") for bm, T in ((16, 3), (16, 200), (32, 200),
+                                                                       (64, 200), (128, 200))]
+
+
+@pytest.mark.parametrize("fmt,H,F,bm,T", CASES)
+def test_expert_ffn_exact(fmt, H, F, bm, T):
+    import mixture_experts_layer_04_amd as moe
+    E, k = 8, 2
+    say(f"exact probe {fmt} H={H} F={F} E={E} k={k} T={T} block_m={bm}")
+    x, w13, w2, ids, w = build(E, H, F, T, k, seed=T + bm)
+    xd, c13, s13, c2, s2 = to_device(fmt, x, w13, w2)
+    ids_d = ids.cuda()
+    w_d = torch.from_numpy(w).cuda()
+    s, b, n = moe.align(ids_d, E, bm)
+    y = moe.expert_ffn(xd, c13, c2, ids_d, w_d, s, b, n, bm, wformat=fmt, w13_scale=s13, w2_scale=s2)
+    torch.cuda.synchronize()
+    weights = offn.ExpertWeights(fmt, to_numpy(c13), to_numpy(c2), to_numpy(s13), to_numpy(s2))
+    ref, _ = offn.layer(to_numpy(xd), {"ids": ids.numpy(), "weights": w}, weights, E)
+    # every true output is a multiple of 8; the float64 oracle is off by
+    # ~1e-11 because it takes silu(32) = 32 (1 - 1.3e-14), so its nearest
+    # integer is the exact value
+    exact = np.round(ref)
+    assert np.max(np.abs(ref - exact)) < 1e-6 and np.all(exact % 8 == 0) and np.any(exact != 0)
+    # exact equality of values (a zero may carry either sign)
+    got = fm.bf16_bits_to_f64(to_numpy(y))
+    bad = np.argwhere(got != exact)
+    assert bad.size == 0, f"{len(bad)} of {got.size} outputs differ, first at {bad[:3].tolist()}"
