@@ -263,22 +263,25 @@ __device__ __forceinline__ int swz(int c, int row) {
   return c ^ ((row / (16 / CPR)) & (CPR - 1));
 }
 
-template <int F, bool G1, int BM, int BNW, int NS>
-__global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
+template <int F, bool G1, int BM, int BNW, int NS, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
   using T = Tr<F>;
   constexpr int CPRB = T::BROW / 16;   // 16-byte chunks per B row and step
   constexpr int ASZ = BM * 128;
   constexpr int BSZ = BNW * T::BROW;
+  constexpr int WN = NW / 2;           // waves: 2 along M x WN along N
+  constexpr int NT = 64 * NW;          // threads
   constexpr int FM = BM / 32;
-  constexpr int FN = BNW / 32;
-  constexpr int LA = BM / 32;          // A copy instructions per wave per step
-  constexpr int LB = BNW * CPRB / 256; // B copy instructions per wave per step
+  constexpr int FN = BNW / WN / 16;
+  constexpr int LA = BM * 8 / NT;      // A copy instructions per wave per step
+  constexpr int LB = BNW * CPRB / NT;  // B copy instructions per wave per step
+  static_assert(LA >= 1 && LB >= 1 && (!G1 || FN % 2 == 0), "tile too small for the wave count");
   // scales (FP8, MX): one 4-byte word per tile row (A: the row's scale(s) of
   // the step, B: the weight row's) copied with the data; every wave issues
   // the same number of copies, the slots past BM + BNW are never read
-  constexpr int LSC = (F == F_BF16) ? 0 : (BM + BNW + 255) / 256;
+  constexpr int LSC = (F == F_BF16) ? 0 : (BM + BNW + NT - 1) / NT;
   constexpr int LS = LA + LB + LSC;
-  constexpr int SCSZ = LSC * 256 * 4;
+  constexpr int SCSZ = LSC * NT * 4;
   constexpr int SSZ = ASZ + BSZ + SCSZ;
   constexpr int D = NS - 1;            // steps in flight ahead of the multiply
   static_assert(LS * (D > 1 ? D - 1 : 1) <= 63, "vmcnt range");
@@ -287,8 +290,8 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int K = G1 ? p.H : p.F;
@@ -307,8 +310,8 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
 
   // tile-local weight row of fragment fn of this wave
   auto frag_lrow = [&](int fn) {
-    return G1 ? (fn < FN / 2 ? wn * (BNW / 4) + fn * 16 : BNW / 2 + wn * (BNW / 4) + (fn - FN / 2) * 16)
-              : wn * (BNW / 2) + fn * 16;
+    return G1 ? (fn < FN / 2 ? wn * (BNW / (2 * WN)) + fn * 16 : BNW / 2 + wn * (BNW / (2 * WN)) + (fn - FN / 2) * 16)
+              : wn * (BNW / WN) + fn * 16;
   };
   auto weight_row = [&](int nt, int lrow) {
     if (G1) return lrow < BNW / 2 ? nt * (BNW / 2) + lrow : p.F + nt * (BNW / 2) + (lrow - BNW / 2);
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
     const uint8_t* ag[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int row = wave * (BM / 4) + 8 * i + (lane >> 3);
+      const int row = wave * (BM / NW) + 8 * i + (lane >> 3);
       bool v;
       const int src = a_row_index<G1>(p, blk, BM, row, v);  // padding rows read token 0; never used
       ag[i] = asrc + (size_t)src * rowbytes_a + 16 * swz<8>(lane & 7, row);
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
       const int row = (wave * LB + i) * (64 / CPRB) + lane / CPRB;
       bg[i] = wsrc + ((size_t)e * erows + weight_row(nt, row)) * rowbytes_b + 16 * swz<CPRB>(lane % CPRB, row);
     }
-    // scale words: slot q = (i * 4 + wave) * 64 + lane of copy i; q < BM: A
+    // scale words: slot q = (i * NW + wave) * 64 + lane of copy i; q < BM: A
     // row q, q < BM + BNW: B row q - BM.  Per step the source advances by
     // sc_step bytes.
     const uint8_t* scg[LSC > 0 ? LSC : 1];
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
       const int kblocks = K / 128;  // FP8: one fp32 scale per 128 K; MX: 4 e8m0 per 128 K
 #pragma unroll
       for (int i = 0; i < LSC; ++i) {
-        const int q = (i * 4 + wave) * 64 + lane;
+        const int q = (i * NW + wave) * 64 + lane;
         if (q < BM) {
           bool v;
           const int src = a_row_index<G1>(p, blk, BM, q, v);
@@ -375,12 +378,12 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
     auto issue = [&](int s, int slot) {
       uint8_t* st = lds + slot * SSZ;
 #pragma unroll
-      for (int i = 0; i < LA; ++i) g2lds16(ag[i] + (size_t)s * 128, st + (wave * (BM / 4) + 8 * i) * 128);
+      for (int i = 0; i < LA; ++i) g2lds16(ag[i] + (size_t)s * 128, st + (wave * (BM / NW) + 8 * i) * 128);
 #pragma unroll
       for (int i = 0; i < LB; ++i)
         g2lds16(bg[i] + (size_t)s * T::BROW, st + ASZ + (wave * LB + i) * (64 / CPRB) * T::BROW);
 #pragma unroll
-      for (int i = 0; i < LSC; ++i) g2lds4(scg[i] + (size_t)s * sc_step[i], st + ASZ + BSZ + (i * 4 + wave) * 256);
+      for (int i = 0; i < LSC; ++i) g2lds4(scg[i] + (size_t)s * sc_step[i], st + ASZ + BSZ + (i * NW + wave) * 256);
     };
 
     f32x4_t acc[FM][FN];
@@ -389,85 +392,111 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // the previous tile is done with LDS
-    // Every step issues exactly one step of copies (the last D - 1 steps copy
-    // step nk - 1 again into ring slots that no later step reads), so the
-    // number of copies in flight is always (D - 1) * LS at the wait below and
-    // the compiler's own waits for the scale loads stay exact.
-#pragma unroll
-    for (int s = 0; s < D; ++s) issue(s < nk ? s : nk - 1, s % NS);
-
-    for (int s = 0; s < nk; ++s) {
-      wait_vm<(D - 1) * LS>();
-      barrier_no_fence();
-      issue(s + D < nk ? s + D : nk - 1, (s + D) % NS);
-
+    // Operand fragments of one MFMA sub-step, read from a ring slot.  BF16
+    // has two 32-wide sub-steps per 64-element step; FP8 / MX one per step.
+    struct Frag {
+      typename SOp<F>::A af[FM];
+      typename SOp<F>::B bfr[FN];
+      float as_[FM][4];  // FP8: A scales of the C rows
+      float wsc[FN];     // FP8: weight block scales
+      int sa[FM];        // MX: A e8m0
+      int sb[FN];        // MX: weight e8m0
+    };
+    auto rd = [&](int s, int ks, Frag& f) {
       const uint8_t* As = lds + (s % NS) * SSZ;
       const uint8_t* Bs = As + ASZ;
-      const uint8_t* Ss = Bs + BSZ;  // scale words of the step
-      if (F == F_BF16) {
+      const uint8_t* Ss = Bs + BSZ;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8_t af[FM], bfr[FN];
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
-            const int rr = wm * (BM / 2) + fm * 16 + r;
-            af[fm] = *reinterpret_cast<const bf16x8_t*>(As + rr * 128 + 16 * swz<8>(ks * 4 + g, rr));
-          }
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int rr = frag_lrow(fn) + r;
-            bfr[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + rr * 128 + 16 * swz<8>(ks * 4 + g, rr));
-          }
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(af[fm], bfr[fn], acc[fm][fn]);
-        }
-      } else {
-        i32x8_t af[FM];
-        float as_[FM][4];
-        int sa[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          if (F == F_FP8) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              as_[fm][i] = reinterpret_cast<const float*>(Ss)[wm * (BM / 2) + fm * 16 + 4 * g + i];
-          } else {
-            sa[fm] = (int)Ss[(wm * (BM / 2) + fm * 16 + r) * 4 + g];
-          }
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int rr = wm * (BM / 2) + fm * 16 + r;
+      for (int fm = 0; fm < FM; ++fm) {
+        const int rr = wm * (BM / 2) + fm * 16 + r;
+        if constexpr (F == F_BF16) {
+          f.af[fm] = *reinterpret_cast<const bf16x8_t*>(As + rr * 128 + 16 * swz<8>(ks * 4 + g, rr));
+        } else {
           const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(As + rr * 128 + 16 * swz<8>(g, rr));
           const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(As + rr * 128 + 16 * swz<8>(4 + g, rr));
-          af[fm] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
+          f.af[fm] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          if constexpr (F == F_FP8) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int rr = frag_lrow(fn) + r;
-          if (F == F_FP8) {
-            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(Bs + rr * 128 + 16 * swz<8>(g, rr));
-            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(Bs + rr * 128 + 16 * swz<8>(4 + g, rr));
-            const i32x8_t bfr = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const float wsc = reinterpret_cast<const float*>(Ss)[BM + frag_lrow(fn)];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-              const f32x4_t t = mfma_f8(af[fm], bfr);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                acc[fm][fn][i] = __builtin_fmaf(t[i], as_[fm][i] * wsc, acc[fm][fn][i]);
-            }
+            for (int q = 0; q < 4; ++q)
+              f.as_[fm][q] = reinterpret_cast<const float*>(Ss)[wm * (BM / 2) + fm * 16 + 4 * g + q];
           } else {
-            const i32x4_t v = *reinterpret_cast<const i32x4_t*>(Bs + rr * 64 + 16 * swz<4>(g, rr));
-            const i32x8_t bfr = {v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-            const int sb = (int)Ss[(BM + rr) * 4 + g];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = mfma_mx(af[fm], bfr, acc[fm][fn], sa[fm], sb);
+            f.sa[fm] = (int)Ss[rr * 4 + g];
           }
         }
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int rr = frag_lrow(fn) + r;
+        if constexpr (F == F_BF16) {
+          f.bfr[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + rr * 128 + 16 * swz<8>(ks * 4 + g, rr));
+        } else if constexpr (F == F_FP8) {
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(Bs + rr * 128 + 16 * swz<8>(g, rr));
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(Bs + rr * 128 + 16 * swz<8>(4 + g, rr));
+          f.bfr[fn] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          f.wsc[fn] = reinterpret_cast<const float*>(Ss)[BM + frag_lrow(fn)];
+        } else {
+          f.bfr[fn] = *reinterpret_cast<const i32x4_t*>(Bs + rr * 64 + 16 * swz<4>(g, rr));
+          f.sb[fn] = (int)Ss[(BM + rr) * 4 + g];
+        }
+      }
+    };
+    auto mm = [&](const Frag& f) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          if constexpr (F == F_BF16) {
+            acc[fm][fn] = mfma_16x16x32_bf16(f.af[fm], f.bfr[fn], acc[fm][fn]);
+          } else if constexpr (F == F_FP8) {
+            const f32x4_t t = mfma_f8(f.af[fm], f.bfr[fn]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[fm][fn][q] = __builtin_fmaf(t[q], f.as_[fm][q] * f.wsc[fn], acc[fm][fn][q]);
+          } else {
+            const i32x4_t v = f.bfr[fn];
+            acc[fm][fn] = mfma_mx(f.af[fm], i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0}, acc[fm][fn], f.sa[fm], f.sb[fn]);
+          }
+        }
+    };
+    // Make step sn visible to every wave and refill the ring: this wave's
+    // reads of the slot about to be refilled are done (lgkmcnt), its copies
+    // of step sn have landed (vmcnt: D - 1 later steps may stay in flight),
+    // then the barrier, then the copies of step sn + D into the slot of step
+    // sn - 1.  Every step issues one step of copies (past the end: step
+    // nk - 1 again, into slots no later step reads), so the wait count is
+    // the same every time.
+    auto next_step = [&](int sn) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wait_vm<(D - 1) * LS>();
+      barrier_no_fence();
+      issue(sn + D < nk ? sn + D : nk - 1, (sn + D) % NS);
+    };
+
+    __syncthreads();  // the previous tile is done with LDS
+#pragma unroll
+    for (int s = 0; s < D; ++s) issue(s < nk ? s : nk - 1, s % NS);
+    if constexpr (F == F_BF16) {
+      // Software pipeline: the fragments of the next sub-step are read from
+      // LDS while the matrix cores work on the current one.
+      Frag f0, f1;
+      next_step(0);
+      rd(0, 0, f0);
+      for (int s = 0; s < nk; ++s) {
+        rd(s, 1, f1);
+        mm(f0);
+        if (s + 1 < nk) {
+          next_step(s + 1);
+          rd(s + 1, 0, f0);
+        }
+        mm(f1);
+      }
+    } else {
+      // one sub-step per step; a second fragment buffer does not fit the
+      // register file next to the accumulators at BLOCK_M 128
+      for (int s = 0; s < nk; ++s) {
+        Frag f0;
+        next_step(s);
+        rd(s, 0, f0);
+        mm(f0);
       }
     }
     __syncthreads();  // every wave is done reading the stage buffers
@@ -483,7 +512,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
         for (int fa = 0; fa < FA; ++fa)
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[fm][fa][i] = swiglu(acc[fm][fa][i], acc[fm][fa + FA][i]);
-      const int lcol0 = wn * (BNA / 2);  // first tile column of this wave
+      const int lcol0 = wn * (BNA / WN);  // first tile column of this wave
       if (F == F_BF16) {
         uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BM][BNA]
 #pragma unroll
@@ -495,7 +524,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
               st[(wm * (BM / 2) + fm * 16 + 4 * g + i) * BNA + lcol0 + fa * 16 + r] =
                   (uint16_t)f32_to_bf16_bits(v[fm][fa][i]);
       } else if (F == F_FP8) {
-        float* xch = reinterpret_cast<float*>(lds + BM * BNA);  // [2][BM] after the byte tile
+        float* xch = reinterpret_cast<float*>(lds + BM * BNA);  // [WN][BM] after the byte tile
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -514,7 +543,9 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int lr = wm * (BM / 2) + fm * 16 + 4 * g + i;
-            const float amax = fmaxf(xch[lr], xch[BM + lr]);
+            float amax = xch[lr];
+#pragma unroll
+            for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, xch[w2 * BM + lr]);
             const float sc = amax > 0.f ? amax / 448.f : 1.f;
             const float inv = 1.f / sc;
             if (wn == 0 && r == 0) act_s[(size_t)(blk * BM + lr) * (p.F / 128) + nt] = sc;
@@ -547,7 +578,7 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
       // whole rows of the tile to act (BNA columns of 2 or 1 bytes)
       constexpr int RB = BNA * T::AB;  // bytes per tile row
       constexpr int CH = RB / 16;
-      for (int idx = tid; idx < BM * CH; idx += 256) {
+      for (int idx = tid; idx < BM * CH; idx += NT) {
         const int lr = idx / CH;
         const int c = idx % CH;
         const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * RB + c * 16);
@@ -561,11 +592,11 @@ __global__ __launch_bounds__(256) void gemm_tiled(GemmP p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
-            st[(wm * (BM / 2) + fm * 16 + 4 * g + i) * BNW + wn * (BNW / 2) + fn * 16 + r] =
+            st[(wm * (BM / 2) + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
                 (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
       __syncthreads();
       constexpr int CH = BNW * 2 / 16;
-      for (int idx = tid; idx < BM * CH; idx += 256) {
+      for (int idx = tid; idx < BM * CH; idx += NT) {
         const int lr = idx / CH;
         const int c = idx % CH;
         const int sid = p.sorted_ids[blk * BM + lr];
@@ -619,6 +650,10 @@ struct SChunk {
 #define MOE_STREAM_FN 0
 #endif
 constexpr int kStreamWaves = MOE_STREAM_WAVES;
+// Waves per tiled (BLOCK_M >= 64, bf16) workgroup: 4 (2 x 2) or 8 (2 x 4).
+#ifndef MOE_TILED_WAVES
+#define MOE_TILED_WAVES 8
+#endif
 
 template <int F, bool G1, int FN>
 __global__ __launch_bounds__(64 * kStreamWaves) void gemm_stream(GemmP p) {
@@ -870,12 +905,12 @@ void launch_stream_one(const GemmP& p, int64_t max_blocks, int N, hipStream_t s)
   gemm_stream<F, G1, FN><<<tile_grid(max_blocks * (N / BNO), wgs), 64 * kStreamWaves, lds, s>>>(p);
 }
 
-template <int F, bool G1, int BM, int BNW, int NS>
+template <int F, bool G1, int BM, int BNW, int NS, int NW = 4>
 moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   using T = Tr<F>;
-  const size_t sc = (F == F_BF16) ? 0 : (size_t)((BM + BNW + 255) / 256) * 1024;
+  const size_t sc = (F == F_BF16) ? 0 : (size_t)((BM + BNW + 64 * NW - 1) / (64 * NW)) * 64 * NW * 4;
   const size_t lds = (size_t)NS * ((size_t)BM * 128 + (size_t)BNW * T::BROW + sc);
-  gemm_tiled<F, G1, BM, BNW, NS><<<tile_grid(max_tiles, 512), 256, lds, s>>>(p);
+  gemm_tiled<F, G1, BM, BNW, NS, NW><<<tile_grid(max_tiles, 512), 64 * NW, lds, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -920,10 +955,17 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
     return MOE_OK;
   }
   const int64_t t1 = mb * (a.F / 128), t2 = mb * (a.H / 128);
+  constexpr int NW = (F == F_BF16) ? MOE_TILED_WAVES : 4;
   switch (a.block_m) {
     case 32: return which == 1 ? launch_tiled_one<F, true, 32, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 32, 128, 3>(p, t2, s);
-    case 64: return which == 1 ? launch_tiled_one<F, true, 64, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 64, 128, 3>(p, t2, s);
-    case 128: return which == 1 ? launch_tiled_one<F, true, 128, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 128, 128, 3>(p, t2, s);
+    case 64:
+      if (which == 1) return launch_tiled_one<F, true, 64, 256, 3, NW>(p, t1, s);
+      if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
+      return launch_tiled_one<F, false, 64, 128, 3, NW>(p, t2, s);
+    case 128:
+      if (which == 1) return launch_tiled_one<F, true, 128, 256, 3, NW>(p, t1, s);
+      if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 128, 256, 3, NW>(p, t2 / 2, s);
+      return launch_tiled_one<F, false, 128, 128, 3, NW>(p, t2, s);
   }
   return MOE_E_INVAL;
 }
