@@ -49,15 +49,22 @@ def expert_bytes(cfg):
 
 
 def w13_bytes(cfg):
-    return expert_bytes(cfg) * 2 // 3 if cfg.wformat == "bf16" else None
+    """Bytes of one expert's w13 [2F, H] with its scales."""
+    H, F = cfg.H, cfg.F
+    if cfg.wformat == "bf16":
+        return 2 * F * H * 2
+    if cfg.wformat == "fp8":
+        return 2 * F * H + 4 * (2 * F // 128) * (H // 128)
+    return 2 * F * H // 2 + 2 * F * H // 32
 
 
 def gemm1_work(cfg, T, touched):
-    """Algorithmic work of one grouped GEMM1 launch: weight bytes of the
-    experts touched + x read once + SwiGLU output written once; FLOPs
-    2 * T * k * 2F * H (padding rows not counted)."""
-    wbytes = touched * 2 * cfg.F * cfg.H * 2
-    nbytes = wbytes + T * cfg.H * 2 + T * cfg.k * cfg.F * 2
+    """Algorithmic work of one grouped GEMM1 launch: w13 bytes of the experts
+    touched + the activation rows read once + the SwiGLU output written once
+    (activations in bf16, or e4m3 for the fp8 formats; scales not counted);
+    FLOPs 2 * T * k * 2F * H (padding rows not counted)."""
+    ab = 2 if cfg.wformat == "bf16" else 1
+    nbytes = touched * w13_bytes(cfg) + T * cfg.H * ab + T * cfg.k * cfg.F * ab
     flops = 2 * T * cfg.k * 2 * cfg.F * cfg.H
     return nbytes, flops
 
@@ -284,9 +291,11 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: all T)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode sweep and router probes")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="diagnostic: only the cold decode cases (for kernel traces), no benchmark line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="first copy MIB MiB device to device once (a kernel of known traffic that calibrates "
-                         "rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+                    help="first write MIB MiB with a fill kernel and read them once with moe_probe_read "
+                         "(kernels of known traffic that calibrate rocprofv3 WRITE_SIZE / FETCH_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (every expert is local to the "
@@ -299,12 +308,18 @@ def main():
 
     cfg = get_config(args.config)
     T = args.T
+    if args.decode_only:
+        timer = ColdTimer(moe, torch)
+        for key, v in decode_sweep(moe, torch, timer, None).items():
+            log(f"{key}: {v}")
+        return 0
     if args.copy_probe:
-        src = torch.ones(args.copy_probe << 18, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+        # kernels of known traffic for the counter calibration: a fill that
+        # writes MIB MiB and moe_probe_read reading them once
+        buf = torch.zeros(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        moe.probe_read(buf)
         torch.cuda.synchronize()
-        del src, dst
+        del buf
     log(f"bench: {cfg.description}, T={T}")
     W, x = make_problem(cfg, T)
     bm = moe.layer_block_m(T, cfg.k, cfg.E)

@@ -46,8 +46,10 @@
 //    K per row each) ahead of the multiply; one barrier per step; the output
 //    tile leaves through LDS as whole rows.
 // Tiles are visited in a grid-stride loop bounded by the padded length read
-// on the device (no workgroup is launched for blocks that do not exist), in
-// an order that keeps the blocks sharing a weight tile on one XCD.
+// on the device (no workgroup is launched for blocks that do not exist),
+// block-major: an XCD takes a contiguous run of blocks and all of their N
+// tiles, so a block's A rows are read from HBM once and the weight tiles of
+// an expert are reused by its following blocks.
 
 #include <cmath>
 
@@ -321,8 +323,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
   for (int64_t it = blockIdx.x; it < 8 * per; it += gridDim.x) {
     const int64_t L = xcd_tile(it, per);
     if (L >= n_valid) continue;
-    const int blk = (int)(L % nblk);
-    const int nt = (int)(L / nblk);
+    // block-major: the N tiles of a block follow each other (its A rows stay
+    // in the L2 for all of them; the weight tiles are shared with the
+    // expert's next blocks through the last-level cache)
+    const int blk = (int)(L / ntn);
+    const int nt = (int)(L % ntn);
     const int e = p.block_expert[blk];
 
     // per-lane global sources of the copy instructions

@@ -84,8 +84,8 @@ int tile_grid(int64_t n_tiles, int max_wgs);
 namespace moe {
 // Maps the i-th grid-stride tile index to a logical tile so that XCD x
 // (workgroups are dealt to the XCDs round-robin) handles the contiguous run
-// [x*per, (x+1)*per) of logical tiles; neighbouring logical tiles share a
-// weight tile and so hit the same L2.
+// [x*per, (x+1)*per) of logical tiles: neighbouring logical tiles (the N
+// tiles of one block) share their A rows in that XCD's L2.
 __device__ __forceinline__ int64_t xcd_tile(int64_t i, int64_t per) { return (i & 7) * per + (i >> 3); }
 }  // namespace moe
 #endif
