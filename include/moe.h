@@ -183,7 +183,9 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
  * bf16 in the workspace (fp8 with scales for the quantised formats).
  * Constraints: H and F multiples of 128 (bf16) or of 512 (fp8 formats,
  * else MOE_E_UNSUPPORTED); block_m in {16, 32, 64, 128}; k <= 16;
- * E <= 1024.
+ * E <= 1024; x [T, H], the SwiGLU rows [max padded rows, F] and one
+ * expert's w13 [2F, H] each below 4 GiB (the kernels address them with
+ * 32-bit byte offsets), else MOE_E_UNSUPPORTED.
  * ------------------------------------------------------------------------ */
 moe_status moe_expert_ffn(const void* x, int wformat,
                           const void* w13, const void* w13_scale,

@@ -1,4 +1,5 @@
-// Block alignment in one launch of one workgroup.
+// Block alignment: one launch of one workgroup for small T*k, two
+// multi-workgroup launches (count, place) for large T*k.
 //
 // [MoE] "vLLM's Triton path: align, then index" (per-expert counts, each
 // rounded up to a whole block, exclusive scan, block-to-expert table, -1
@@ -19,6 +20,17 @@
 //      cnt[w][e] by the group size.
 // Padding slots and the tail get the sentinel T*k; block_expert is filled by
 // a binary search of the scanned starts and -1 past the padded length.
+//
+// For large T*k the same steps are spread over G workgroups, workgroup g
+// owning the contiguous chunk [g*C, (g+1)*C) of assignments:
+//   count: each workgroup writes its per-expert counts cnt[e][g]; the last
+//          one to finish (agent-scope counter) sums, pads and scans them (a
+//          wave per expert) and turns cnt[e][g] into workgroup g's first slot
+//          for expert e;
+//   place: each workgroup recounts its chunk per wave, offsets the waves
+//          from cnt[g][e] and places as in step 3; all workgroups share the
+//          sentinel fill and the block table.
+// Positions are the same as in the one-workgroup kernel.
 
 #include "common.h"
 #include "launch.h"
@@ -36,6 +48,81 @@ struct AlignParams {
   int A, E, bm, nbits;
   int max_padded, max_blocks;
 };
+
+// expert owning padded row `row`: upper_bound of row in start[0..E], minus one
+__device__ __forceinline__ int expert_of_row(const int* start, int E, int row) {
+  int lo = 0, hi = E + 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (start[mid] <= row) lo = mid + 1; else hi = mid;
+  }
+  return lo - 1;
+}
+
+// Stable placement of the assignments [a_begin, a_end) of one wave, 64 at a
+// time, ids read CH per lane at once; first[e] is the wave's next slot for
+// expert e (LDS, advanced here).
+template <int CH>
+__device__ __forceinline__ void place_segment(const int32_t* ids, int32_t* sorted_ids, int* first, int E, int nbits,
+                                              int a_begin, int a_end, int lane) {
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int a1 = a_begin; a1 < a_end; a1 += 64 * CH) {
+    int idv[CH];
+    const int nc = min(CH, (a_end - a1 + 63) >> 6);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int a = a1 + 64 * c + lane;
+      idv[c] = (c < nc && a < a_end) ? ids[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {  // 64 consecutive assignments at a time, in order
+      if (c >= nc) break;
+      const int a = a1 + 64 * c + lane;
+      int id = idv[c];
+      const bool valid = id >= 0 && id < E;
+      if (!valid) id = 0;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const int rank = __popcll(m & lt);
+        const int pos = first[id] + rank;
+        sorted_ids[pos] = a;
+        if (rank == 0) first[id] += __popcll(m);
+      }
+    }
+  }
+}
+
+// Count the valid ids of [a_begin, a_end) into hist (LDS atomics), CH ids
+// per lane in flight; returns whether an id outside [0, E) other than -1
+// was seen.
+template <int CH>
+__device__ __forceinline__ bool count_segment(const int32_t* ids, int* hist, int E, int a_begin, int a_end, int lane) {
+  bool bad = false;
+  for (int a0 = a_begin; a0 < a_end; a0 += 64 * CH) {
+    int idv[CH];
+    const int nc = min(CH, (a_end - a0 + 63) >> 6);  // sub-chunks of 64 holding ids
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int a = a0 + 64 * c + lane;
+      idv[c] = (c < nc && a < a_end) ? ids[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c >= nc) break;
+      const int id = idv[c];
+      if (id >= 0 && id < E)
+        atomicAdd(&hist[id], 1);
+      else if (id != -1)
+        bad = true;
+    }
+  }
+  return bad;
+}
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
@@ -57,27 +144,9 @@ __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
 
   int* my = cnt + wave * E;
   for (int e = lane; e < E; e += 64) my[e] = 0;
-  bool bad = false;
   // ids are read CH per lane at a time (all loads in flight together)
   constexpr int CH = 16;
-  for (int a0 = a_begin; a0 < a_end; a0 += 64 * CH) {
-    int idv[CH];
-    const int nc = min(CH, (a_end - a0 + 63) >> 6);  // sub-chunks of 64 holding ids
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int a = a0 + 64 * c + lane;
-      idv[c] = (c < nc && a < a_end) ? p.ids[a] : -1;
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (c >= nc) break;
-      const int id = idv[c];
-      if (id >= 0 && id < E)
-        atomicAdd(&my[id], 1);
-      else if (id != -1)
-        bad = true;
-    }
-  }
+  const bool bad = count_segment<CH>(p.ids, my, E, a_begin, a_end, lane);
   if (__ballot(bad) != 0ull && lane == 0) atomicOr(p.err, 1);
   __syncthreads();
 
@@ -130,52 +199,160 @@ __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
   for (int i = total + tid; i < p.max_padded; i += NT) p.sorted_ids[i] = A;
   // block table
   const int nb = total / p.bm;
-  for (int b = tid; b < p.max_blocks; b += NT) {
-    int e = -1;
-    if (b < nb) {
-      const int row = b * p.bm;
-      int lo = 0, hi = E + 1;  // upper_bound of row in start[0..E]
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (start[mid] <= row) lo = mid + 1; else hi = mid;
-      }
-      e = lo - 1;
-    }
-    p.block_expert[b] = e;
-  }
+  for (int b = tid; b < p.max_blocks; b += NT) p.block_expert[b] = b < nb ? expert_of_row(start, E, b * p.bm) : -1;
   __syncthreads();
 
   // stable placement
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int a1 = a_begin; a1 < a_end; a1 += 64 * CH) {
-    int idv[CH];
-    const int nc = min(CH, (a_end - a1 + 63) >> 6);
+  place_segment<CH>(p.ids, p.sorted_ids, my, E, p.nbits, a_begin, a_end, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Multi-workgroup path.
+struct Align2Params {
+  const int32_t* ids;
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_post_padded;
+  int32_t* err;
+  unsigned* counter;  // control-block word, zero between calls
+  int32_t* cnt;       // [E][G] counts, then first slots
+  int32_t* start;     // [E + 1] scanned padded sizes
+  int32_t* count;     // [E] per-expert totals
+  int A, E, bm, nbits, C, G, max_padded, max_blocks;
+};
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void align_count_kernel(Align2Params p) {
+  extern __shared__ int smem[];
+  int* h = smem;              // [E] this workgroup's counts; last workgroup: padded sizes
+  int* st = smem + p.E;       // [E + 1] (last workgroup)
+  int* M = st + p.E + 1;      // [E][G] every workgroup's counts (last workgroup)
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NT = NW * 64;
+  const int E = p.E;
+  for (int e = tid; e < E; e += NT) h[e] = 0;
+  __syncthreads();
+  const int g = blockIdx.x;
+  const int c0 = g * p.C, c1 = min(p.A, c0 + p.C);
+  const int seg = ((p.C + NW - 1) / NW + 63) & ~63;
+  const int a_begin = min(c1, c0 + wave * seg), a_end = min(c1, a_begin + seg);
+  const bool bad = count_segment<8>(p.ids, h, E, a_begin, a_end, lane);
+  if (__ballot(bad) != 0ull && lane == 0) atomicOr(p.err, 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) p.cnt[(size_t)e * p.G + g] = h[e];
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == (unsigned)(p.G - 1);
+    if (last) __hip_atomic_store(p.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every workgroup's counts are visible
+
+  // every workgroup's counts to LDS, 8 loads per thread in flight
+  const int G = p.G;
+  const int EG = E * G;
+  for (int i0 = tid; i0 < EG; i0 += 8 * NT) {
+    int v[8];
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int a = a1 + 64 * c + lane;
-      idv[c] = (c < nc && a < a_end) ? p.ids[a] : -1;
+    for (int j = 0; j < 8; ++j) v[j] = i0 + j * NT < EG ? p.cnt[i0 + j * NT] : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (i0 + j * NT < EG) M[i0 + j * NT] = v[j];
+  }
+  __syncthreads();
+  // totals and padded sizes (a thread per expert)
+  for (int e = tid; e < E; e += NT) {
+    const int* row = M + e * G;
+    int c = 0;
+    for (int w = 0; w < G; ++w) c += row[w];
+    p.count[e] = c;
+    h[e] = (c + p.bm - 1) / p.bm * p.bm;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int per = (E + 63) / 64;
+    const int lo = min(E, lane * per);
+    const int hi = min(E, lo + per);
+    int run = 0;
+    for (int e = lo; e < hi; ++e) run += h[e];
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
     }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {  // 64 consecutive assignments at a time, in order
-      if (c >= nc) break;
-      const int a = a1 + 64 * c + lane;
-      int id = idv[c];
-      const bool valid = id >= 0 && id < E;
-      if (!valid) id = 0;
-      uint64_t m = __ballot(valid);
-      for (int b = 0; b < p.nbits; ++b) {
-        const bool bit = (id >> b) & 1;
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-      }
-      if (valid) {
-        const int rank = __popcll(m & lt);
-        const int pos = my[id] + rank;
-        p.sorted_ids[pos] = a;
-        if (rank == 0) my[id] += __popcll(m);
-      }
+    int excl = incl - run;
+    for (int e = lo; e < hi; ++e) {
+      st[e] = excl;
+      excl += h[e];
+    }
+    if (lane == 63) st[E] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += NT) p.start[e] = st[e];
+  if (tid == 0) p.num_post_padded[0] = st[E];
+  // first slot of each (expert, workgroup): exclusive scan over g, a
+  // thread per expert
+  for (int e = tid; e < E; e += NT) {
+    const int* row = M + e * G;
+    int32_t* out = p.cnt + (size_t)e * G;
+    int run = st[e];
+    for (int w = 0; w < G; ++w) {
+      const int c = row[w];
+      out[w] = run;
+      run += c;
     }
   }
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void align_place_kernel(Align2Params p) {
+  extern __shared__ int smem[];
+  const int E = p.E;
+  int* cw = smem;                 // [NW][E] per-wave counts, then first slots
+  int* st = smem + NW * E;        // [E + 1]
+  int* ct = st + E + 1;           // [E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NT = NW * 64;
+  const int g = blockIdx.x;
+  for (int i = tid; i < NW * E; i += NT) cw[i] = 0;
+  for (int e = tid; e <= E; e += NT) st[e] = p.start[e];
+  for (int e = tid; e < E; e += NT) ct[e] = p.count[e];
+  __syncthreads();
+  const int c0 = g * p.C, c1 = min(p.A, c0 + p.C);
+  const int seg = ((p.C + NW - 1) / NW + 63) & ~63;
+  const int a_begin = min(c1, c0 + wave * seg), a_end = min(c1, a_begin + seg);
+  int* my = cw + wave * E;
+  count_segment<8>(p.ids, my, E, a_begin, a_end, lane);  // bad ids were flagged by the count launch
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int run = p.cnt[(size_t)e * p.G + g];
+    for (int w = 0; w < NW; ++w) {
+      const int c = cw[w * E + e];
+      cw[w * E + e] = run;
+      run += c;
+    }
+  }
+  // padding slots and the tail: the sentinel
+  const int total = st[E];
+  const int A = p.A;
+  for (int i = g * NT + tid; i < p.max_padded; i += p.G * NT) {
+    if (i >= total) {
+      p.sorted_ids[i] = A;
+    } else {
+      const int e = expert_of_row(st, E, i);
+      if (i - st[e] >= ct[e]) p.sorted_ids[i] = A;
+    }
+  }
+  const int nb = total / p.bm;
+  for (int b = g * NT + tid; b < p.max_blocks; b += p.G * NT)
+    p.block_expert[b] = b < nb ? expert_of_row(st, E, b * p.bm) : -1;
+  __syncthreads();
+  place_segment<8>(p.ids, p.sorted_ids, my, E, p.nbits, a_begin, a_end, lane);
 }
 
 }  // namespace
@@ -183,6 +360,35 @@ __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
 int align_waves(int E) { return E <= 512 ? 16 : 8; }
 
 size_t align_lds_bytes(int E) { return ((size_t)align_waves(E) * E + 2 * E + 1) * sizeof(int); }
+
+// The multi-workgroup path: T*k of at least kAlignMultiMin assignments,
+// chunks of at least 2048 (a multiple of 512) and at most
+// min(256, kAlignMaxCounts / E) workgroups (the last one holds every
+// workgroup's counts in LDS and walks them with a thread per expert).
+#ifndef MOE_ALIGN_MULTI_MIN
+#define MOE_ALIGN_MULTI_MIN 12288
+#endif
+constexpr int kAlignMultiMin = MOE_ALIGN_MULTI_MIN;
+constexpr int kAlignMultiWaves = 8;
+constexpr int kAlignMaxCounts = 16384;
+
+struct AlignSplit {
+  int C, G;
+};
+AlignSplit align_split(int64_t A, int E) {
+  int64_t gmax = kAlignMaxCounts / E;
+  if (gmax > 256) gmax = 256;
+  if (gmax < 1) gmax = 1;
+  int64_t C = (A + gmax - 1) / gmax;
+  if (C < 2048) C = 2048;
+  C = (C + 511) / 512 * 512;
+  return AlignSplit{(int)C, (int)((A + C - 1) / C)};
+}
+bool align_multi(int64_t A) { return A >= kAlignMultiMin; }
+size_t align_scratch_bytes(int64_t A, int E) {
+  if (!align_multi(A)) return 0;
+  return align_up(((size_t)align_split(A, E).G * E + 2 * (size_t)E + 1) * sizeof(int32_t), 256);
+}
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
                           const void* block_expert, const void* num_post_padded) {
@@ -210,6 +416,27 @@ moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
   p.nbits = nbits;
   p.max_padded = (int)align_max_padded(T, k, E, block_m);
   p.max_blocks = (int)align_max_blocks(T, k, E, block_m);
+  if (align_multi(p.A)) {
+    const AlignSplit sp = align_split(p.A, E);
+    Align2Params q;
+    q.ids = ids;
+    q.sorted_ids = sorted_ids;
+    q.block_expert = block_expert;
+    q.num_post_padded = num_post_padded;
+    q.err = p.err;
+    q.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kAlignCounterOffset);
+    q.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kCtrlBytes);
+    q.start = q.cnt + (size_t)sp.G * E;
+    q.count = q.start + E + 1;
+    q.A = p.A; q.E = E; q.bm = block_m; q.nbits = nbits; q.C = sp.C; q.G = sp.G;
+    q.max_padded = p.max_padded; q.max_blocks = p.max_blocks;
+    constexpr int NW = kAlignMultiWaves;
+    align_count_kernel<NW><<<sp.G, NW * 64, ((size_t)E * sp.G + 2 * (size_t)E + 1) * sizeof(int), stream>>>(q);
+    MOE_CHECK_LAUNCH();
+    align_place_kernel<NW><<<sp.G, NW * 64, ((size_t)NW * E + 2 * (size_t)E + 1) * sizeof(int), stream>>>(q);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   const size_t lds = align_lds_bytes(E);
   if (align_waves(E) == 16)
     align_kernel<16><<<1, 16 * 64, lds, stream>>>(p);
@@ -225,7 +452,7 @@ int64_t align_max_padded(int T, int k, int E, int block_m) {
 int64_t align_max_blocks(int T, int k, int E, int block_m) {
   return ceil_div64(align_max_padded(T, k, E, block_m), block_m);
 }
-size_t align_workspace_size() { return kCtrlBytes; }
+size_t align_workspace_size(int T, int k, int E) { return kCtrlBytes + align_scratch_bytes((int64_t)T * k, E); }
 
 }  // namespace moe
 
@@ -236,14 +463,14 @@ extern "C" moe_status moe_align(const int32_t* topk_ids, int T, int k, int E, in
   moe_status st = align_validate(topk_ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded);
   if (st != MOE_OK) return st;
   if (!workspace) return MOE_E_INVAL;
-  if (workspace_bytes < align_workspace_size()) return MOE_E_WORKSPACE;
+  if (workspace_bytes < align_workspace_size(T, k, E)) return MOE_E_WORKSPACE;
   return launch_align(topk_ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, workspace,
                       stream);
 }
 
 extern "C" size_t moe_align_workspace_size(int T, int k, int E) {
-  (void)T; (void)k; (void)E;
-  return moe::align_workspace_size();
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return moe::align_workspace_size(T, k, E);
 }
 extern "C" int64_t moe_align_max_padded(int T, int k, int E, int block_m) {
   return moe::align_max_padded(T, k, E, block_m);

@@ -12,13 +12,15 @@ struct LayerLayout {
   size_t ctrl, ids, w, sorted, bexp, npp, ffn, total;
 };
 
-// The route workspace (control block + logits) sits at offset 0 and its
-// control block doubles as the alignment workspace.
+// The route workspace (control block + group partials) sits at offset 0;
+// the alignment workspace (the same control block + its scratch) overlaps it,
+// the router being done with its partials before the alignment starts.
 LayerLayout layer_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
   LayerLayout L;
   size_t off = 0;
   L.ctrl = off;
-  off += align_up(route_workspace_size(T, H, E), 256);
+  const size_t rw = route_workspace_size(T, H, E), aw = align_workspace_size(T, k, E);
+  off += align_up(rw > aw ? rw : aw, 256);
   L.ids = off;
   off += align_up((size_t)T * k * sizeof(int32_t), 256);
   L.w = off;

@@ -99,6 +99,12 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
     return MOE_E_INVAL;
   if (wformat != MOE_W_BF16 && (!w13_scale || !w2_scale)) return MOE_E_INVAL;
   if (wformat != MOE_W_BF16 && (H % 512 != 0 || F % 512 != 0)) return MOE_E_UNSUPPORTED;
+  // x, the SwiGLU rows and one expert's weights are addressed with 32-bit
+  // byte offsets
+  const uint64_t eb = wformat == MOE_W_BF16 ? 2 : 1, lim = 0xFFFFFFFFull;
+  if ((uint64_t)T * H * eb > lim || (uint64_t)align_max_padded(T, k, E, block_m) * F * eb > lim ||
+      (uint64_t)2 * F * H * eb > lim)
+    return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -228,12 +228,12 @@ __device__ __forceinline__ int a_row_index(const GemmP& p, int blk, int bm, int 
 // ---------------------------------------------------------------------------
 // Tiled kernel.  Tile: BM rows x BNW weight rows (GEMM1: BNW/2 gate rows then
 // the matching BNW/2 up rows = BNW/2 SwiGLU columns; GEMM2: BNW output
-// columns).  Waves 2 x 2: wave (wm, wn) owns rows [wm*BM/2, +BM/2) and weight
-// rows: GEMM1 gate [wn*BNW/4, +BNW/4) and up [BNW/2 + wn*BNW/4, +BNW/4);
-// GEMM2 [wn*BNW/2, +BNW/2).
+// columns).  NW waves as 2 x WN (WN = NW / 2): wave (wm, wn) owns rows
+// [wm*BM/2, +BM/2) and weight rows: GEMM1 gate [wn*BNW/(2 WN), +BNW/(2 WN))
+// and the matching up rows BNW/2 further; GEMM2 [wn*BNW/WN, +BNW/WN).
 //
 // K steps of 128 bytes per row are copied global -> LDS with
-// global_load_lds_dwordx4 (no VGPR staging) into a ring of NS stages, NS - 1
+// buffer_load_dwordx4 ... lds (no VGPR staging) into a ring of NS stages, NS - 1
 // steps ahead of the multiply; one barrier per step.  Inside a stage a row's
 // 16-byte chunk c sits at slot c ^ f(row) (f(row) = (row / (16 / chunks per
 // row)) mod chunks per row), so the 16 rows one MFMA operand read touches
@@ -242,11 +242,23 @@ __device__ __forceinline__ int a_row_index(const GemmP& p, int blk, int bm, int 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 
-__device__ __forceinline__ void g2lds16(const uint8_t* g, uint8_t* lds_dst) {
-  __builtin_amdgcn_global_load_lds((gvoid_t*)g, (lvoid_t*)lds_dst, 16, 0, 0);
-}
+// 4-byte copy of a scale word (flat address)
 __device__ __forceinline__ void g2lds4(const void* g, uint8_t* lds_dst) {
   __builtin_amdgcn_global_load_lds((gvoid_t*)g, (lvoid_t*)lds_dst, 4, 0, 0);
+}
+// 16-byte tile copies use the buffer-resource form: a per-lane 32-bit byte
+// offset, a wave-uniform offset (the K step) and a 4-dword descriptor of the
+// source range (reads at or past `bytes` return zero).  Unlike the
+// flat-address form it lets the compiler keep counting the LDS reads in
+// flight precisely instead of waiting for all of them, and the step offset
+// costs no vector instruction.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ void buf2lds16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lvoid_t*)lds_dst, 16, voff, soff, 0, 0);
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -290,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int wm = wave / WN;
   const int wn = wave % WN;
@@ -309,6 +321,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
   const uint8_t* asrc = G1 ? p.x : p.act;
   const uint8_t* wsrc = G1 ? p.w13 : p.w2;
   const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
+  // A source: the T token rows (GEMM1) or the padded rows (GEMM2)
+  const rsrc_t ra = make_rsrc(asrc, (uint64_t)(G1 ? p.A / p.k : nblk * BM) * rowbytes_a);
 
   // tile-local weight row of fragment fn of this wave
   auto frag_lrow = [&](int fn) {
@@ -330,20 +344,22 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     const int nt = (int)(L % ntn);
     const int e = p.block_expert[blk];
 
-    // per-lane global sources of the copy instructions
-    const uint8_t* ag[LA];
+    // per-lane source offsets of the copy instructions (the K step is added
+    // as a uniform offset)
+    uint32_t ag[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int row = wave * (BM / NW) + 8 * i + (lane >> 3);
       bool v;
       const int src = a_row_index<G1>(p, blk, BM, row, v);  // padding rows read token 0; never used
-      ag[i] = asrc + (size_t)src * rowbytes_a + 16 * swz<8>(lane & 7, row);
+      ag[i] = (uint32_t)src * rowbytes_a + 16 * swz<8>(lane & 7, row);
     }
-    const uint8_t* bg[LB];
+    const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes_b, (uint64_t)erows * rowbytes_b);
+    uint32_t bg[LB];
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int row = (wave * LB + i) * (64 / CPRB) + lane / CPRB;
-      bg[i] = wsrc + ((size_t)e * erows + weight_row(nt, row)) * rowbytes_b + 16 * swz<CPRB>(lane % CPRB, row);
+      bg[i] = (uint32_t)weight_row(nt, row) * rowbytes_b + 16 * swz<CPRB>(lane % CPRB, row);
     }
     // scale words: slot q = (i * NW + wave) * 64 + lane of copy i; q < BM: A
     // row q, q < BM + BNW: B row q - BM.  Per step the source advances by
@@ -383,10 +399,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     auto issue = [&](int s, int slot) {
       uint8_t* st = lds + slot * SSZ;
 #pragma unroll
-      for (int i = 0; i < LA; ++i) g2lds16(ag[i] + (size_t)s * 128, st + (wave * (BM / NW) + 8 * i) * 128);
+      for (int i = 0; i < LA; ++i) buf2lds16(ra, ag[i], s * 128, st + (wave * (BM / NW) + 8 * i) * 128);
 #pragma unroll
-      for (int i = 0; i < LB; ++i)
-        g2lds16(bg[i] + (size_t)s * T::BROW, st + ASZ + (wave * LB + i) * (64 / CPRB) * T::BROW);
+      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * T::BROW, st + ASZ + (wave * LB + i) * (64 / CPRB) * T::BROW);
 #pragma unroll
       for (int i = 0; i < LSC; ++i) g2lds4(scg[i] + (size_t)s * sc_step[i], st + ASZ + BSZ + (i * NW + wave) * 256);
     };
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     // nk - 1 again, into slots no later step reads), so the wait count is
     // the same every time.
     auto next_step = [&](int sn) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
       wait_vm<(D - 1) * LS>();
       barrier_no_fence();
       issue(sn + D < nk ? sn + D : nk - 1, (sn + D) % NS);
@@ -482,18 +497,27 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     if constexpr (F == F_BF16) {
       // Software pipeline: the fragments of the next sub-step are read from
       // LDS while the matrix cores work on the current one.
+      // The last step is peeled so the loop body is straight-line code and
+      // the LDS read counts the compiler waits for are exact; scheduling
+      // barriers keep each group of reads ahead of the multiplies they
+      // overlap with.
       Frag f0, f1;
       next_step(0);
       rd(0, 0, f0);
-      for (int s = 0; s < nk; ++s) {
+      for (int s = 0; s + 1 < nk; ++s) {
         rd(s, 1, f1);
+        __builtin_amdgcn_sched_barrier(0);
         mm(f0);
-        if (s + 1 < nk) {
-          next_step(s + 1);
-          rd(s + 1, 0, f0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        next_step(s + 1);
+        rd(s + 1, 0, f0);
+        __builtin_amdgcn_sched_barrier(0);
         mm(f1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      rd(nk - 1, 1, f1);
+      mm(f0);
+      mm(f1);
     } else {
       // one sub-step per step; a second fragment buffer does not fit the
       // register file next to the accumulators at BLOCK_M 128
@@ -964,7 +988,7 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   switch (a.block_m) {
     case 32: return which == 1 ? launch_tiled_one<F, true, 32, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 32, 128, 3>(p, t2, s);
     case 64:
-      if (which == 1) return launch_tiled_one<F, true, 64, 256, 3, NW>(p, t1, s);
+      if (which == 1) return launch_tiled_one<F, true, 64, 256, (F == F_BF16 ? 4 : 3), NW>(p, t1, s);
       if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
       return launch_tiled_one<F, false, 64, 128, 3, NW>(p, t2, s);
     case 128:

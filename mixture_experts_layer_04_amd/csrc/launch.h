@@ -13,8 +13,10 @@ namespace moe {
 // workspace, the words in it only ever hold what their owners leave there
 // (zero after each call):
 //   [0, 4)            sticky alignment error bits
+//   [4, 8)            alignment counter (multi-workgroup path)
 //   [256, kCtrlBytes) one counter per router token tile
 constexpr size_t kCtrlBytes = 65536;
+constexpr size_t kAlignCounterOffset = 4;
 constexpr size_t kCounterOffset = 256;
 constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);
 
@@ -27,7 +29,7 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
                           const void* block_expert, const void* num_post_padded);
-size_t align_workspace_size();
+size_t align_workspace_size(int T, int k, int E);
 int64_t align_max_padded(int T, int k, int E, int block_m);
 int64_t align_max_blocks(int T, int k, int E, int block_m);
 moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,

@@ -91,6 +91,10 @@ def test_ffn_and_layer_argument_checks(L):
     assert ffn(wf=1, s13=None) == 1   # fp8 needs scales
     assert ffn(nbytes=100) == 3
     assert ffn(T=0) == 0
+    # 32-bit byte offsets: x of 300000 x 7168 bf16 and one expert's w13 of
+    # 2 x 32768 x 32768 bf16 are 4 GiB or more
+    assert ffn(T=300000, H=7168, F=2048, E=256, k=8, bm=128) == 2
+    assert ffn(T=4, H=32768, F=32768) == 2
 
     def layer(T=4, H=256, E=8, F=128, k=2, bm=0, ws=FAKE, nbytes=1 << 30):
         return L.moe_layer(FAKE, FAKE, None, 0, FAKE, None, FAKE, None, T, H, E, F, k, 1, 1, 0, 1, 1.0, bm,

@@ -39,6 +39,9 @@ CASES = [
     (2048, 8, 256, 64, "skewed"), (37, 3, 1024, 32, "uniform"), (333, 8, 600, 16, "skewed"),
     (100, 4, 16, 16, "hot"), (5000, 2, 8, 128, "uniform"), (16, 2, 8, 16, "uniform"),
     (1, 1, 1, 16, "uniform"), (77, 6, 256, 1, "uniform"),
+    # around the switch to the multi-workgroup path (12288 assignments)
+    (12287, 1, 64, 16, "uniform"), (6144, 2, 64, 16, "skewed"), (1536, 8, 1024, 16, "uniform"),
+    (65536, 8, 256, 128, "uniform"), (13000, 1, 1, 64, "uniform"),
 ]
 
 
@@ -73,3 +76,23 @@ def test_align_invalid_ids_are_skipped_and_flagged():
     ids = torch.tensor([[0, -1]], dtype=torch.int32).cuda()
     moe.align(ids, 4, 16, ws=ws)
     assert moe.debug_error(ws) == 0  # -1 alone is not an error
+
+
+def test_align_invalid_ids_multi_workgroup():
+    import mixture_experts_layer_04_amd as moe
+    T, k, E, bm = 4096, 4, 64, 32
+    ids = make_topk_ids(T, k, E, seed=7, device="cuda")
+    ids[5, 1] = -1
+    ids[100, 0] = E + 3
+    ids[4000, 3] = -7
+    ws = torch.zeros(moe.lib().moe_align_workspace_size(T, k, E), dtype=torch.uint8, device="cuda")
+    s, b, n = moe.align(ids, E, bm, ws=ws)
+    so, bo, no, bad = oracle_align(ids, E, bm)
+    assert bad and s.cpu().tolist() == so and b.cpu().tolist() == bo and int(n.item()) == no
+    assert moe.debug_error(ws) == 1
+    ids[100, 0] = 0
+    ids[4000, 3] = 1
+    s, b, n = moe.align(ids, E, bm, ws=ws)  # the counter left at zero: a second call works
+    so, bo, no, _ = oracle_align(ids, E, bm)
+    assert s.cpu().tolist() == so and b.cpu().tolist() == bo and int(n.item()) == no
+    assert moe.debug_error(ws) == 0
