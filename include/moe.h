@@ -164,6 +164,34 @@ int64_t moe_align_max_padded(int T, int k, int E, int block_m);
 int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
 
 /* ------------------------------------------------------------------------
+ * moe_route_align - moe_route followed by moe_align in one call, one
+ * launch while T <= 256 ([Router] §6 and §6.1: one routing stage that
+ * scores, selects, counts and sorts; [Router] §8.1: the gate product stays
+ * expert-parallel, the selection row-parallel).
+ *
+ * Arguments as moe_route (without logits_out) and moe_align, with the same
+ * layouts, ownership and results: topk_ids / topk_weights are written and
+ * then aligned with block_m.  The outputs equal those of moe_route followed
+ * by moe_align on the same stream, bit for bit.  For T <= 256 the router's
+ * workgroups compute the gate product and each token tile's last one
+ * selects its tokens; the last token tile to finish then aligns all T*k
+ * assignments in the same launch.  For T > 256 the router's two launches
+ * run, then moe_align's.
+ * Errors: as moe_route and moe_align (validated on the host before anything
+ * is enqueued); the workspace must hold
+ * moe_route_align_workspace_size(T, H, E, k) bytes.
+ * ------------------------------------------------------------------------ */
+moe_status moe_route_align(const void* x, const float* gate, const float* bias,
+                           int T, int H, int E, int k, int n_group, int topk_group,
+                           int scoring, int renormalize, float routed_scale,
+                           int block_m, int32_t* topk_ids, float* topk_weights,
+                           int32_t* sorted_ids, int32_t* block_expert,
+                           int32_t* num_post_padded,
+                           void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+size_t moe_route_align_workspace_size(int T, int H, int E, int k);
+
+/* ------------------------------------------------------------------------
  * moe_expert_ffn - grouped expert GEMMs and combine ([Kernels] "The fused
  * expert GEMM" and "Combine"; [MoE] align-then-index path; [MegaMoE] §1.1,
  * §3.5).

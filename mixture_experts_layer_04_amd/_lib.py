@@ -25,6 +25,9 @@ SIGNATURES = {
     "moe_status_str": (ctypes.c_char_p, [_i]),
     "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_workspace_size": (_sz, [_i, _i, _i]),
+    "moe_route_align": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _sz, _vp]),
+    "moe_route_align_workspace_size": (_sz, [_i, _i, _i, _i]),
     "moe_align": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_align_workspace_size": (_sz, [_i, _i, _i]),
     "moe_align_max_padded": (_i64, [_i, _i, _i, _i]),

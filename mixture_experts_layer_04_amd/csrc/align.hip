@@ -1,4 +1,5 @@
-// Block alignment: one launch of one workgroup for small T*k, two
+// Block alignment: one launch of one workgroup for small T*k (the device
+// code in align_block.h, which the router's fused launch shares), two
 // multi-workgroup launches (count, place) for large T*k.
 //
 // [MoE] "vLLM's Triton path: align, then index" (per-expert counts, each
@@ -7,31 +8,20 @@
 // tileable" (flat assignment ids, sentinel T*k, worst-case sizing
 // T*k + E*(BLOCK_M-1) so the padded length can stay on the device).
 //
-// Unlike an atomic-add placement, every position here is decided without
-// atomics, so the layout is deterministic and stable (ascending assignment id
-// within an expert):
-//   1. each wave owns one contiguous segment of the assignments and counts its
-//      ids per expert into its own LDS row cnt[w][e];
-//   2. counts are summed over waves, padded to a multiple of BLOCK_M and
-//      scanned (wave 0); cnt[w][e] becomes wave w's first slot for expert e;
-//   3. each wave walks its segment again 64 assignments at a time; lanes with
-//      equal ids find each other with one ballot per id bit, take
-//      rank = #equal lanes below them, and the lowest such lane advances
-//      cnt[w][e] by the group size.
-// Padding slots and the tail get the sentinel T*k; block_expert is filled by
-// a binary search of the scanned starts and -1 past the padded length.
-//
-// For large T*k the same steps are spread over G workgroups, workgroup g
-// owning the contiguous chunk [g*C, (g+1)*C) of assignments:
+// Unlike an atomic-add placement, every position is decided without atomics,
+// so the layout is deterministic and stable (ascending assignment id within
+// an expert).  For large T*k the steps are spread over G workgroups,
+// workgroup g owning the contiguous chunk [g*C, (g+1)*C) of assignments:
 //   count: each workgroup writes its per-expert counts cnt[e][g]; the last
-//          one to finish (agent-scope counter) sums, pads and scans them (a
-//          wave per expert) and turns cnt[e][g] into workgroup g's first slot
-//          for expert e;
+//          one to finish (agent-scope counter) sums, pads and scans them and
+//          turns cnt[e][g] into workgroup g's first slot for expert e;
+//          The count launch also fills every slot with the sentinel;
 //   place: each workgroup recounts its chunk per wave, offsets the waves
-//          from cnt[g][e] and places as in step 3; all workgroups share the
-//          sentinel fill and the block table.
+//          from cnt[e][g] and places as the one-workgroup kernel does; all
+//          workgroups share the block table.
 // Positions are the same as in the one-workgroup kernel.
 
+#include "align_block.h"
 #include "common.h"
 #include "launch.h"
 
@@ -39,171 +29,10 @@ namespace moe {
 
 namespace {
 
-struct AlignParams {
-  const int32_t* ids;
-  int32_t* sorted_ids;
-  int32_t* block_expert;
-  int32_t* num_post_padded;
-  int32_t* err;
-  int A, E, bm, nbits;
-  int max_padded, max_blocks;
-};
-
-// expert owning padded row `row`: upper_bound of row in start[0..E], minus one
-__device__ __forceinline__ int expert_of_row(const int* start, int E, int row) {
-  int lo = 0, hi = E + 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (start[mid] <= row) lo = mid + 1; else hi = mid;
-  }
-  return lo - 1;
-}
-
-// Stable placement of the assignments [a_begin, a_end) of one wave, 64 at a
-// time, ids read CH per lane at once; first[e] is the wave's next slot for
-// expert e (LDS, advanced here).
-template <int CH>
-__device__ __forceinline__ void place_segment(const int32_t* ids, int32_t* sorted_ids, int* first, int E, int nbits,
-                                              int a_begin, int a_end, int lane) {
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int a1 = a_begin; a1 < a_end; a1 += 64 * CH) {
-    int idv[CH];
-    const int nc = min(CH, (a_end - a1 + 63) >> 6);
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int a = a1 + 64 * c + lane;
-      idv[c] = (c < nc && a < a_end) ? ids[a] : -1;
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {  // 64 consecutive assignments at a time, in order
-      if (c >= nc) break;
-      const int a = a1 + 64 * c + lane;
-      int id = idv[c];
-      const bool valid = id >= 0 && id < E;
-      if (!valid) id = 0;
-      uint64_t m = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (id >> b) & 1;
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-      }
-      if (valid) {
-        const int rank = __popcll(m & lt);
-        const int pos = first[id] + rank;
-        sorted_ids[pos] = a;
-        if (rank == 0) first[id] += __popcll(m);
-      }
-    }
-  }
-}
-
-// Count the valid ids of [a_begin, a_end) into hist (LDS atomics), CH ids
-// per lane in flight; returns whether an id outside [0, E) other than -1
-// was seen.
-template <int CH>
-__device__ __forceinline__ bool count_segment(const int32_t* ids, int* hist, int E, int a_begin, int a_end, int lane) {
-  bool bad = false;
-  for (int a0 = a_begin; a0 < a_end; a0 += 64 * CH) {
-    int idv[CH];
-    const int nc = min(CH, (a_end - a0 + 63) >> 6);  // sub-chunks of 64 holding ids
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int a = a0 + 64 * c + lane;
-      idv[c] = (c < nc && a < a_end) ? ids[a] : -1;
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (c >= nc) break;
-      const int id = idv[c];
-      if (id >= 0 && id < E)
-        atomicAdd(&hist[id], 1);
-      else if (id != -1)
-        bad = true;
-    }
-  }
-  return bad;
-}
-
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
   extern __shared__ int smem[];
-  int* cnt = smem;                   // [NW][E]
-  int* start = smem + NW * p.E;      // [E + 1]
-  int* count = start + p.E + 1;      // [E]
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int NT = NW * 64;
-  const int A = p.A;
-  const int E = p.E;
-
-  // segment of this wave, a multiple of 64 long
-  const int seg = ((A + NW - 1) / NW + 63) & ~63;
-  const int a_begin = min(A, wave * seg);
-  const int a_end = min(A, a_begin + seg);
-
-  int* my = cnt + wave * E;
-  for (int e = lane; e < E; e += 64) my[e] = 0;
-  // ids are read CH per lane at a time (all loads in flight together)
-  constexpr int CH = 16;
-  const bool bad = count_segment<CH>(p.ids, my, E, a_begin, a_end, lane);
-  if (__ballot(bad) != 0ull && lane == 0) atomicOr(p.err, 1);
-  __syncthreads();
-
-  // per-expert totals and padded sizes
-  for (int e = tid; e < E; e += NT) {
-    int c = 0;
-    for (int w = 0; w < NW; ++w) c += cnt[w * E + e];
-    count[e] = c;
-    start[e] = (c + p.bm - 1) / p.bm * p.bm;  // padded, scanned below
-  }
-  __syncthreads();
-
-  // exclusive scan of the padded sizes by wave 0 (each lane a run of E/64)
-  if (wave == 0) {
-    const int per = (E + 63) / 64;
-    const int lo = min(E, lane * per);
-    const int hi = min(E, lo + per);
-    int run = 0;
-    for (int e = lo; e < hi; ++e) run += start[e];
-    int incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    int excl = incl - run;
-    for (int e = lo; e < hi; ++e) {
-      const int v = start[e];
-      start[e] = excl;
-      excl += v;
-    }
-    if (lane == 63) start[E] = incl;
-  }
-  __syncthreads();
-
-  const int total = start[E];
-  if (tid == 0) p.num_post_padded[0] = total;
-  // first slot of each (wave, expert)
-  for (int e = tid; e < E; e += NT) {
-    int run = start[e];
-    for (int w = 0; w < NW; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = run;
-      run += c;
-    }
-  }
-  // sentinel in the padding of each expert and in the tail
-  for (int e = tid; e < E; e += NT)
-    for (int i = start[e] + count[e]; i < start[e + 1]; ++i) p.sorted_ids[i] = A;
-  for (int i = total + tid; i < p.max_padded; i += NT) p.sorted_ids[i] = A;
-  // block table
-  const int nb = total / p.bm;
-  for (int b = tid; b < p.max_blocks; b += NT) p.block_expert[b] = b < nb ? expert_of_row(start, E, b * p.bm) : -1;
-  __syncthreads();
-
-  // stable placement
-  place_segment<CH>(p.ids, p.sorted_ids, my, E, p.nbits, a_begin, a_end, lane);
+  align_block<NW>(p, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -217,7 +46,6 @@ struct Align2Params {
   unsigned* counter;  // control-block word, zero between calls
   int32_t* cnt;       // [E][G] counts, then first slots
   int32_t* start;     // [E + 1] scanned padded sizes
-  int32_t* count;     // [E] per-expert totals
   int A, E, bm, nbits, C, G, max_padded, max_blocks;
 };
 
@@ -232,6 +60,7 @@ __global__ __launch_bounds__(NW * 64) void align_count_kernel(Align2Params p) {
   const int NT = NW * 64;
   const int E = p.E;
   for (int e = tid; e < E; e += NT) h[e] = 0;
+  for (int i = blockIdx.x * NT + tid; i < p.max_padded; i += p.G * NT) p.sorted_ids[i] = p.A;
   __syncthreads();
   const int g = blockIdx.x;
   const int c0 = g * p.C, c1 = min(p.A, c0 + p.C);
@@ -269,7 +98,6 @@ __global__ __launch_bounds__(NW * 64) void align_count_kernel(Align2Params p) {
     const int* row = M + e * G;
     int c = 0;
     for (int w = 0; w < G; ++w) c += row[w];
-    p.count[e] = c;
     h[e] = (c + p.bm - 1) / p.bm * p.bm;
   }
   __syncthreads();
@@ -315,13 +143,11 @@ __global__ __launch_bounds__(NW * 64) void align_place_kernel(Align2Params p) {
   const int E = p.E;
   int* cw = smem;                 // [NW][E] per-wave counts, then first slots
   int* st = smem + NW * E;        // [E + 1]
-  int* ct = st + E + 1;           // [E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NT = NW * 64;
   const int g = blockIdx.x;
   for (int i = tid; i < NW * E; i += NT) cw[i] = 0;
   for (int e = tid; e <= E; e += NT) st[e] = p.start[e];
-  for (int e = tid; e < E; e += NT) ct[e] = p.count[e];
   __syncthreads();
   const int c0 = g * p.C, c1 = min(p.A, c0 + p.C);
   const int seg = ((p.C + NW - 1) / NW + 63) & ~63;
@@ -337,17 +163,7 @@ __global__ __launch_bounds__(NW * 64) void align_place_kernel(Align2Params p) {
       run += c;
     }
   }
-  // padding slots and the tail: the sentinel
   const int total = st[E];
-  const int A = p.A;
-  for (int i = g * NT + tid; i < p.max_padded; i += p.G * NT) {
-    if (i >= total) {
-      p.sorted_ids[i] = A;
-    } else {
-      const int e = expert_of_row(st, E, i);
-      if (i - st[e] >= ct[e]) p.sorted_ids[i] = A;
-    }
-  }
   const int nb = total / p.bm;
   for (int b = g * NT + tid; b < p.max_blocks; b += p.G * NT)
     p.block_expert[b] = b < nb ? expert_of_row(st, E, b * p.bm) : -1;
@@ -359,7 +175,7 @@ __global__ __launch_bounds__(NW * 64) void align_place_kernel(Align2Params p) {
 
 int align_waves(int E) { return E <= 512 ? 16 : 8; }
 
-size_t align_lds_bytes(int E) { return ((size_t)align_waves(E) * E + 2 * E + 1) * sizeof(int); }
+size_t align_lds_bytes(int E) { return ((size_t)align_waves(E) * E + E + 1) * sizeof(int); }
 
 // The multi-workgroup path: T*k of at least kAlignMultiMin assignments,
 // chunks of at least 2048 (a multiple of 512) and at most
@@ -387,7 +203,7 @@ AlignSplit align_split(int64_t A, int E) {
 bool align_multi(int64_t A) { return A >= kAlignMultiMin; }
 size_t align_scratch_bytes(int64_t A, int E) {
   if (!align_multi(A)) return 0;
-  return align_up(((size_t)align_split(A, E).G * E + 2 * (size_t)E + 1) * sizeof(int32_t), 256);
+  return align_up(((size_t)align_split(A, E).G * E + (size_t)E + 1) * sizeof(int32_t), 256);
 }
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
@@ -400,8 +216,8 @@ moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, 
   return MOE_OK;
 }
 
-moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream) {
+AlignParams align_params(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                         int32_t* block_expert, int32_t* num_post_padded, void* ws) {
   AlignParams p;
   p.ids = ids;
   p.sorted_ids = sorted_ids;
@@ -416,6 +232,13 @@ moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
   p.nbits = nbits;
   p.max_padded = (int)align_max_padded(T, k, E, block_m);
   p.max_blocks = (int)align_max_blocks(T, k, E, block_m);
+  return p;
+}
+
+moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream) {
+  const AlignParams p = align_params(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws);
+  const int nbits = p.nbits;
   if (align_multi(p.A)) {
     const AlignSplit sp = align_split(p.A, E);
     Align2Params q;
@@ -427,13 +250,12 @@ moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
     q.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kAlignCounterOffset);
     q.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kCtrlBytes);
     q.start = q.cnt + (size_t)sp.G * E;
-    q.count = q.start + E + 1;
     q.A = p.A; q.E = E; q.bm = block_m; q.nbits = nbits; q.C = sp.C; q.G = sp.G;
     q.max_padded = p.max_padded; q.max_blocks = p.max_blocks;
     constexpr int NW = kAlignMultiWaves;
     align_count_kernel<NW><<<sp.G, NW * 64, ((size_t)E * sp.G + 2 * (size_t)E + 1) * sizeof(int), stream>>>(q);
     MOE_CHECK_LAUNCH();
-    align_place_kernel<NW><<<sp.G, NW * 64, ((size_t)NW * E + 2 * (size_t)E + 1) * sizeof(int), stream>>>(q);
+    align_place_kernel<NW><<<sp.G, NW * 64, ((size_t)NW * E + (size_t)E + 1) * sizeof(int), stream>>>(q);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
   }

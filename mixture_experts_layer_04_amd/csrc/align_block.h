@@ -1,0 +1,193 @@
+// Block alignment in one workgroup: the device code shared by the alignment
+// kernel and the router's fused route + align launch.
+//
+// [MoE] "vLLM's Triton path: align, then index" and [Kernels] "Alignment:
+// making ragged routing tileable": per-expert counts rounded up to whole
+// blocks, exclusive scan, expert e's assignments in ascending order from its
+// start, the sentinel T*k elsewhere, a block-to-expert table with -1 after
+// the padded length.  Every position is decided without atomics:
+//   1. each wave owns one contiguous segment of the assignments and counts its
+//      ids per expert into its own LDS row cnt[w][e];
+//   2. counts are summed over waves, padded to a multiple of BLOCK_M and
+//      scanned (wave 0); cnt[w][e] becomes wave w's first slot for expert e;
+//   3. each wave walks its segment again 64 assignments at a time; lanes with
+//      equal ids find each other with one ballot per id bit, take
+//      rank = #equal lanes below them, and the lowest such lane advances
+//      cnt[w][e] by the group size.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct AlignParams {
+  const int32_t* ids;
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_post_padded;
+  int32_t* err;
+  int A, E, bm, nbits;
+  int max_padded, max_blocks;
+};
+
+// AlignParams of one call (the error word at the start of the workspace).
+AlignParams align_params(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
+                         int32_t* block_expert, int32_t* num_post_padded, void* ws);
+
+// expert owning padded row `row`: upper_bound of row in start[0..E], minus one
+__device__ __forceinline__ int expert_of_row(const int* start, int E, int row) {
+  int lo = 0, hi = E + 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (start[mid] <= row) lo = mid + 1; else hi = mid;
+  }
+  return lo - 1;
+}
+
+// Stable placement of the assignments [a_begin, a_end) of one wave, 64 at a
+// time, ids read CH per lane at once; first[e] is the wave's next slot for
+// expert e (LDS, advanced here).
+template <int CH>
+__device__ __forceinline__ void place_segment(const int32_t* ids, int32_t* sorted_ids, int* first, int E, int nbits,
+                                              int a_begin, int a_end, int lane) {
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int a1 = a_begin; a1 < a_end; a1 += 64 * CH) {
+    int idv[CH];
+    const int nc = min(CH, (a_end - a1 + 63) >> 6);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int a = a1 + 64 * c + lane;
+      idv[c] = (c < nc && a < a_end) ? ids[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {  // 64 consecutive assignments at a time, in order
+      if (c >= nc) break;
+      const int a = a1 + 64 * c + lane;
+      int id = idv[c];
+      const bool valid = id >= 0 && id < E;
+      if (!valid) id = 0;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (id >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      if (valid) {
+        const int rank = __popcll(m & lt);
+        const int pos = first[id] + rank;
+        sorted_ids[pos] = a;
+        if (rank == 0) first[id] += __popcll(m);
+      }
+    }
+  }
+}
+
+// Count the valid ids of [a_begin, a_end) into hist (LDS atomics), CH ids
+// per lane in flight; returns whether an id outside [0, E) other than -1
+// was seen.
+template <int CH>
+__device__ __forceinline__ bool count_segment(const int32_t* ids, int* hist, int E, int a_begin, int a_end, int lane) {
+  bool bad = false;
+  for (int a0 = a_begin; a0 < a_end; a0 += 64 * CH) {
+    int idv[CH];
+    const int nc = min(CH, (a_end - a0 + 63) >> 6);  // sub-chunks of 64 holding ids
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int a = a0 + 64 * c + lane;
+      idv[c] = (c < nc && a < a_end) ? ids[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (c >= nc) break;
+      const int id = idv[c];
+      if (id >= 0 && id < E)
+        atomicAdd(&hist[id], 1);
+      else if (id != -1)
+        bad = true;
+    }
+  }
+  return bad;
+}
+
+// The whole alignment in one workgroup of NW waves (threadIdx.x < NW * 64);
+// smem holds (NW * E + E + 1) ints.  Every slot first gets the sentinel
+// (coalesced stores); the placement overwrites the assignment slots after a
+// wait for those stores and a barrier.
+template <int NW>
+__device__ __forceinline__ void align_block(const AlignParams& p, int* smem) {
+  int* cnt = smem;                   // [NW][E]
+  int* start = smem + NW * p.E;      // [E + 1]
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int NT = NW * 64;
+  const int A = p.A;
+  const int E = p.E;
+
+  // segment of this wave, a multiple of 64 long
+  const int seg = ((A + NW - 1) / NW + 63) & ~63;
+  const int a_begin = min(A, wave * seg);
+  const int a_end = min(A, a_begin + seg);
+
+  for (int i = tid; i < p.max_padded; i += NT) p.sorted_ids[i] = A;
+  int* my = cnt + wave * E;
+  for (int e = lane; e < E; e += 64) my[e] = 0;
+  // ids are read CH per lane at a time (all loads in flight together)
+  constexpr int CH = 16;
+  const bool bad = count_segment<CH>(p.ids, my, E, a_begin, a_end, lane);
+  if (__ballot(bad) != 0ull && lane == 0) atomicOr(p.err, 1);
+  __syncthreads();
+
+  // per-expert totals and padded sizes
+  for (int e = tid; e < E; e += NT) {
+    int c = 0;
+    for (int w = 0; w < NW; ++w) c += cnt[w * E + e];
+    start[e] = (c + p.bm - 1) / p.bm * p.bm;  // padded, scanned below
+  }
+  __syncthreads();
+
+  // exclusive scan of the padded sizes by wave 0 (each lane a run of E/64)
+  if (wave == 0) {
+    const int per = (E + 63) / 64;
+    const int lo = min(E, lane * per);
+    const int hi = min(E, lo + per);
+    int run = 0;
+    for (int e = lo; e < hi; ++e) run += start[e];
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    int excl = incl - run;
+    for (int e = lo; e < hi; ++e) {
+      const int v = start[e];
+      start[e] = excl;
+      excl += v;
+    }
+    if (lane == 63) start[E] = incl;
+  }
+  __syncthreads();
+
+  const int total = start[E];
+  if (tid == 0) p.num_post_padded[0] = total;
+  // first slot of each (wave, expert)
+  for (int e = tid; e < E; e += NT) {
+    int run = start[e];
+    for (int w = 0; w < NW; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+  }
+  // block table
+  const int nb = total / p.bm;
+  for (int b = tid; b < p.max_blocks; b += NT) p.block_expert[b] = b < nb ? expert_of_row(start, E, b * p.bm) : -1;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the sentinel stores are done
+  __syncthreads();
+
+  // stable placement
+  place_segment<CH>(p.ids, p.sorted_ids, my, E, p.nbits, a_begin, a_end, lane);
+}
+
+}  // namespace moe

@@ -19,8 +19,7 @@ LayerLayout layer_layout(int T, int H, int E, int F, int k, int block_m, int wfo
   LayerLayout L;
   size_t off = 0;
   L.ctrl = off;
-  const size_t rw = route_workspace_size(T, H, E), aw = align_workspace_size(T, k, E);
-  off += align_up(rw > aw ? rw : aw, 256);
+  off += align_up(route_align_workspace_size(T, H, E, k), 256);
   L.ids = off;
   off += align_up((size_t)T * k * sizeof(int32_t), 256);
   L.w = off;
@@ -126,10 +125,8 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   int32_t* bexp = reinterpret_cast<int32_t*>(b + L.bexp);
   int32_t* npp = reinterpret_cast<int32_t*>(b + L.npp);
 
-  st = launch_route(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, ids, w,
-                    nullptr, b + L.ctrl, stream);
-  if (st != MOE_OK) return st;
-  st = launch_align(ids, T, k, E, block_m, sorted, bexp, npp, b + L.ctrl, stream);
+  st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+                          block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream);
   if (st != MOE_OK) return st;
   FfnArgs a;
   a.x = x; a.wformat = wformat;

@@ -14,9 +14,11 @@ namespace moe {
 // (zero after each call):
 //   [0, 4)            sticky alignment error bits
 //   [4, 8)            alignment counter (multi-workgroup path)
+//   [8, 12)           fused route + align counter (token tiles done)
 //   [256, kCtrlBytes) one counter per router token tile
 constexpr size_t kCtrlBytes = 65536;
 constexpr size_t kAlignCounterOffset = 4;
+constexpr size_t kFusedCounterOffset = 8;
 constexpr size_t kCounterOffset = 256;
 constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);
 
@@ -26,6 +28,15 @@ size_t route_workspace_size(int T, int H, int E);
 moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream);
+
+// Route + align in one call: one launch while T <= 256 (the router's decode
+// layout, whose last token tile aligns every assignment), else the router's
+// two launches and launch_align.
+moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+                              int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
+                              int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream);
+size_t route_align_workspace_size(int T, int H, int E, int k);
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
                           const void* block_expert, const void* num_post_padded);

@@ -26,12 +26,16 @@
 //    last (nobody waits); it adds the G_j, then runs the selection for the
 //    tile's tokens, one wave per token, with the E logits in VGPRs (slot s of
 //    lane l is expert s*64 + l), and resets the counter.
+//    With the alignment fused in (route + align in one launch), the last
+//    token tile to finish (a second agent-scope counter) then runs the
+//    one-workgroup block alignment over all T*k assignments.
 //  * large T (prefill, T > 256, where a second launch is cheap next to the
 //    layer): a tiled logits kernel (64 tokens x 64 experts per workgroup,
 //    each gate value split once per 64 tokens into LDS planes) writes fp32
 //    logits, then a row-parallel kernel runs the same selection, one wave per
 //    token.
 
+#include "align_block.h"
 #include "common.h"
 #include "launch.h"
 
@@ -51,6 +55,7 @@ struct RouteParams {
   float* part;        // decode layout: group sums [NG][T][E]
   float* logits_out;  // optional [T][E]
   unsigned* counters;
+  unsigned* fused_counter;  // route + align: token tiles done
   int32_t* ids;
   float* weights;
   int T, H, E, k, n_group, topk_group, scoring, renorm;
@@ -98,9 +103,10 @@ __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t& a, const bf16x8_t& bh, 
 // s*64 + lane, -inf past E); writes ids / weights of token t.  Every
 // arg-max is a wave max of the keys (DPP) followed by one ballot per slot
 // for the lowest expert id holding that key.
+// sid (optional, LDS): the token's k ids are also stored there.
 template <int SLOTS>
 __device__ __forceinline__ void select_token(const RouteParams& p, int t, const float (&l)[SLOTS],
-                                             const float (&bv)[SLOTS]) {
+                                             const float (&bv)[SLOTS], int* sid = nullptr) {
   const int lane = threadIdx.x & 63;
   float key[SLOTS], sc[SLOTS];
   bool ok[SLOTS];
@@ -217,6 +223,7 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
   if (lane < p.k) {
     p.ids[(size_t)t * p.k + lane] = sel_id;
     p.weights[(size_t)t * p.k + lane] = wgt;
+    if (sid) sid[lane] = sel_id;
   }
 }
 
@@ -267,9 +274,11 @@ __device__ __forceinline__ void sum_groups(const RouteParams& p, int t, float (&
 }
 
 // ---------------------------------------------------------------------------
-// Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token tiles.
-template <int SLOTS>
-__global__ __launch_bounds__(256) void route_small(RouteParams p) {
+// Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token
+// tiles.  FUSE: the last token tile also aligns (dynamic LDS of
+// (5 E + 1) ints); with a single token tile, from the ids it keeps in LDS.
+template <int SLOTS, bool FUSE>
+__global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
@@ -281,6 +290,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p) {
   const int c = j * CPG + wave;
   __shared__ float red[CPG][16][17];
   __shared__ int s_last;
+  __shared__ int s_ids[FUSE ? 16 * 16 : 1];  // FUSE: the tile's ids [16][k]
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (c < p.NC) {
@@ -340,7 +350,29 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p) {
     load_bias<SLOTS>(p, bv);
     float l[SLOTS];
     sum_groups<SLOTS>(p, t, l);
-    select_token<SLOTS>(p, t, l, bv);
+    select_token<SLOTS>(p, t, l, bv, FUSE ? s_ids + tl * p.k : nullptr);
+  }
+  if constexpr (FUSE) {
+    extern __shared__ int smem[];
+    if (gridDim.y == 1) {  // this workgroup selected every token
+      __syncthreads();
+      AlignParams lp = ap;
+      lp.ids = s_ids;
+      align_block<4>(lp, smem);
+      return;
+    }
+    __syncthreads();  // this tile's ids are written
+    if (threadIdx.x == 0) {
+      const unsigned prev =
+          __hip_atomic_fetch_add(p.fused_counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = prev == (unsigned)(gridDim.y - 1);
+      if (last) __hip_atomic_store(p.fused_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every tile's ids are visible
+    align_block<4>(ap, smem);
   }
 }
 
@@ -482,15 +514,19 @@ __global__ __launch_bounds__(256) void route_select(RouteParams p) {
 
 bool use_large(int T, int E) { (void)E; return T > SMALL_T_MAX; }
 
+// ap: the alignment to fuse into the decode layout, or nullptr
 template <int SLOTS>
-moe_status launch_slots(const RouteParams& p, hipStream_t stream) {
+moe_status launch_slots(const RouteParams& p, const AlignParams* ap, hipStream_t stream) {
   if (use_large(p.T, p.E)) {
     route_logits_group<<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE), p.NG), 256, 0, stream>>>(p);
     MOE_CHECK_LAUNCH();
     route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
   } else {
     dim3 grid(p.NF * p.NG, ceil_div(p.T, 16));
-    route_small<SLOTS><<<grid, 256, 0, stream>>>(p);
+    if (ap)
+      route_small<SLOTS, true><<<grid, 256, (5 * (size_t)p.E + 1) * sizeof(int), stream>>>(p, *ap);
+    else
+      route_small<SLOTS, false><<<grid, 256, 0, stream>>>(p, AlignParams{});
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -516,10 +552,11 @@ moe_status route_validate(const void* x, const float* gate, int T, int H, int E,
   return MOE_OK;
 }
 
-moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+namespace {
+moe_status route_launch(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
-                        int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream) {
-  if (T == 0) return MOE_OK;
+                        int32_t* ids, float* weights, float* logits_out, void* ws, const AlignParams* ap,
+                        hipStream_t stream) {
   RouteParams p;
   p.x = static_cast<const uint16_t*>(x);
   p.gate = gate;
@@ -528,6 +565,7 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
   p.part = reinterpret_cast<float*>(base + kCtrlBytes);
   p.logits_out = logits_out;
   p.counters = reinterpret_cast<unsigned*>(base + kCounterOffset);
+  p.fused_counter = reinterpret_cast<unsigned*>(base + kFusedCounterOffset);
   p.ids = ids;
   p.weights = weights;
   p.T = T; p.H = H; p.E = E; p.k = k;
@@ -538,12 +576,42 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
   p.NC = H / KCH;
   p.NG = ceil_div(p.NC, CPG);
   const int slots = ceil_div(E, kWave);
-  if (slots <= 1) return launch_slots<1>(p, stream);
-  if (slots <= 2) return launch_slots<2>(p, stream);
-  if (slots <= 4) return launch_slots<4>(p, stream);
-  if (slots <= 5) return launch_slots<5>(p, stream);
-  if (slots <= 8) return launch_slots<8>(p, stream);
-  return launch_slots<16>(p, stream);
+  if (slots <= 1) return launch_slots<1>(p, ap, stream);
+  if (slots <= 2) return launch_slots<2>(p, ap, stream);
+  if (slots <= 4) return launch_slots<4>(p, ap, stream);
+  if (slots <= 5) return launch_slots<5>(p, ap, stream);
+  if (slots <= 8) return launch_slots<8>(p, ap, stream);
+  return launch_slots<16>(p, ap, stream);
+}
+}  // namespace
+
+moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+                        int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
+                        int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream) {
+  if (T == 0) return MOE_OK;
+  return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, ids,
+                      weights, logits_out, ws, nullptr, stream);
+}
+
+size_t route_align_workspace_size(int T, int H, int E, int k) {
+  const size_t r = route_workspace_size(T, H, E), a = align_workspace_size(T, k, E);
+  return r > a ? r : a;
+}
+
+moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+                              int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
+                              int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream) {
+  if (T == 0) return launch_align(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
+  if (!use_large(T, E)) {
+    const AlignParams ap = align_params(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws);
+    return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, ids,
+                        weights, nullptr, ws, &ap, stream);
+  }
+  moe_status st = launch_route(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                               routed_scale, ids, weights, nullptr, ws, stream);
+  if (st != MOE_OK) return st;
+  return launch_align(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
 }
 
 }  // namespace moe
@@ -566,4 +634,26 @@ extern "C" moe_status moe_route(const void* x, const float* gate, const float* b
 extern "C" size_t moe_route_workspace_size(int T, int H, int E) {
   if (T < 0 || H < 1 || E < 1) return 0;
   return moe::route_workspace_size(T, H, E);
+}
+
+extern "C" moe_status moe_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E,
+                                      int k, int n_group, int topk_group, int scoring, int renormalize,
+                                      float routed_scale, int block_m, int32_t* topk_ids, float* topk_weights,
+                                      int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_padded,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace moe;
+  moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, topk_ids, topk_weights);
+  if (st != MOE_OK) return st;
+  st = align_validate(topk_ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded);
+  if (st != MOE_OK) return st;
+  if (!workspace) return MOE_E_INVAL;
+  if (workspace_bytes < route_align_workspace_size(T, H, E, k)) return MOE_E_WORKSPACE;
+  return launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+                            block_m, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded, workspace,
+                            stream);
+}
+
+extern "C" size_t moe_route_align_workspace_size(int T, int H, int E, int k) {
+  if (T < 0 || H < 1 || E < 1 || k < 1) return 0;
+  return moe::route_align_workspace_size(T, H, E, k);
 }

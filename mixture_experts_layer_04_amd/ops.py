@@ -76,6 +76,27 @@ def route(x, gate, bias, k, scoring="softmax", n_group=1, topk_group=1, renormal
     return (ids, w, logits) if return_logits else (ids, w)
 
 
+def route_align(x, gate, bias, k, block_m, scoring="softmax", n_group=1, topk_group=1, renormalize=True,
+                routed_scale=1.0, ws=None):
+    """moe_route_align -> (topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded [1])."""
+    _check_cuda(x, gate, bias)
+    T, H = x.shape
+    E = gate.shape[0]
+    dev = x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sorted_ids = torch.empty(align_max_padded(T, k, E, block_m), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(align_max_blocks(T, k, E, block_m), dtype=torch.int32, device=dev)
+    npp = torch.empty(1, dtype=torch.int32, device=dev)
+    need = lib().moe_route_align_workspace_size(T, H, E, k)
+    ws = workspace(dev, need) if ws is None else ws
+    check(lib().moe_route_align(_ptr(x), _ptr(gate), _ptr(bias), T, H, E, k, n_group, topk_group,
+                                SCORING[scoring], int(bool(renormalize)), float(routed_scale), block_m,
+                                _ptr(ids), _ptr(w), _ptr(sorted_ids), _ptr(block_expert), _ptr(npp),
+                                _ptr(ws), ws.numel(), _stream(dev)), "moe_route_align")
+    return ids, w, sorted_ids, block_expert, npp
+
+
 def align(topk_ids, E, block_m, ws=None):
     """moe_align -> (sorted_ids, block_expert, num_post_padded [1]) on the device."""
     _check_cuda(topk_ids)

@@ -80,6 +80,20 @@ def test_align_argument_checks(L):
     assert call(nbytes=4) == 3
 
 
+def test_route_align_argument_checks(L):
+    def call(T=4, H=128, E=8, k=2, bm=16, ws=FAKE, nbytes=1 << 22):
+        return L.moe_route_align(FAKE, FAKE, None, T, H, E, k, 1, 1, 0, 1, 1.0, bm, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 ws, nbytes, None)
+    assert call(H=192) == 1           # router checks
+    assert call(k=9) == 1
+    assert call(bm=0) == 1            # alignment checks
+    assert call(bm=2048) == 1
+    assert call(ws=None) == 1
+    assert call(nbytes=16) == 3
+    need = L.moe_route_align_workspace_size(4096, 2048, 128, 8)
+    assert need >= L.moe_route_workspace_size(4096, 2048, 128) and need >= L.moe_align_workspace_size(4096, 8, 128)
+
+
 def test_ffn_and_layer_argument_checks(L):
     def ffn(T=4, H=256, E=8, F=128, k=2, bm=16, wf=0, ws=FAKE, nbytes=1 << 30, s13=FAKE):
         return L.moe_expert_ffn(FAKE, wf, FAKE, s13, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
