@@ -70,6 +70,7 @@ __global__ __launch_bounds__(NW * 64) void align_count_kernel(Align2Params p) {
   if (__ballot(bad) != 0ull && lane == 0) atomicOr(p.err, 1);
   __syncthreads();
   for (int e = tid; e < E; e += NT) p.cnt[(size_t)e * p.G + g] = h[e];
+  wait_wave_stores();
   __syncthreads();
   if (tid == 0) {
     const unsigned prev = __hip_atomic_fetch_add(p.counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);

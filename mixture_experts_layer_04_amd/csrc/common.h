@@ -87,6 +87,14 @@ __device__ __forceinline__ float wave_sum_u(float v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Last-workgroup elections: before the barrier that precedes one thread's
+// agent-scope release, every wave that stored data the elected workgroup
+// reads waits until its stores are complete (in the L2).  The barrier does
+// not wait for them, and the one thread's release (L2 write-back, then its
+// own wave's count) would otherwise miss stores of the other waves still in
+// flight.
+__device__ __forceinline__ void wait_wave_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -7,6 +7,7 @@
 // once): one workgroup per token reads the token's k expert-output rows,
 // multiplies each by its routing weight and adds them in slot order in fp32.
 
+#include "combine.h"
 #include "common.h"
 #include "launch.h"
 
@@ -30,37 +31,11 @@ struct FinP {
 
 template <int KT>  // = k
 __global__ __launch_bounds__(256) void finalize_kernel(FinP p) {
-  constexpr int KM = KT;
   const int t = blockIdx.x;
   const int32_t* ids = p.ids + (size_t)t * p.k;
   const float* w = p.w + (size_t)t * p.k;
-  for (int h = threadIdx.x * 8; h < p.H; h += 256 * 8) {
-    // all k rows in flight at once, then added in slot order
-    uint4 o[KM];
-#pragma unroll
-    for (int j = 0; j < KM; ++j) o[j] = *reinterpret_cast<const uint4*>(p.out + ((size_t)t * KM + j) * p.H + h);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      const int e = ids[j];
-      if (e < 0 || e >= p.E) continue;
-      const float wj = w[j];
-      acc[0] = __builtin_fmaf(wj, bf16_lo(o[j].x), acc[0]);
-      acc[1] = __builtin_fmaf(wj, bf16_hi(o[j].x), acc[1]);
-      acc[2] = __builtin_fmaf(wj, bf16_lo(o[j].y), acc[2]);
-      acc[3] = __builtin_fmaf(wj, bf16_hi(o[j].y), acc[3]);
-      acc[4] = __builtin_fmaf(wj, bf16_lo(o[j].z), acc[4]);
-      acc[5] = __builtin_fmaf(wj, bf16_hi(o[j].z), acc[5]);
-      acc[6] = __builtin_fmaf(wj, bf16_lo(o[j].w), acc[6]);
-      acc[7] = __builtin_fmaf(wj, bf16_hi(o[j].w), acc[7]);
-    }
-    uint4 v;
-    v.x = pack_bf16x2(acc[0], acc[1]);
-    v.y = pack_bf16x2(acc[2], acc[3]);
-    v.z = pack_bf16x2(acc[4], acc[5]);
-    v.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(p.y + (size_t)t * p.H + h) = v;
-  }
+  for (int h = threadIdx.x * 8; h < p.H; h += 256 * 8)
+    *reinterpret_cast<uint4*>(p.y + (size_t)t * p.H + h) = combine8<KT>(p.out, ids, w, t, h, p.H, p.E, KT);
 }
 
 }  // namespace

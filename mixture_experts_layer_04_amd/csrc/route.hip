@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
       if (t < p.T && e < p.E) p.part[((size_t)j * p.T + t) * p.E + e] = gsum;
     }
   }
-  __syncthreads();
+  __syncthreads();  // only wave 0 (thread 0's wave) stored group sums
   if (threadIdx.x == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(p.counters + ttile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -361,7 +361,8 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
       align_block<4>(lp, smem);
       return;
     }
-    __syncthreads();  // this tile's ids are written
+    wait_wave_stores();  // every wave stored ids of this tile
+    __syncthreads();
     if (threadIdx.x == 0) {
       const unsigned prev =
           __hip_atomic_fetch_add(p.fused_counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);

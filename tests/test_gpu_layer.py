@@ -138,3 +138,29 @@ def test_layer_graph_capture_and_determinism():
         other = call(None)  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other, ref)
+
+
+def test_layer_shapes_share_one_workspace():
+    """Calls of different shapes (fused decode paths included) on one
+    workspace give the bits of calls on fresh zeroed workspaces: every
+    counter lives in the control block at the workspace's start and is left
+    at zero."""
+    import mixture_experts_layer_04_amd as moe
+    shapes = [(dict(F=256), 100, 16), (dict(E=16, k=4, H=256, F=128, scoring="sigmoid", has_bias=True, n_group=4,
+                                          topk_group=2, routed_scale=2.5), 64, 16),
+              (dict(F=256), 3, 0), (dict(E=16, k=4, H=256, F=128), 17, 0), (dict(F=256), 100, 16)]
+    shared = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
+    for over, T, bm in shapes:
+        cfg = get_config("toy", **over)
+        W = make_weights(cfg, "cuda")
+        x = make_x(cfg, T, "cuda")
+        kw = dict(wformat=cfg.wformat, w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], block_m=bm)
+        args = (x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                cfg.renormalize, cfg.routed_scale)
+        need = moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, bm, cfg.wformat)
+        assert need <= shared.numel()
+        y = moe.layer(*args, ws=shared, **kw)
+        fresh = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        y_ref = moe.layer(*args, ws=fresh, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (over, T, bm)
