@@ -67,7 +67,12 @@ typedef enum moe_status {
 /* Scoring of the router logits ([Router] §1.3 "The Rank Key and the Weight"):
  * softmax over the experts (Mixtral, Qwen3) or an independent sigmoid per
  * expert (DeepSeek-V3 and successors). */
-typedef enum moe_scoring { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_scoring;
+typedef enum moe_scoring {
+  MOE_SOFTMAX = 0,       /* softmax over the E logits                        */
+  MOE_SIGMOID = 1,       /* sigmoid per expert                               */
+  MOE_SQRTSOFTPLUS = 2   /* sqrt(softplus(logit)) per expert ([Router] §1.3:
+                            the DeepSeek-V4 variant of the sigmoid score)    */
+} moe_scoring;
 
 /* Expert weight storage formats.
  *  MOE_W_BF16:          w13 bf16 [E, 2F, H], w2 bf16 [E, H, F]; scales unused.
@@ -201,10 +206,14 @@ size_t moe_route_align_workspace_size(int T, int H, int E, int k);
  *  topk_ids       int32 [T, k], topk_weights float32 [T, k] (the router's)
  *  sorted_ids, block_expert, num_post_padded  moe_align's outputs for the
  *                 same topk_ids and block_m
+ *  swiglu_limit   L > 0: before SwiGLU the gate is capped at L and the up
+ *                 value clipped to [-L, L] ([MegaMoE] §3.5, DeepSeek-V4);
+ *                 +infinity: no clamp.  NaN or L <= 0: MOE_E_INVAL.
  *  y              bf16 [T, H] out:
- *                 y[t] = sum_j w[t,j] * W2_e (silu(W1_e x_t) * (W3_e x_t)),
- *                 e = topk_ids[t,j], summed over j in slot order in fp32 and
- *                 rounded once; slots whose id is outside [0, E) add nothing.
+ *                 y[t] = sum_j w[t,j] * W2_e (silu(g) * u), g = W1_e x_t and
+ *                 u = W3_e x_t (clamped with a finite L), e = topk_ids[t,j],
+ *                 summed over j in slot order in fp32 and rounded once;
+ *                 slots whose id is outside [0, E) add nothing.
  * Each block of block_m rows multiplies by exactly one expert's weights;
  * rows are gathered through sorted_ids / k; blocks at or past the padded
  * length exit without work.  The SwiGLU output and the expert outputs are
@@ -223,6 +232,7 @@ moe_status moe_expert_ffn(const void* x, int wformat,
                           const int32_t* block_expert,
                           const int32_t* num_post_padded,
                           int T, int H, int E, int F, int k, int block_m,
+                          float swiglu_limit,
                           void* y, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 size_t moe_expert_ffn_workspace_size(int T, int H, int E, int F, int k,
@@ -250,7 +260,7 @@ moe_status moe_expert_ffn_stages(const void* x, int wformat,
                                  const int32_t* block_expert,
                                  const int32_t* num_post_padded,
                                  int T, int H, int E, int F, int k, int block_m,
-                                 void* y, void* workspace,
+                                 float swiglu_limit, void* y, void* workspace,
                                  size_t workspace_bytes, int stages,
                                  hipStream_t stream);
 
@@ -267,6 +277,7 @@ moe_status moe_layer(const void* x, const float* gate, const float* bias,
                      int T, int H, int E, int F, int k,
                      int n_group, int topk_group, int scoring,
                      int renormalize, float routed_scale, int block_m,
+                     float swiglu_limit,
                      void* y, int32_t* topk_ids_out, float* topk_weights_out,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);

@@ -10,7 +10,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
-SCORING = {"softmax": 0, "sigmoid": 1}
+SCORING = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 WFORMAT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 STAGE = {"quant": 1, "gemm1": 2, "gemm2": 4, "combine": 8, "all": 15}
 
@@ -33,11 +33,11 @@ SIGNATURES = {
     "moe_align_max_padded": (_i64, [_i, _i, _i, _i]),
     "moe_align_max_blocks": (_i64, [_i, _i, _i, _i]),
     "moe_expert_ffn": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                            _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+                            _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn_stages": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                   _i, _i, _i, _i, _i, _i, _vp, _vp, _sz, _i, _vp]),
-    "moe_layer": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                   _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _i, _vp]),
+    "moe_layer": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f,
                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_layer_block_m": (_i, [_i, _i, _i]),

@@ -101,7 +101,7 @@ extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, in
 extern "C" moe_status moe_layer(const void* x, const float* gate, const float* bias, int wformat,
                                 const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
                                 int T, int H, int E, int F, int k, int n_group, int topk_group, int scoring,
-                                int renormalize, float routed_scale, int block_m, void* y,
+                                int renormalize, float routed_scale, int block_m, float swiglu_limit, void* y,
                                 int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   using namespace moe;
@@ -112,7 +112,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, &dummy_i, &dummy_f);
   if (st != MOE_OK) return st;
   st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, &dummy_i, &dummy_f, &dummy_i, &dummy_i, &dummy_i,
-                    T, H, E, F, k, block_m, y);
+                    T, H, E, F, k, block_m, swiglu_limit, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!workspace) return MOE_E_INVAL;
@@ -134,6 +134,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   a.topk_ids = ids; a.topk_weights = w;
   a.sorted_ids = sorted; a.block_expert = bexp; a.num_post_padded = npp;
   a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.swiglu_limit = swiglu_limit;
   a.stages = MOE_STAGE_ALL;
   a.y = y;
   ffn_carve(a, b + L.ffn);

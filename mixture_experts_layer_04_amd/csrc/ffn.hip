@@ -63,8 +63,9 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
                         const void* w2_scale, const int32_t* topk_ids, const float* topk_weights,
                         const int32_t* sorted_ids, const int32_t* block_expert,
                         const int32_t* num_post_padded, int T, int H, int E, int F, int k, int block_m,
-                        const void* y) {
+                        float swiglu_limit, const void* y) {
   if (T < 0 || H < 128 || F < 128 || H % 128 || F % 128) return MOE_E_INVAL;
+  if (!(swiglu_limit > 0.f)) return MOE_E_INVAL;  // NaN or <= 0
   if (E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_E_INVAL;
   if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_E_INVAL;
   if ((int64_t)T * k > (1 << 24)) return MOE_E_INVAL;
@@ -150,13 +151,13 @@ extern "C" moe_status moe_expert_ffn_stages(const void* x, int wformat, const vo
                                             const void* w2, const void* w2_scale, const int32_t* topk_ids,
                                             const float* topk_weights, const int32_t* sorted_ids,
                                             const int32_t* block_expert, const int32_t* num_post_padded,
-                                            int T, int H, int E, int F, int k, int block_m, void* y,
-                                            void* workspace, size_t workspace_bytes, int stages,
-                                            hipStream_t stream) {
+                                            int T, int H, int E, int F, int k, int block_m,
+                                            float swiglu_limit, void* y, void* workspace,
+                                            size_t workspace_bytes, int stages, hipStream_t stream) {
   using namespace moe;
   if (stages & ~MOE_STAGE_ALL) return MOE_E_INVAL;
   moe_status st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
-                               block_expert, num_post_padded, T, H, E, F, k, block_m, y);
+                               block_expert, num_post_padded, T, H, E, F, k, block_m, swiglu_limit, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!workspace) return MOE_E_INVAL;
@@ -167,6 +168,7 @@ extern "C" moe_status moe_expert_ffn_stages(const void* x, int wformat, const vo
   a.topk_ids = topk_ids; a.topk_weights = topk_weights;
   a.sorted_ids = sorted_ids; a.block_expert = block_expert; a.num_post_padded = num_post_padded;
   a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.swiglu_limit = swiglu_limit;
   a.stages = stages;
   a.y = y;
   ffn_carve(a, workspace);
@@ -177,10 +179,10 @@ extern "C" moe_status moe_expert_ffn(const void* x, int wformat, const void* w13
                                      const void* w2, const void* w2_scale, const int32_t* topk_ids,
                                      const float* topk_weights, const int32_t* sorted_ids,
                                      const int32_t* block_expert, const int32_t* num_post_padded, int T,
-                                     int H, int E, int F, int k, int block_m, void* y, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
+                                     int H, int E, int F, int k, int block_m, float swiglu_limit, void* y,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return moe_expert_ffn_stages(x, wformat, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
-                               block_expert, num_post_padded, T, H, E, F, k, block_m, y, workspace,
+                               block_expert, num_post_padded, T, H, E, F, k, block_m, swiglu_limit, y, workspace,
                                workspace_bytes, MOE_STAGE_ALL, stream);
 }
 

@@ -76,6 +76,7 @@ struct GemmP {
   void* act_s;            // fp32 [max_padded, F/128] (FP8) or e8m0 [max_padded, F/32] (MX)
   float* act32;           // BLOCK_M 16, FP8 / MX: fp32 SwiGLU rows [max_padded, F]
   uint16_t* out;          // [T*k, H] bf16
+  float lim;              // SwiGLU clamp (+inf: none)
   int H, F, k, A;
 };
 
@@ -128,7 +129,12 @@ struct SOp<F_MX> {
   static constexpr int S = 4;
 };
 
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.f + expf(-g)) * u; }
+// silu(min(g, lim)) * clamp(u, -lim, lim) ([MegaMoE] §3.5); lim = +inf: no clamp
+__device__ __forceinline__ float swiglu(float g, float u, float lim) {
+  g = fminf(g, lim);
+  u = fminf(fmaxf(u, -lim), lim);
+  return g / (1.f + expf(-g)) * u;
+}
 
 // e4m3 (OCP) of v, v already within [-448, 448]; round to nearest even
 __device__ __forceinline__ uint32_t to_e4m3(float v) {
@@ -540,7 +546,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 #pragma unroll
         for (int fa = 0; fa < FA; ++fa)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[fm][fa][i] = swiglu(acc[fm][fa][i], acc[fm][fa + FA][i]);
+          for (int i = 0; i < 4; ++i) v[fm][fa][i] = swiglu(acc[fm][fa][i], acc[fm][fa + FA][i], p.lim);
       const int lcol0 = wn * (BNA / WN);  // first tile column of this wave
       if (F == F_BF16) {
         uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BM][BNA]
@@ -838,7 +844,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemm_stream(GemmP p) {
           gs += red[w][row][col];
           us += red[w][row][BNO + col];
         }
-        const float v = swiglu(gs, us);
+        const float v = swiglu(gs, us, p.lim);
         const size_t o = (size_t)(blk * 16 + row) * p.F + nt * BNO + col;
         if (F == F_BF16)
           reinterpret_cast<uint16_t*>(p.act)[o] = (uint16_t)f32_to_bf16_bits(v);
@@ -961,6 +967,7 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   p.act_s = a.act_s;
   p.act32 = static_cast<float*>(a.act32);
   p.out = static_cast<uint16_t*>(a.out);
+  p.lim = a.swiglu_limit;
   p.H = a.H; p.F = a.F; p.k = a.k; p.A = a.T * a.k;
   const int64_t mb = align_max_blocks(a.T, a.k, a.E, a.block_m);
   if (a.block_m == 16) {

@@ -60,6 +60,7 @@ struct FfnArgs {
   const int32_t* block_expert;
   const int32_t* num_post_padded;
   int T, H, E, F, k, block_m;
+  float swiglu_limit;  // +inf: no clamp
   int stages;      // bit mask of MOE_STAGE_* to run
   void* y;
   // workspace regions
@@ -75,7 +76,7 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
                         const void* w2_scale, const int32_t* topk_ids, const float* topk_weights,
                         const int32_t* sorted_ids, const int32_t* block_expert,
                         const int32_t* num_post_padded, int T, int H, int E, int F, int k, int block_m,
-                        const void* y);
+                        float swiglu_limit, const void* y);
 size_t ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat);
 void ffn_carve(FfnArgs& a, void* ws);
 moe_status launch_ffn(const FfnArgs& a, hipStream_t stream);

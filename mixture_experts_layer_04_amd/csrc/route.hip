@@ -131,12 +131,16 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
       sc[s] = sc[s] * inv;
       key[s] = ok[s] ? sc[s] : NEG_INF;
     }
-  } else {
+  } else if (p.scoring == MOE_SIGMOID) {
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) {
-      const int e = s * kWave + lane;
-      (void)e;
       sc[s] = 1.f / (1.f + expf(-l[s]));
+      key[s] = ok[s] ? sc[s] + bv[s] : NEG_INF;
+    }
+  } else {  // sqrt(softplus), softplus(l) = max(l, 0) + log1p(exp(-|l|))
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) {
+      sc[s] = sqrtf(fmaxf(l[s], 0.f) + log1pf(expf(-fabsf(l[s]))));
       key[s] = ok[s] ? sc[s] + bv[s] : NEG_INF;
     }
   }
@@ -543,7 +547,7 @@ size_t route_workspace_size(int T, int H, int E) {
 moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
                           int topk_group, int scoring, const int32_t* ids, const float* w) {
   if (T < 0 || H < 128 || H % 128 != 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_E_INVAL;
-  if (scoring != MOE_SOFTMAX && scoring != MOE_SIGMOID) return MOE_E_INVAL;
+  if (scoring != MOE_SOFTMAX && scoring != MOE_SIGMOID && scoring != MOE_SQRTSOFTPLUS) return MOE_E_INVAL;
   if (n_group < 1 || n_group > 64 || E % n_group != 0) return MOE_E_INVAL;
   if (n_group > 1 && (E / n_group < 2)) return MOE_E_INVAL;
   if (topk_group < 1 || topk_group > n_group) return MOE_E_INVAL;

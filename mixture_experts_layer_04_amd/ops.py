@@ -9,6 +9,8 @@ stream.  The workspace is a zero-initialised byte tensor cached per device
 (or passed in); calls that overlap in time must not share one.
 """
 
+import math
+
 import torch
 
 from ._lib import SCORING, STAGE, WFORMAT, check, lib
@@ -120,7 +122,8 @@ def _dims(x, w13, w2, wformat):
 
 
 def expert_ffn(x, w13, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded, block_m,
-               wformat="bf16", w13_scale=None, w2_scale=None, ws=None, stages=None, out=None):
+               wformat="bf16", w13_scale=None, w2_scale=None, ws=None, stages=None, out=None,
+               swiglu_limit=math.inf):
     """moe_expert_ffn -> y bf16 [T, H].  ``stages`` (names from
     _lib.STAGE, or an int mask) selects moe_expert_ffn_stages instead."""
     _check_cuda(x, w13, w2, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded,
@@ -133,7 +136,7 @@ def expert_ffn(x, w13, w2, topk_ids, topk_weights, sorted_ids, block_expert, num
     ws = workspace(x.device, need) if ws is None else ws
     args = [_ptr(x), wf, _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale),
             _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert),
-            _ptr(num_post_padded), T, H, E, F, k, block_m, _ptr(y), _ptr(ws), ws.numel()]
+            _ptr(num_post_padded), T, H, E, F, k, block_m, float(swiglu_limit), _ptr(y), _ptr(ws), ws.numel()]
     if stages is None:
         check(lib().moe_expert_ffn(*args, _stream(x.device)), "moe_expert_ffn")
     else:
@@ -148,7 +151,7 @@ def layer_workspace_size(T, H, E, F, k, block_m=0, wformat="bf16"):
 
 def layer(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_group=1, renormalize=True,
           routed_scale=1.0, wformat="bf16", w13_scale=None, w2_scale=None, block_m=0, return_routing=False,
-          ws=None, out=None):
+          ws=None, out=None, swiglu_limit=math.inf):
     """moe_layer -> y bf16 [T, H] (and topk ids / weights with return_routing)."""
     _check_cuda(x, gate, bias, w13, w2, w13_scale, w2_scale)
     T, H, E, F = _dims(x, w13, w2, wformat)
@@ -162,7 +165,8 @@ def layer(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_group=1,
     ws = workspace(x.device, need) if ws is None else ws
     check(lib().moe_layer(_ptr(x), _ptr(gate), _ptr(bias), wf, _ptr(w13), _ptr(w13_scale), _ptr(w2),
                           _ptr(w2_scale), T, H, E, F, k, n_group, topk_group, SCORING[scoring],
-                          int(bool(renormalize)), float(routed_scale), block_m, _ptr(y), _ptr(ids), _ptr(w),
+                          int(bool(renormalize)), float(routed_scale), block_m, float(swiglu_limit), _ptr(y),
+                          _ptr(ids), _ptr(w),
                           _ptr(ws), ws.numel(), _stream(x.device)), "moe_layer")
     return (y, ids, w) if return_routing else y
 

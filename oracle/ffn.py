@@ -8,7 +8,9 @@ Test infrastructure only (see ``oracle/__init__``).
   the gate columns before the up columns).
 * Its output for one hidden state x is w2 . (silu(g) * u) with g = W1 x and
   u = W3 x, silu(g) = g / (1 + exp(-g)) ([Kernels] "The fused expert GEMM":
-  SwiGLU silu(g) * u; [MegaMoE] §1.1: silu(gate) * up).
+  SwiGLU silu(g) * u; [MegaMoE] §1.1: silu(gate) * up).  With a SwiGLU
+  limit L, g is first capped at L and u clipped to [-L, L] ([MegaMoE] §3.5,
+  the DeepSeek-V4 epilogue); L = inf is no clamp.
 * The layer output of token t is sum_j w[t, j] * o[t, j], summed over the k
   slots in slot order ([Kernels] "Combine ...": a gather per token summing
   its k rows in a fixed order; [MegaMoE] §3.7: sum the slots in slot order).
@@ -118,13 +120,20 @@ def quantize_act(v, fmt):
     return out
 
 
-def expert_forward(X, W13, W2, act_fmt=None):
+def swiglu(g, u, limit=np.inf):
+    """silu(min(g, L)) * clip(u, -L, L) ([MegaMoE] §3.5); L = inf: silu(g) * u."""
+    g = np.minimum(np.asarray(g, dtype=np.float64), limit)
+    u = np.clip(np.asarray(u, dtype=np.float64), -limit, limit)
+    return silu(g) * u
+
+
+def expert_forward(X, W13, W2, act_fmt=None, limit=np.inf):
     """SwiGLU expert on the rows of X [n, H] -> [n, H].  With ``act_fmt``
     the SwiGLU output is quantised as in the emulate mode."""
     F = W13.shape[0] // 2
     g = X @ W13[:F].T
     u = X @ W13[F:].T
-    a = silu(g) * u
+    a = swiglu(g, u, limit)
     if act_fmt is not None:
         a = quantize_act(a, act_fmt)
     return a @ W2.T
@@ -169,7 +178,7 @@ def layer_grouped(x, ids, w, expert_fn, E):
     return combine_direct(outs, w), outs
 
 
-def make_expert_fn(weights, mode="dense"):
+def make_expert_fn(weights, mode="dense", limit=np.inf):
     """expert_fn for ``layer_*`` from an ExpertWeights; caches each expert's
     dequantised matrices for the lifetime of the returned function."""
     cache = {}
@@ -181,12 +190,12 @@ def make_expert_fn(weights, mode="dense"):
         W13, W2 = cache[e]
         if act_fmt is not None:
             rows = quantize_act(rows, act_fmt)
-        return expert_forward(rows, W13, W2, act_fmt)
+        return expert_forward(rows, W13, W2, act_fmt, limit)
 
     return fn
 
 
-def layer(x_bits, route_out, weights, E, mode="dense", tokens=None):
+def layer(x_bits, route_out, weights, E, mode="dense", tokens=None, limit=np.inf):
     """The full layer for the tokens in ``tokens`` (all by default), given a
     router result (``oracle.router.route``).  Returns (y [n, H] float64,
     per-assignment outputs [n, k, H])."""
@@ -195,5 +204,5 @@ def layer(x_bits, route_out, weights, E, mode="dense", tokens=None):
     w = route_out["weights"]
     if tokens is not None:
         x, ids, w = x[tokens], ids[tokens], w[tokens]
-    fn = make_expert_fn(weights, mode)
+    fn = make_expert_fn(weights, mode, limit)
     return layer_grouped(x, ids, w, fn, E)

@@ -29,7 +29,7 @@ import numpy as np
 
 from .formats import bf16_bits_to_f64
 
-SCORINGS = ("softmax", "sigmoid")
+SCORINGS = ("softmax", "sigmoid", "sqrtsoftplus")
 
 
 def logits(x_bits, gate):
@@ -44,10 +44,14 @@ def logits(x_bits, gate):
 
 
 def scores(lg, scoring):
-    """R2.  softmax over experts (max subtracted) or an independent sigmoid
-    per expert ([Router] §1.3; [MoE] fused_topk / grouped_topk listings).
+    """R2.  softmax over experts (max subtracted), an independent sigmoid
+    per expert ([Router] §1.3; [MoE] fused_topk / grouped_topk listings), or
+    the square root of a softplus per expert, the score DeepSeek-V4 uses in
+    place of the sigmoid ([Router] §1.3, Fig. 3 discussion).  The softplus is
+    written in its overflow-free form max(l, 0) + log1p(exp(-|l|)).
 
-    Pinned against scipy.special.softmax / expit."""
+    Pinned against scipy.special.softmax / expit / softplus and closed forms
+    (sqrt(ln 2) at 0, sqrt(l) for large l, exp(l / 2) for very negative l)."""
     lg = np.asarray(lg, dtype=np.float64)
     if scoring == "softmax":
         m = lg.max(axis=1, keepdims=True)
@@ -56,6 +60,8 @@ def scores(lg, scoring):
     if scoring == "sigmoid":
         with np.errstate(over="ignore"):
             return 1.0 / (1.0 + np.exp(-lg))
+    if scoring == "sqrtsoftplus":
+        return np.sqrt(np.maximum(lg, 0.0) + np.log1p(np.exp(-np.abs(lg))))
     raise ValueError(f"unsupported scoring function: {scoring!r}")
 
 

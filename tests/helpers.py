@@ -73,11 +73,11 @@ def routing_for_layer(cfg, r, ids_gpu):
     return {"ids": ids, "weights": w}
 
 
-def oracle_layer(cfg, x, routing, weights_t, tokens=None, mode="dense"):
+def oracle_layer(cfg, x, routing, weights_t, tokens=None, mode="dense", limit=np.inf):
     W = offn.ExpertWeights(cfg.wformat, LazyExperts(weights_t["w13"]), LazyExperts(weights_t["w2"]),
                            None if weights_t["w13_scale"] is None else LazyExperts(weights_t["w13_scale"]),
                            None if weights_t["w2_scale"] is None else LazyExperts(weights_t["w2_scale"]))
-    y, _ = offn.layer(to_numpy(x), routing, W, cfg.E, mode=mode, tokens=tokens)
+    y, _ = offn.layer(to_numpy(x), routing, W, cfg.E, mode=mode, tokens=tokens, limit=limit)
     return y
 
 

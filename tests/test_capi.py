@@ -4,6 +4,7 @@ checks return the documented status codes before anything is enqueued, and
 the sizing helpers agree with the oracle's worst-case formulas."""
 
 import ctypes
+import math
 import os
 import re
 
@@ -95,15 +96,16 @@ def test_route_align_argument_checks(L):
 
 
 def test_ffn_and_layer_argument_checks(L):
-    def ffn(T=4, H=256, E=8, F=128, k=2, bm=16, wf=0, ws=FAKE, nbytes=1 << 30, s13=FAKE):
+    def ffn(T=4, H=256, E=8, F=128, k=2, bm=16, wf=0, ws=FAKE, nbytes=1 << 30, s13=FAKE, lim=math.inf):
         return L.moe_expert_ffn(FAKE, wf, FAKE, s13, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                T, H, E, F, k, bm, FAKE, ws, nbytes, None)
+                                T, H, E, F, k, bm, lim, FAKE, ws, nbytes, None)
     assert ffn(H=200) == 1            # H not a multiple of 128
     assert ffn(F=96) == 1
     assert ffn(bm=8) == 1             # GEMM blocks are 16, 32, 64 or 128
     assert ffn(wf=5) == 1
     assert ffn(wf=1, s13=None) == 1   # fp8 needs scales
     assert ffn(nbytes=100) == 3
+    assert ffn(lim=0.0) == 1 and ffn(lim=-1.0) == 1 and ffn(lim=math.nan) == 1  # SwiGLU limit
     assert ffn(T=0) == 0
     # 32-bit byte offsets: x of 300000 x 7168 bf16 and one expert's w13 of
     # 2 x 32768 x 32768 bf16 are 4 GiB or more
@@ -112,7 +114,7 @@ def test_ffn_and_layer_argument_checks(L):
 
     def layer(T=4, H=256, E=8, F=128, k=2, bm=0, ws=FAKE, nbytes=1 << 30):
         return L.moe_layer(FAKE, FAKE, None, 0, FAKE, None, FAKE, None, T, H, E, F, k, 1, 1, 0, 1, 1.0, bm,
-                           FAKE, None, None, ws, nbytes, None)
+                           math.inf, FAKE, None, None, ws, nbytes, None)
     assert layer(bm=48) == 1
     assert layer(nbytes=1000) == 3
     assert layer(T=0) == 0

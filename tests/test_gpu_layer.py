@@ -26,18 +26,20 @@ def weights_for(cfg):
     return _CACHE[key]
 
 
-def run_layer(cfg, W, x, block_m=0):
+def run_layer(cfg, W, x, block_m=0, limit=np.inf):
     import mixture_experts_layer_04_amd as moe
     return moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,
                      cfg.topk_group, cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat,
-                     w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], block_m=block_m, return_routing=True)
+                     w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], block_m=block_m, return_routing=True,
+                     swiglu_limit=limit)
 
 
-def check_layer(cfg, T, block_m=0, sample=None, seed=0):
-    say(f"layer {cfg.name} {cfg.wformat} E={cfg.E} H={cfg.H} F={cfg.F} k={cfg.k} T={T} block_m={block_m}")
+def check_layer(cfg, T, block_m=0, sample=None, seed=0, limit=np.inf):
+    say(f"layer {cfg.name} {cfg.wformat} E={cfg.E} H={cfg.H} F={cfg.F} k={cfg.k} T={T} block_m={block_m}"
+        + (f" SwiGLU limit {limit}" if np.isfinite(limit) else ""))
     W = weights_for(cfg)
     x = make_x(cfg, T, "cuda")
-    y, ids, w = run_layer(cfg, W, x, block_m)
+    y, ids, w = run_layer(cfg, W, x, block_m, limit)
     torch.cuda.synchronize()
     r = oracle_route(cfg, x, W["gate"], W["bias"])
     check_routing(cfg, r, ids.cpu().numpy(), w.cpu().numpy())
@@ -46,7 +48,7 @@ def check_layer(cfg, T, block_m=0, sample=None, seed=0):
     if sample is not None and sample < T:
         rng = np.random.default_rng(seed)
         tokens = np.unique(np.concatenate([rng.choice(T, sample - 1, replace=False), [T - 1]]))
-    y_ref = oracle_layer(cfg, x, routing, W, tokens=tokens)
+    y_ref = oracle_layer(cfg, x, routing, W, tokens=tokens, limit=limit)
     got = bf16_to_f64(y)
     if tokens is not None:
         got = got[tokens]
@@ -55,7 +57,7 @@ def check_layer(cfg, T, block_m=0, sample=None, seed=0):
     if cfg.wformat != "bf16" and (tokens is None or len(tokens) <= 8):
         # diagnostic: against the oracle that quantises activations as the
         # kernels do (scales in float64, so rare e4m3 rounding flips differ)
-        y_em = oracle_layer(cfg, x, routing, W, tokens=tokens, mode="emulate")
+        y_em = oracle_layer(cfg, x, routing, W, tokens=tokens, mode="emulate", limit=limit)
         say(f"  vs emulate-mode oracle: {rel_fro(got, y_em):.3e}")
     assert np.all(np.isfinite(got))
     assert err <= LAYER_TOL[cfg.wformat]
@@ -72,6 +74,7 @@ SMALL = [
     ("toy", dict(E=16, k=4, H=256, F=128, scoring="sigmoid", has_bias=True, n_group=4, topk_group=2,
                  routed_scale=2.5), 64, 16),
     ("toy", dict(E=1, k=1, H=128, F=128), 19, 16),
+    ("toy", dict(E=16, k=4, H=256, F=128, scoring="sqrtsoftplus", has_bias=True), 50, 16),
     # fp8 128x128 block scales (DeepSeek-V3 routing), several tiles and ragged tails
     ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 37, 16),
     ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 300, 32),
@@ -89,6 +92,28 @@ SMALL = [
 def test_layer_small_all_tokens(name, over, T, bm):
     cfg = get_config(name, **over)
     check_layer(cfg, T, bm)
+
+
+CLAMPED = [("toy", dict(F=256), 100, 16, 0.25), ("toy", dict(F=256), 300, 64, 0.25),
+           ("toy", dict(F=256), 300, 128, 0.25),
+           ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 300, 32, 0.5),
+           ("dsv4", dict(E=16, H=512, F=512, k=4), 37, 16, 0.5), ("dsv4", dict(E=8, H=512, F=1024, k=2), 700, 128, 0.5)]
+
+
+@pytest.mark.parametrize("name,over,T,bm,limit", CLAMPED)
+def test_layer_swiglu_clamp(name, over, T, bm, limit):
+    """The DeepSeek-V4 SwiGLU clamp ([MegaMoE] §3.5) with a limit that a
+    large share of the gate and up values exceed (they are ~N(0, 0.3); the
+    quantised formats take 0.5, where the fp8 activation error of the
+    concentrated clamped values stays inside their tolerance)."""
+    cfg = get_config(name, **over)
+    x, W, y, ids, w, err = check_layer(cfg, T, bm, limit=limit)
+    # the clamp changes the layer by far more than the tolerance
+    r = oracle_route(cfg, x, W["gate"], W["bias"])
+    routing = routing_for_layer(cfg, r, ids.cpu().numpy())
+    diff = rel_fro(oracle_layer(cfg, x, routing, W), oracle_layer(cfg, x, routing, W, limit=limit))
+    say(f"  clamped vs unclamped oracle: {diff:.3e}")
+    assert diff > 3 * LAYER_TOL[cfg.wformat]
 
 
 FULL = [("qwen3", 1), ("qwen3", 64), ("qwen3", 4096), ("glm", 1), ("glm", 8), ("glm", 512),

@@ -43,6 +43,25 @@ def test_route_parity(name, T):
     say(f"  clear tokens {int(clear.sum())}/{T}, near-tie tokens with other ids: {differ}")
 
 
+SQRT_SOFTPLUS = [("dsv4", {}, 1), ("dsv4", {}, 37), ("dsv4", {}, 512), ("dsv3", {}, 5),
+                 ("toy", dict(E=64, k=6, H=512, has_bias=True, renormalize=False), 300)]
+
+
+@pytest.mark.parametrize("name,over,T", SQRT_SOFTPLUS)
+def test_route_parity_sqrt_softplus(name, over, T):
+    """The sqrt(softplus) score (DeepSeek-V4's variant, [Router] §1.3) with
+    bias, group limit (dsv3 shape) and without renormalisation."""
+    cfg = get_config(name, scoring="sqrtsoftplus", **over)
+    say(f"route parity sqrt(softplus) {name} {over} T={T}")
+    gate, bias = make_router_weights(cfg, "cuda")
+    x = make_x(cfg, T, "cuda")
+    ids, w = _route(cfg, x, gate, bias)
+    torch.cuda.synchronize()
+    r = oracle_route(cfg, x, gate, bias)
+    clear, differ = check_routing(cfg, r, ids.cpu().numpy(), w.cpu().numpy())
+    say(f"  clear tokens {int(clear.sum())}/{T}, near-tie tokens with other ids: {differ}")
+
+
 def test_route_toy_worked_example(golden):
     """[Router] §1.1 / §1.3 / §2.1 toy example on the GPU."""
     g = golden("router_toy.json")

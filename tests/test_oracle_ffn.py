@@ -113,3 +113,24 @@ def test_activation_quantiser_error_bound(fmt, group):
             np.array([[fm.pow2_at_least(a / 448.0) if a > 0 else 1.0] for a in amax[:, 0]])
         assert np.all(np.abs(qb - blk) <= 2.0 ** -4 * np.abs(blk) + 2.0 ** -10 * s + 1e-15)
         assert np.all(np.abs(qb) <= 448.0 * s * (1 + 1e-15))
+
+
+def test_swiglu_clamp_worked_values_and_bounds():
+    """[MegaMoE] §3.5: gate capped at L, up clipped to [-L, L] before SwiGLU.
+    Hand values, L = inf as the plain SwiGLU, inputs inside the limit
+    unchanged, and |act| <= max(silu(L), silu's minimum magnitude) * L."""
+    import math
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    assert offn.swiglu(5.0, -7.0, 3.0) == pytest.approx(silu(3.0) * -3.0, rel=1e-15)
+    assert offn.swiglu(-2.0, 10.0, 3.0) == pytest.approx(silu(-2.0) * 3.0, rel=1e-15)  # no lower cap on the gate
+    assert offn.swiglu(-40.0, -2.0, 3.0) == pytest.approx(silu(-40.0) * -2.0, rel=1e-15)
+    rng = np.random.default_rng(11)
+    g, u = rng.normal(0, 4, size=(2, 5000))
+    assert np.array_equal(offn.swiglu(g, u), offn.silu(g) * u)
+    assert np.array_equal(offn.swiglu(g, u, np.inf), offn.silu(g) * u)
+    inside = (np.abs(g) < 2.5) & (np.abs(u) < 2.5)
+    assert np.array_equal(offn.swiglu(g, u, 2.5)[inside], (offn.silu(g) * u)[inside])
+    L = 2.5
+    bound = max(silu(L), 0.2785) * L
+    assert np.all(np.abs(offn.swiglu(g, u, L)) <= bound + 1e-12)
+    assert np.any(np.abs(offn.swiglu(g, u, L)) > 0.9 * silu(L) * L)  # the cap is reached

@@ -66,8 +66,25 @@ def test_scores_match_scipy():
     lg = rng.normal(0, 3, size=(50, 37))
     assert np.allclose(orouter.scores(lg, "softmax"), scipy.special.softmax(lg, axis=1), rtol=1e-13, atol=0)
     assert np.allclose(orouter.scores(lg, "sigmoid"), scipy.special.expit(lg), rtol=1e-13, atol=0)
+    assert np.allclose(orouter.scores(lg, "sqrtsoftplus"), np.sqrt(scipy.special.softplus(lg)), rtol=1e-13, atol=0)
     with pytest.raises(ValueError):
         orouter.scores(lg, "sqrt_softplus")
+
+
+def test_sqrt_softplus_closed_forms():
+    """sqrt(softplus): sqrt(ln 2) at 0; sqrt(l) + O(e^-l) for large l;
+    exp(l / 2) (1 + O(e^l)) for very negative l; increasing, positive, and
+    sqrt(log(1 + e^l)) by np.logaddexp on moderate l."""
+    s = lambda v: orouter.scores(np.array([v], dtype=np.float64), "sqrtsoftplus")[0]
+    assert s([0.0])[0] == pytest.approx(math.sqrt(math.log(2.0)), rel=1e-15)
+    assert s([100.0])[0] == pytest.approx(10.0, rel=1e-15)
+    assert s([800.0])[0] == pytest.approx(math.sqrt(800.0), rel=1e-15)  # no overflow
+    assert s([-40.0])[0] == pytest.approx(math.exp(-20.0), rel=1e-12)
+    assert s([-800.0])[0] == 0.0 or s([-800.0])[0] < 1e-170
+    lg = np.linspace(-30, 30, 601)
+    v = s(lg)
+    assert np.all(np.diff(v) > 0) and np.all(v > 0)
+    assert np.allclose(v, np.sqrt(np.logaddexp(0.0, lg)), rtol=1e-14, atol=0)
 
 
 def test_logits_are_exact_products():
