@@ -206,7 +206,7 @@ def decode_sweep(moe, torch, timer, qwen3_weights):
         W = cache[name]
         x = make_x(cfg, T, "cuda")
         y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
-        ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, 0, cfg.wformat),
+        ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, 0, cfg.wformat, 0),
                          dtype=torch.uint8, device="cuda")
         def call():
             moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,

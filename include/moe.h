@@ -176,25 +176,34 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
  *
  * Arguments as moe_route (without logits_out) and moe_align, with the same
  * layouts, ownership and results: topk_ids / topk_weights are written and
- * then aligned with block_m.  The outputs equal those of moe_route followed
- * by moe_align on the same stream, bit for bit.  For T <= 256 the router's
- * workgroups compute the gate product and each token tile's last one
- * selects its tokens; the last token tile to finish then aligns all T*k
- * assignments in the same launch.  For T > 256 the router's two launches
- * run, then moe_align's.
+ * then aligned with block_m.  With n_shared = 0 the outputs equal those of
+ * moe_route followed by moe_align on the same stream, bit for bit.  For
+ * T <= 256 the router's workgroups compute the gate product and each token
+ * tile's last one selects its tokens; the last token tile to finish then
+ * aligns all assignments in the same launch.  For T > 256 the router's two
+ * launches run, then moe_align's.
+ *  n_shared       0, or 1 for a shared expert as an always-selected slot
+ *                 ([MoE] SGLang's fused shared expert: appended as expert
+ *                 id E, top-k becomes top-(k+1); [MegaMoE] §3.8: its output
+ *                 is added to the routed sum): topk_ids / topk_weights are
+ *                 then [T, k+1] with slot k = (E, 1.0) for every token, and
+ *                 the alignment covers E+1 experts (its buffers sized with
+ *                 moe_align_max_*(T, k+1, E+1, block_m)).
  * Errors: as moe_route and moe_align (validated on the host before anything
- * is enqueued); the workspace must hold
- * moe_route_align_workspace_size(T, H, E, k) bytes.
+ * is enqueued); n_shared outside {0, 1}, or E + n_shared > 1024, or
+ * k + n_shared > 16: MOE_E_INVAL.  The workspace must hold
+ * moe_route_align_workspace_size(T, H, E, k, n_shared) bytes.
  * ------------------------------------------------------------------------ */
 moe_status moe_route_align(const void* x, const float* gate, const float* bias,
-                           int T, int H, int E, int k, int n_group, int topk_group,
+                           int T, int H, int E, int k, int n_shared,
+                           int n_group, int topk_group,
                            int scoring, int renormalize, float routed_scale,
                            int block_m, int32_t* topk_ids, float* topk_weights,
                            int32_t* sorted_ids, int32_t* block_expert,
                            int32_t* num_post_padded,
                            void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
-size_t moe_route_align_workspace_size(int T, int H, int E, int k);
+size_t moe_route_align_workspace_size(int T, int H, int E, int k, int n_shared);
 
 /* ------------------------------------------------------------------------
  * moe_expert_ffn - grouped expert GEMMs and combine ([Kernels] "The fused
@@ -266,22 +275,29 @@ moe_status moe_expert_ffn_stages(const void* x, int wformat,
 
 /* ------------------------------------------------------------------------
  * moe_layer - the whole forward: moe_route -> moe_align -> moe_expert_ffn
- * on one stream with one workspace (arguments as above).
+ * on one stream with one workspace (arguments as above; the router and
+ * the alignment run as moe_route_align).
+ *  E, k           routed experts and routed slots per token.
+ *  n_shared       0, or 1 for a shared expert (see moe_route_align): w13,
+ *                 w2 and their scales then hold E + 1 experts, the shared
+ *                 one last, and y adds its output with weight 1.
  *  block_m        0 lets the library choose from the tokens per expert
- *                 (moe_layer_block_m); otherwise 16, 32, 64 or 128.
- *  topk_ids_out, topk_weights_out   optional outputs (NULL allowed).
+ *                 (moe_layer_block_m of T, k + n_shared, E + n_shared);
+ *                 otherwise 16, 32, 64 or 128.
+ *  topk_ids_out, topk_weights_out   optional outputs (NULL allowed),
+ *                 [T, k + n_shared].
  * ------------------------------------------------------------------------ */
 moe_status moe_layer(const void* x, const float* gate, const float* bias,
                      int wformat, const void* w13, const void* w13_scale,
                      const void* w2, const void* w2_scale,
-                     int T, int H, int E, int F, int k,
+                     int T, int H, int E, int F, int k, int n_shared,
                      int n_group, int topk_group, int scoring,
                      int renormalize, float routed_scale, int block_m,
                      float swiglu_limit,
                      void* y, int32_t* topk_ids_out, float* topk_weights_out,
                      void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
-size_t moe_layer_workspace_size(int T, int H, int E, int F, int k,
+size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared,
                                 int block_m, int wformat);
 /* The block size moe_layer uses for block_m = 0, from the mean rows per
  * expert m = T*k/E: 16 if m < 2, 32 if m <= 32, 64 if m <= 96, else 128. */

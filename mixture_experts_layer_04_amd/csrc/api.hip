@@ -14,24 +14,27 @@ struct LayerLayout {
 
 // The route workspace (control block + group partials) sits at offset 0;
 // the alignment workspace (the same control block + its scratch) overlaps it,
-// the router being done with its partials before the alignment starts.
-LayerLayout layer_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
+// the router being done with its partials before the alignment starts.  With
+// a shared expert the ids, the alignment and the FFN cover E + 1 experts and
+// k + 1 slots.
+LayerLayout layer_layout(int T, int H, int E, int F, int k, int ns, int block_m, int wformat) {
   LayerLayout L;
+  const int Ea = E + ns, ka = k + ns;
   size_t off = 0;
   L.ctrl = off;
-  off += align_up(route_align_workspace_size(T, H, E, k), 256);
+  off += align_up(route_align_workspace_size(T, H, E, k, ns), 256);
   L.ids = off;
-  off += align_up((size_t)T * k * sizeof(int32_t), 256);
+  off += align_up((size_t)T * ka * sizeof(int32_t), 256);
   L.w = off;
-  off += align_up((size_t)T * k * sizeof(float), 256);
+  off += align_up((size_t)T * ka * sizeof(float), 256);
   L.sorted = off;
-  off += align_up((size_t)align_max_padded(T, k, E, block_m) * sizeof(int32_t), 256);
+  off += align_up((size_t)align_max_padded(T, ka, Ea, block_m) * sizeof(int32_t), 256);
   L.bexp = off;
-  off += align_up((size_t)align_max_blocks(T, k, E, block_m) * sizeof(int32_t), 256);
+  off += align_up((size_t)align_max_blocks(T, ka, Ea, block_m) * sizeof(int32_t), 256);
   L.npp = off;
   off += 256;
   L.ffn = off;
-  off += align_up(ffn_workspace_size(T, H, E, F, k, block_m, wformat), 256);
+  off += align_up(ffn_workspace_size(T, H, Ea, F, ka, block_m, wformat), 256);
   L.total = off;
   return L;
 }
@@ -92,31 +95,34 @@ extern "C" int moe_layer_block_m(int T, int k, int E) {
   return moe::layer_block_m(T, k, E);
 }
 
-extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat) {
-  if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1) return 0;
-  if (block_m == 0) block_m = moe::layer_block_m(T, k, E);
-  return moe::layer_layout(T, H, E, F, k, block_m, wformat).total;
+extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared, int block_m,
+                                           int wformat) {
+  if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1 || n_shared < 0 || n_shared > 1) return 0;
+  if (block_m == 0) block_m = moe::layer_block_m(T, k + n_shared, E + n_shared);
+  return moe::layer_layout(T, H, E, F, k, n_shared, block_m, wformat).total;
 }
 
 extern "C" moe_status moe_layer(const void* x, const float* gate, const float* bias, int wformat,
                                 const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
-                                int T, int H, int E, int F, int k, int n_group, int topk_group, int scoring,
-                                int renormalize, float routed_scale, int block_m, float swiglu_limit, void* y,
-                                int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                                int T, int H, int E, int F, int k, int n_shared, int n_group, int topk_group,
+                                int scoring, int renormalize, float routed_scale, int block_m, float swiglu_limit,
+                                void* y, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   using namespace moe;
-  if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1) ? layer_block_m(T, k, E) : 16;
+  if (n_shared != 0 && n_shared != 1) return MOE_E_INVAL;
+  const int Ea = E + n_shared, ka = k + n_shared;  // the expert FFN sees the shared expert as expert E
+  if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1) ? layer_block_m(T, ka, Ea) : 16;
   // validate everything before enqueuing anything
   int32_t dummy_i = 0;
   float dummy_f = 0.f;
   moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, &dummy_i, &dummy_f);
   if (st != MOE_OK) return st;
   st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, &dummy_i, &dummy_f, &dummy_i, &dummy_i, &dummy_i,
-                    T, H, E, F, k, block_m, swiglu_limit, y);
+                    T, H, Ea, F, ka, block_m, swiglu_limit, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!workspace) return MOE_E_INVAL;
-  const LayerLayout L = layer_layout(T, H, E, F, k, block_m, wformat);
+  const LayerLayout L = layer_layout(T, H, E, F, k, n_shared, block_m, wformat);
   if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
   char* b = static_cast<char*>(workspace);
   int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(b + L.ids);
@@ -126,14 +132,14 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   int32_t* npp = reinterpret_cast<int32_t*>(b + L.npp);
 
   st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
-                          block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream);
+                          n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream);
   if (st != MOE_OK) return st;
   FfnArgs a;
   a.x = x; a.wformat = wformat;
   a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
   a.topk_ids = ids; a.topk_weights = w;
   a.sorted_ids = sorted; a.block_expert = bexp; a.num_post_padded = npp;
-  a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
+  a.T = T; a.H = H; a.E = Ea; a.F = F; a.k = ka; a.block_m = block_m;
   a.swiglu_limit = swiglu_limit;
   a.stages = MOE_STAGE_ALL;
   a.y = y;

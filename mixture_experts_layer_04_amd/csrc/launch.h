@@ -32,11 +32,13 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
 // Route + align in one call: one launch while T <= 256 (the router's decode
 // layout, whose last token tile aligns every assignment), else the router's
 // two launches and launch_align.
+// n_shared = 1: slot k of every token is the shared expert (id E, weight 1),
+// ids / weights rows hold k + 1 slots and the alignment covers E + 1 experts.
 moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
-                              int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
+                              int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream);
-size_t route_align_workspace_size(int T, int H, int E, int k);
+size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared);
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
                           const void* block_expert, const void* num_post_padded);

@@ -59,6 +59,8 @@ struct RouteParams {
   int32_t* ids;
   float* weights;
   int T, H, E, k, n_group, topk_group, scoring, renorm;
+  int n_shared;  // 1: slot k of every token is the shared expert (id E, weight 1)
+  int ks;        // ids / weights row stride, k + n_shared
   float scale;
   int NF, NC, NG;
 };
@@ -224,9 +226,13 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
     wgt = sel_s / (sum + 1e-20f);
   }
   wgt *= p.scale;
-  if (lane < p.k) {
-    p.ids[(size_t)t * p.k + lane] = sel_id;
-    p.weights[(size_t)t * p.k + lane] = wgt;
+  if (p.n_shared && lane == p.k) {  // the shared expert: an always-selected slot
+    sel_id = p.E;
+    wgt = 1.f;
+  }
+  if (lane < p.ks) {
+    p.ids[(size_t)t * p.ks + lane] = sel_id;
+    p.weights[(size_t)t * p.ks + lane] = wgt;
     if (sid) sid[lane] = sel_id;
   }
 }
@@ -294,7 +300,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
   const int c = j * CPG + wave;
   __shared__ float red[CPG][16][17];
   __shared__ int s_last;
-  __shared__ int s_ids[FUSE ? 16 * 16 : 1];  // FUSE: the tile's ids [16][k]
+  __shared__ int s_ids[FUSE ? 16 * 17 : 1];  // FUSE: the tile's ids [16][k + n_shared]
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (c < p.NC) {
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
     load_bias<SLOTS>(p, bv);
     float l[SLOTS];
     sum_groups<SLOTS>(p, t, l);
-    select_token<SLOTS>(p, t, l, bv, FUSE ? s_ids + tl * p.k : nullptr);
+    select_token<SLOTS>(p, t, l, bv, FUSE ? s_ids + tl * p.ks : nullptr);
   }
   if constexpr (FUSE) {
     extern __shared__ int smem[];
@@ -560,8 +566,8 @@ moe_status route_validate(const void* x, const float* gate, int T, int H, int E,
 namespace {
 moe_status route_launch(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
-                        int32_t* ids, float* weights, float* logits_out, void* ws, const AlignParams* ap,
-                        hipStream_t stream) {
+                        int n_shared, int32_t* ids, float* weights, float* logits_out, void* ws,
+                        const AlignParams* ap, hipStream_t stream) {
   RouteParams p;
   p.x = static_cast<const uint16_t*>(x);
   p.gate = gate;
@@ -574,6 +580,7 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.ids = ids;
   p.weights = weights;
   p.T = T; p.H = H; p.E = E; p.k = k;
+  p.n_shared = n_shared; p.ks = k + n_shared;
   p.n_group = n_group; p.topk_group = topk_group;
   p.scoring = scoring; p.renorm = renormalize != 0;
   p.scale = routed_scale;
@@ -594,29 +601,31 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream) {
   if (T == 0) return MOE_OK;
-  return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, ids,
+  return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, 0, ids,
                       weights, logits_out, ws, nullptr, stream);
 }
 
-size_t route_align_workspace_size(int T, int H, int E, int k) {
-  const size_t r = route_workspace_size(T, H, E), a = align_workspace_size(T, k, E);
+size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
+  const size_t r = route_workspace_size(T, H, E), a = align_workspace_size(T, k + n_shared, E + n_shared);
   return r > a ? r : a;
 }
 
 moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
-                              int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
+                              int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream) {
-  if (T == 0) return launch_align(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
+  // the alignment sees the shared expert as expert E and slot k
+  const int Ea = E + n_shared, ka = k + n_shared;
+  if (T == 0) return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
   if (!use_large(T, E)) {
-    const AlignParams ap = align_params(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws);
-    return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, ids,
-                        weights, nullptr, ws, &ap, stream);
+    const AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
+    return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+                        n_shared, ids, weights, nullptr, ws, &ap, stream);
   }
-  moe_status st = launch_route(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
-                               routed_scale, ids, weights, nullptr, ws, stream);
+  moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                               routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream);
   if (st != MOE_OK) return st;
-  return launch_align(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
+  return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
 }
 
 }  // namespace moe
@@ -642,23 +651,25 @@ extern "C" size_t moe_route_workspace_size(int T, int H, int E) {
 }
 
 extern "C" moe_status moe_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E,
-                                      int k, int n_group, int topk_group, int scoring, int renormalize,
-                                      float routed_scale, int block_m, int32_t* topk_ids, float* topk_weights,
-                                      int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_padded,
-                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                      int k, int n_shared, int n_group, int topk_group, int scoring,
+                                      int renormalize, float routed_scale, int block_m, int32_t* topk_ids,
+                                      float* topk_weights, int32_t* sorted_ids, int32_t* block_expert,
+                                      int32_t* num_post_padded, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
   using namespace moe;
+  if (n_shared != 0 && n_shared != 1) return MOE_E_INVAL;
   moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, topk_ids, topk_weights);
   if (st != MOE_OK) return st;
-  st = align_validate(topk_ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded);
+  st = align_validate(topk_ids, T, k + n_shared, E + n_shared, block_m, sorted_ids, block_expert, num_post_padded);
   if (st != MOE_OK) return st;
   if (!workspace) return MOE_E_INVAL;
-  if (workspace_bytes < route_align_workspace_size(T, H, E, k)) return MOE_E_WORKSPACE;
+  if (workspace_bytes < route_align_workspace_size(T, H, E, k, n_shared)) return MOE_E_WORKSPACE;
   return launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
-                            block_m, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded, workspace,
-                            stream);
+                            n_shared, block_m, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded,
+                            workspace, stream);
 }
 
-extern "C" size_t moe_route_align_workspace_size(int T, int H, int E, int k) {
-  if (T < 0 || H < 1 || E < 1 || k < 1) return 0;
-  return moe::route_align_workspace_size(T, H, E, k);
+extern "C" size_t moe_route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
+  if (T < 0 || H < 1 || E < 1 || k < 1 || n_shared < 0 || n_shared > 1) return 0;
+  return moe::route_align_workspace_size(T, H, E, k, n_shared);
 }

@@ -79,20 +79,22 @@ def route(x, gate, bias, k, scoring="softmax", n_group=1, topk_group=1, renormal
 
 
 def route_align(x, gate, bias, k, block_m, scoring="softmax", n_group=1, topk_group=1, renormalize=True,
-                routed_scale=1.0, ws=None):
-    """moe_route_align -> (topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded [1])."""
+                routed_scale=1.0, ws=None, n_shared=0):
+    """moe_route_align -> (topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded [1]);
+    with n_shared = 1 the ids / weights have k + 1 slots (slot k: the shared expert E, weight 1)."""
     _check_cuda(x, gate, bias)
     T, H = x.shape
     E = gate.shape[0]
     dev = x.device
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    sorted_ids = torch.empty(align_max_padded(T, k, E, block_m), dtype=torch.int32, device=dev)
-    block_expert = torch.empty(align_max_blocks(T, k, E, block_m), dtype=torch.int32, device=dev)
+    ka, Ea = k + n_shared, E + n_shared
+    ids = torch.empty((T, ka), dtype=torch.int32, device=dev)
+    w = torch.empty((T, ka), dtype=torch.float32, device=dev)
+    sorted_ids = torch.empty(align_max_padded(T, ka, Ea, block_m), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(align_max_blocks(T, ka, Ea, block_m), dtype=torch.int32, device=dev)
     npp = torch.empty(1, dtype=torch.int32, device=dev)
-    need = lib().moe_route_align_workspace_size(T, H, E, k)
+    need = lib().moe_route_align_workspace_size(T, H, E, k, n_shared)
     ws = workspace(dev, need) if ws is None else ws
-    check(lib().moe_route_align(_ptr(x), _ptr(gate), _ptr(bias), T, H, E, k, n_group, topk_group,
+    check(lib().moe_route_align(_ptr(x), _ptr(gate), _ptr(bias), T, H, E, k, n_shared, n_group, topk_group,
                                 SCORING[scoring], int(bool(renormalize)), float(routed_scale), block_m,
                                 _ptr(ids), _ptr(w), _ptr(sorted_ids), _ptr(block_expert), _ptr(npp),
                                 _ptr(ws), ws.numel(), _stream(dev)), "moe_route_align")
@@ -145,26 +147,31 @@ def expert_ffn(x, w13, w2, topk_ids, topk_weights, sorted_ids, block_expert, num
     return y
 
 
-def layer_workspace_size(T, H, E, F, k, block_m=0, wformat="bf16"):
-    return int(lib().moe_layer_workspace_size(T, H, E, F, k, block_m, WFORMAT[wformat]))
+def layer_workspace_size(T, H, E, F, k, block_m=0, wformat="bf16", n_shared=0):
+    return int(lib().moe_layer_workspace_size(T, H, E, F, k, n_shared, block_m, WFORMAT[wformat]))
 
 
 def layer(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_group=1, renormalize=True,
           routed_scale=1.0, wformat="bf16", w13_scale=None, w2_scale=None, block_m=0, return_routing=False,
-          ws=None, out=None, swiglu_limit=math.inf):
-    """moe_layer -> y bf16 [T, H] (and topk ids / weights with return_routing)."""
+          ws=None, out=None, swiglu_limit=math.inf, n_shared=0):
+    """moe_layer -> y bf16 [T, H] (and topk ids / weights with return_routing).
+    With n_shared = 1, w13 / w2 (and scales) hold the gate's E experts plus
+    the shared expert last."""
     _check_cuda(x, gate, bias, w13, w2, w13_scale, w2_scale)
-    T, H, E, F = _dims(x, w13, w2, wformat)
+    T, H, Ew, F = _dims(x, w13, w2, wformat)
+    E = gate.shape[0]
+    if Ew != E + n_shared:
+        raise ValueError(f"w13 holds {Ew} experts, the gate {E} and n_shared = {n_shared}")
     y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if out is None else out
     ids = w = None
     if return_routing:
-        ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
-        w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+        ids = torch.empty((T, k + n_shared), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k + n_shared), dtype=torch.float32, device=x.device)
     wf = WFORMAT[wformat]
-    need = lib().moe_layer_workspace_size(T, H, E, F, k, block_m, wf)
+    need = lib().moe_layer_workspace_size(T, H, E, F, k, n_shared, block_m, wf)
     ws = workspace(x.device, need) if ws is None else ws
     check(lib().moe_layer(_ptr(x), _ptr(gate), _ptr(bias), wf, _ptr(w13), _ptr(w13_scale), _ptr(w2),
-                          _ptr(w2_scale), T, H, E, F, k, n_group, topk_group, SCORING[scoring],
+                          _ptr(w2_scale), T, H, E, F, k, n_shared, n_group, topk_group, SCORING[scoring],
                           int(bool(renormalize)), float(routed_scale), block_m, float(swiglu_limit), _ptr(y),
                           _ptr(ids), _ptr(w),
                           _ptr(ws), ws.numel(), _stream(x.device)), "moe_layer")

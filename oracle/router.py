@@ -161,6 +161,22 @@ def weights(sc, ids, renormalize=True, routed_scale=1.0):
     return w * float(routed_scale)
 
 
+def with_shared_expert(r, E):
+    """The shared expert as an always-selected slot: ids and weights gain a
+    slot k holding expert E with weight 1 for every token ([MoE], SGLang's
+    fused shared expert: appended as expert id E, top-k becomes top-(k+1);
+    [MegaMoE] §3.8: its output is added to the sum of the routed ones).
+    Reading: the routed weights keep their renormalisation and scale, and
+    the shared expert's output adds unscaled."""
+    ids = np.asarray(r["ids"])
+    w = np.asarray(r["weights"], dtype=np.float64)
+    T = ids.shape[0]
+    out = dict(r)
+    out["ids"] = np.concatenate([ids, np.full((T, 1), E, dtype=ids.dtype)], axis=1)
+    out["weights"] = np.concatenate([w, np.ones((T, 1))], axis=1)
+    return out
+
+
 def route(x_bits, gate, bias, k, scoring, n_group=1, topk_group=1,
           renormalize=True, routed_scale=1.0):
     """The whole router (R1-R6).  Returns a dict with logits, scores, keys,

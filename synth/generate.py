@@ -81,9 +81,10 @@ def quantize_mxfp4(w):
     return packed.contiguous(), e8.contiguous()
 
 
-def _weights(cfg: LayerConfig, device, which, N, K):
-    """All experts of one weight tensor in its storage format."""
-    E = cfg.E
+def _weights(cfg: LayerConfig, device, which, N, K, n_shared=0):
+    """All experts of one weight tensor in its storage format (E routed
+    experts, then n_shared more)."""
+    E = cfg.E + n_shared
     if cfg.wformat == "bf16":
         out = torch.empty((E, N, K), dtype=torch.bfloat16, device=device)
         for e in range(E):
@@ -111,11 +112,13 @@ def make_router_weights(cfg: LayerConfig, device="cpu"):
     return gate, bias
 
 
-def make_weights(cfg: LayerConfig, device="cpu"):
-    """Router and expert weights of a configuration (independent of T)."""
+def make_weights(cfg: LayerConfig, device="cpu", n_shared=0):
+    """Router and expert weights of a configuration (independent of T).
+    With n_shared = 1 the expert tensors hold one more expert (index E, the
+    shared expert); the gate keeps its E rows."""
     gate, bias = make_router_weights(cfg, device)
-    w13, w13_scale = _weights(cfg, device, "w13", 2 * cfg.F, cfg.H)
-    w2, w2_scale = _weights(cfg, device, "w2", cfg.H, cfg.F)
+    w13, w13_scale = _weights(cfg, device, "w13", 2 * cfg.F, cfg.H, n_shared)
+    w2, w2_scale = _weights(cfg, device, "w2", cfg.H, cfg.F, n_shared)
     return {"gate": gate, "bias": bias, "w13": w13, "w13_scale": w13_scale,
             "w2": w2, "w2_scale": w2_scale}
 

@@ -82,8 +82,8 @@ def test_align_argument_checks(L):
 
 
 def test_route_align_argument_checks(L):
-    def call(T=4, H=128, E=8, k=2, bm=16, ws=FAKE, nbytes=1 << 22):
-        return L.moe_route_align(FAKE, FAKE, None, T, H, E, k, 1, 1, 0, 1, 1.0, bm, FAKE, FAKE, FAKE, FAKE, FAKE,
+    def call(T=4, H=128, E=8, k=2, bm=16, ws=FAKE, nbytes=1 << 22, ns=0):
+        return L.moe_route_align(FAKE, FAKE, None, T, H, E, k, ns, 1, 1, 0, 1, 1.0, bm, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  ws, nbytes, None)
     assert call(H=192) == 1           # router checks
     assert call(k=9) == 1
@@ -91,7 +91,10 @@ def test_route_align_argument_checks(L):
     assert call(bm=2048) == 1
     assert call(ws=None) == 1
     assert call(nbytes=16) == 3
-    need = L.moe_route_align_workspace_size(4096, 2048, 128, 8)
+    assert call(ns=2) == 1            # at most one shared expert
+    assert call(E=1024, ns=1) == 1    # E + n_shared <= 1024
+    assert call(k=16, E=32, ns=1) == 1  # k + n_shared <= 16
+    need = L.moe_route_align_workspace_size(4096, 2048, 128, 8, 0)
     assert need >= L.moe_route_workspace_size(4096, 2048, 128) and need >= L.moe_align_workspace_size(4096, 8, 128)
 
 
@@ -112,10 +115,11 @@ def test_ffn_and_layer_argument_checks(L):
     assert ffn(T=300000, H=7168, F=2048, E=256, k=8, bm=128) == 2
     assert ffn(T=4, H=32768, F=32768) == 2
 
-    def layer(T=4, H=256, E=8, F=128, k=2, bm=0, ws=FAKE, nbytes=1 << 30):
-        return L.moe_layer(FAKE, FAKE, None, 0, FAKE, None, FAKE, None, T, H, E, F, k, 1, 1, 0, 1, 1.0, bm,
+    def layer(T=4, H=256, E=8, F=128, k=2, bm=0, ws=FAKE, nbytes=1 << 30, ns=0):
+        return L.moe_layer(FAKE, FAKE, None, 0, FAKE, None, FAKE, None, T, H, E, F, k, ns, 1, 1, 0, 1, 1.0, bm,
                            math.inf, FAKE, None, None, ws, nbytes, None)
     assert layer(bm=48) == 1
+    assert layer(ns=2) == 1 and layer(ns=-1) == 1
     assert layer(nbytes=1000) == 3
     assert layer(T=0) == 0
 

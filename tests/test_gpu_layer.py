@@ -189,3 +189,46 @@ def test_layer_shapes_share_one_workspace():
         y_ref = moe.layer(*args, ws=fresh, **kw)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (over, T, bm)
+
+
+SHARED = [("toy", {}, 16, 0), ("toy", dict(F=256), 100, 16), ("toy", dict(F=256), 300, 64),
+          ("toy", dict(F=256), 300, 128),
+          ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 300, 32),
+          ("dsv4", dict(E=16, H=512, F=512, k=4), 37, 16), ("dsv4", dict(E=8, H=512, F=1024, k=2), 700, 128),
+          ("dsv3", {}, 1, 0), ("dsv4", {}, 512, 0)]
+
+
+@pytest.mark.parametrize("name,over,T,bm", SHARED)
+def test_layer_shared_expert(name, over, T, bm):
+    """The shared expert as an always-selected slot (id E, weight 1): the
+    router writes slot k, the alignment and the grouped GEMMs treat it as
+    expert E, and y adds its output (full DSV3 / DSV4 shapes on sampled
+    tokens)."""
+    import mixture_experts_layer_04_amd as moe
+    cfg = get_config(name, **over)
+    say(f"layer + shared expert {cfg.name} {cfg.wformat} E={cfg.E}+1 k={cfg.k}+1 T={T} block_m={bm}")
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+    W = make_weights(cfg, "cuda", n_shared=1)
+    x = make_x(cfg, T, "cuda")
+    y, ids, w = moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,
+                          cfg.topk_group, cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat,
+                          w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], block_m=bm, return_routing=True,
+                          n_shared=1)
+    torch.cuda.synchronize()
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    assert ids.shape == (T, cfg.k + 1)
+    assert np.all(ids[:, cfg.k] == cfg.E) and np.all(w[:, cfg.k] == 1.0)
+    r = oracle_route(cfg, x, W["gate"], W["bias"])
+    check_routing(cfg, r, ids[:, :cfg.k], w[:, :cfg.k])
+    from oracle import router as orouter
+    routing = orouter.with_shared_expert(routing_for_layer(cfg, r, ids[:, :cfg.k]), cfg.E)
+    tokens = None
+    if T > 64:
+        rng = np.random.default_rng(1)
+        tokens = np.unique(np.concatenate([rng.choice(T, 5, replace=False), [T - 1]]))
+    y_ref = oracle_layer(get_config(name, **dict(over, E=cfg.E + 1)), x, routing, W, tokens=tokens)
+    got = bf16_to_f64(y) if tokens is None else bf16_to_f64(y)[tokens]
+    err = rel_fro(got, y_ref)
+    say(f"  rel. Frobenius error {err:.3e} (tolerance {LAYER_TOL[cfg.wformat]:.0e})")
+    assert np.all(np.isfinite(got)) and err <= LAYER_TOL[cfg.wformat]

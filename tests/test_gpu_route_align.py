@@ -46,7 +46,7 @@ def test_route_align_repeated_calls_share_one_workspace():
         cfg = get_config(name)
         gate, bias = make_router_weights(cfg, "cuda")
         x = make_x(cfg, T, "cuda")
-        need = moe.lib().moe_route_align_workspace_size(T, cfg.H, cfg.E, cfg.k)
+        need = moe.lib().moe_route_align_workspace_size(T, cfg.H, cfg.E, cfg.k, 0)
         if ws is None or ws.numel() < need:
             ws = torch.zeros(max(need, 1 << 22), dtype=torch.uint8, device="cuda")
         out = moe.route_align(x, gate, bias, cfg.k, bm, cfg.scoring, cfg.n_group, cfg.topk_group,
@@ -55,3 +55,26 @@ def test_route_align_repeated_calls_share_one_workspace():
                               cfg.renormalize, cfg.routed_scale)
         for a, r in zip(out, ref):
             assert torch.equal(a, r)
+
+
+@pytest.mark.parametrize("name,T,bm", [("dsv3", 1, 16), ("dsv3", 37, 32), ("dsv4", 300, 64), ("toy", 16, 16)])
+def test_route_align_shared_expert_slot(name, T, bm):
+    """n_shared = 1: slot k is (E, 1.0) for every token, the routed slots
+    equal moe_route's, and the alignment equals moe_align over E + 1
+    experts and k + 1 slots (and the oracle's)."""
+    import mixture_experts_layer_04_amd as moe
+    cfg = get_config(name)
+    say(f"route+align + shared expert {name} T={T} block_m={bm}")
+    gate, bias = make_router_weights(cfg, "cuda")
+    x = make_x(cfg, T, "cuda")
+    args = (cfg.scoring, cfg.n_group, cfg.topk_group, cfg.renormalize, cfg.routed_scale)
+    ids, w, s, b, n = moe.route_align(x, gate, bias, cfg.k, bm, *args, n_shared=1)
+    ids_r, w_r = moe.route(x, gate, bias, cfg.k, *args)
+    torch.cuda.synchronize()
+    assert ids.shape == (T, cfg.k + 1)
+    assert torch.equal(ids[:, :cfg.k], ids_r) and torch.equal(w[:, :cfg.k].view(torch.int32), w_r.view(torch.int32))
+    assert bool((ids[:, cfg.k] == cfg.E).all()) and bool((w[:, cfg.k] == 1.0).all())
+    s_r, b_r, n_r = moe.align(ids.contiguous(), cfg.E + 1, bm)
+    assert torch.equal(s, s_r) and torch.equal(b, b_r) and int(n.item()) == int(n_r.item())
+    so, bo, no, bad = oracle_align(ids, cfg.E + 1, bm)
+    assert not bad and s.cpu().tolist() == so and b.cpu().tolist() == bo and int(n.item()) == no

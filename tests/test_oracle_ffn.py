@@ -134,3 +134,25 @@ def test_swiglu_clamp_worked_values_and_bounds():
     bound = max(silu(L), 0.2785) * L
     assert np.all(np.abs(offn.swiglu(g, u, L)) <= bound + 1e-12)
     assert np.any(np.abs(offn.swiglu(g, u, L)) > 0.9 * silu(L) * L)  # the cap is reached
+
+
+def test_shared_expert_slot_is_routed_sum_plus_dense_expert():
+    """The shared expert as slot k (id E, weight 1) gives the routed layer
+    plus the shared expert's dense forward on every token."""
+    cfg = get_config("toy", E=6, k=2, H=128, F=128)
+    d = make_inputs(cfg, 9)
+    from synth import make_weights
+    W = make_weights(cfg, "cpu", n_shared=1)
+    xb = to_numpy(d["x"])
+    r = orouter.route(xb, to_numpy(W["gate"]), None, cfg.k, cfg.scoring)
+    rs = orouter.with_shared_expert(r, cfg.E)
+    assert rs["ids"].shape == (9, 3) and np.all(rs["ids"][:, 2] == cfg.E) and np.all(rs["weights"][:, 2] == 1.0)
+    assert np.array_equal(rs["ids"][:, :2], r["ids"]) and np.array_equal(rs["weights"][:, :2], r["weights"])
+    ew = offn.ExpertWeights("bf16", to_numpy(W["w13"]), to_numpy(W["w2"]))
+    y_shared, _ = offn.layer(xb, rs, ew, cfg.E + 1)
+    y_routed, _ = offn.layer(xb, r, ew, cfg.E + 1)
+    W13, W2 = ew.expert(cfg.E)
+    x = fm.bf16_bits_to_f64(xb)
+    dense = x @ W13[:cfg.F].T, x @ W13[cfg.F:].T
+    y_dense = (dense[0] / (1.0 + np.exp(-dense[0])) * dense[1]) @ W2.T
+    assert np.allclose(y_shared, y_routed + y_dense, rtol=1e-12, atol=1e-15)
