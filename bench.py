@@ -230,6 +230,61 @@ def decode_sweep(moe, torch, timer, qwen3_weights):
     return out
 
 
+# One GPU's share of DeepSeek-V4 expert parallelism over 8 GPUs: 32 local
+# experts at DeepSeek-V4-Flash dimensions, random routing over them ([MegaMoE]
+# §3.4, where the fused kernel ran this on one B300 with every fetch local).
+EP_SHARE_T = (1, 4, 16, 64, 512)
+EP_SHARE_PAGE_US = {1: 40.0, 4: 68.0, 16: 95.0, 64: 99.0, 512: 112.0}  # B300, the page's figures
+
+
+def ep_share_sweep(moe, torch, timer):
+    """Cold alignment + expert FFN (fp8 quantisation, both grouped GEMMs and
+    the combine) for 32 MXFP4 experts, k = 6, at the page's token counts."""
+    from synth import get_config, make_topk_ids, make_weights, make_x
+    cfg = get_config("dsv4", E=32)
+    W = make_weights(cfg, "cuda")
+    out = {}
+    for T in EP_SHARE_T:
+        x = make_x(cfg, T, "cuda")
+        ids = make_topk_ids(T, cfg.k, cfg.E, seed=T, kind="uniform", device="cuda")
+        g = torch.Generator(device="cpu").manual_seed(T)
+        w = torch.rand((T, cfg.k), generator=g)
+        w = (w / w.sum(dim=1, keepdim=True)).to("cuda")
+        bm = moe.layer_block_m(T, cfg.k, cfg.E)
+        y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
+        fmt = 2
+        ws = torch.zeros(max(moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, bm, fmt),
+                             moe.lib().moe_align_workspace_size(T, cfg.k, cfg.E)), dtype=torch.uint8, device="cuda")
+        holder = {}
+
+        def align():
+            holder["a"] = moe.align(ids, cfg.E, bm, ws=ws)
+
+        def ffn():
+            s_, b_, n_ = holder["a"]
+            moe.expert_ffn(x, W["w13"], W["w2"], ids, w, s_, b_, n_, bm, wformat=cfg.wformat,
+                           w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], ws=ws, out=y)
+
+        def both():
+            align()
+            ffn()
+
+        us = timer(both)
+        align()
+        us_ffn = timer(ffn)
+        touched = int(torch.unique(ids).numel())
+        nbytes = touched * expert_bytes(cfg)
+        out[f"T{T}"] = {"us_align_ffn": round(us, 2), "us_ffn": round(us_ffn, 2), "block_m": bm,
+                        "experts_touched": touched, "weight_bytes": nbytes,
+                        "hbm_TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+                        "page_b300_us": EP_SHARE_PAGE_US[T]}
+        log(f"EP share (32 MXFP4 experts, k=6) T={T}: {us:.1f} us (FFN alone {us_ffn:.1f}), {touched} experts, "
+            f"{out[f'T{T}']['hbm_TBps']} TB/s; the page's B300 figure {EP_SHARE_PAGE_US[T]:.0f} us")
+    del W
+    torch.cuda.empty_cache()
+    return out
+
+
 def router_probe(moe, torch, timer):
     """moe_route alone at T = 1 next to the bare read of its gate weight
     (moe_probe_read, the same bytes) and an empty kernel, all cold."""
@@ -293,6 +348,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the decode sweep and router probes")
     ap.add_argument("--decode-only", action="store_true",
                     help="diagnostic: only the cold decode cases (for kernel traces), no benchmark line")
+    ap.add_argument("--ep-share-only", action="store_true",
+                    help="diagnostic: only the 32-expert DeepSeek-V4 share cases, no benchmark line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first write MIB MiB with a fill kernel and read them once with moe_probe_read "
                          "(kernels of known traffic that calibrate rocprofv3 WRITE_SIZE / FETCH_SIZE)")
@@ -311,6 +368,11 @@ def main():
     if args.decode_only:
         timer = ColdTimer(moe, torch)
         for key, v in decode_sweep(moe, torch, timer, None).items():
+            log(f"{key}: {v}")
+        return 0
+    if args.ep_share_only:
+        timer = ColdTimer(moe, torch)
+        for key, v in ep_share_sweep(moe, torch, timer).items():
             log(f"{key}: {v}")
         return 0
     if args.copy_probe:
@@ -369,6 +431,7 @@ def main():
         timer = ColdTimer(moe, torch)
         result["router"] = router_probe(moe, torch, timer)
         result["decode"] = decode_sweep(moe, torch, timer, W if cfg.name == "qwen3" else None)
+        result["ep_share_dsv4_32_experts"] = ep_share_sweep(moe, torch, timer)
         result["cold_timing"] = ("median event-pair time after a 1 GiB read, minus the empty event-pair "
                                  f"time ({timer.base:.2f} us)")
         del timer

@@ -991,7 +991,10 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
     return MOE_OK;
   }
   const int64_t t1 = mb * (a.F / 128), t2 = mb * (a.H / 128);
-  constexpr int NW = (F == F_BF16) ? MOE_TILED_WAVES : 4;
+  // 8 waves (2 x 4) for bf16 and fp8 at BLOCK_M >= 64; MX keeps 4 (measured:
+  // 8 waves were 7 % faster for the fp8 DeepSeek-V3 prefill, and no faster
+  // or slower for MX)
+  constexpr int NW = (F == F_MX) ? 4 : MOE_TILED_WAVES;
   switch (a.block_m) {
     case 32: return which == 1 ? launch_tiled_one<F, true, 32, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 32, 128, 3>(p, t2, s);
     case 64:

@@ -85,6 +85,8 @@ SMALL = [
     ("dsv4", dict(E=16, H=512, F=512, k=4), 300, 32),
     ("dsv4", dict(E=16, H=1024, F=512, k=4), 300, 64),
     ("dsv4", dict(E=8, H=512, F=1024, k=2), 700, 128),
+    # one GPU's share of DeepSeek-V4 over 8 GPUs: 32 experts at full dimensions
+    ("dsv4", dict(E=32), 16, 0),
 ]
 
 
