@@ -410,7 +410,8 @@ def main():
         achieved, peak, unit = g1_flops / (g1_us * 1e-6) / 1e12, MFMA_PEAK[cfg.wformat] / 1e12, "TFLOP/s"
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
-            "kernel": "grouped GEMM1 + SwiGLU (gemm_tiled)" if bm > 16 else "grouped GEMM1 + SwiGLU (gemm_stream)",
+            "kernel": "grouped GEMM1 + SwiGLU (" + ("gemm_stream" if bm == 16 else "gemm_pair_bf16"
+                                                   if bm == 128 and cfg.wformat == "bf16" else "gemm_tiled") + ")",
             "kernel_us": round(g1_us, 2), "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops,
             "mfma_frac": round(g1_flops / (g1_us * 1e-6) / MFMA_PEAK[cfg.wformat], 4),
             "hbm_frac": round(g1_bytes / (g1_us * 1e-6) / HBM_PEAK, 4)}

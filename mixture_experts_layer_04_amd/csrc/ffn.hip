@@ -86,7 +86,7 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
 
 namespace {
 struct Layout {
-  size_t xq, xs, act, act_s, act32, out, total;
+  size_t xq, xs, act, act_s, act32, out, pairs, total;
 };
 Layout ffn_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
   Layout L;
@@ -106,6 +106,8 @@ Layout ffn_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
   off += (q && block_m == 16) ? align_up(mp * F * sizeof(float), 256) : 0;
   L.out = off;
   off += align_up((size_t)T * k * H * 2, 256);
+  L.pairs = off;
+  off += ffn_paired(wformat, block_m) ? align_up(((size_t)align_max_blocks(T, k, E, block_m) + 1) * 4, 256) : 0;
   L.total = off;
   return L;
 }
@@ -124,6 +126,7 @@ void ffn_carve(FfnArgs& a, void* ws) {
   a.act_s = b + L.act_s;
   a.act32 = b + L.act32;
   a.out = b + L.out;
+  a.pairs = ffn_paired(a.wformat, a.block_m) ? b + L.pairs : nullptr;
 }
 
 static moe_status launch_gemm(const FfnArgs& a, int which, hipStream_t s) {
@@ -139,6 +142,7 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
   moe_status st = MOE_OK;
   if ((a.stages & MOE_STAGE_QUANT) && a.wformat != MOE_W_BF16) st = launch_quant_x(a, s);
+  if (st == MOE_OK && a.pairs && (a.stages & MOE_STAGE_QUANT)) st = launch_pair_table(a, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM1)) st = launch_gemm(a, 1, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM2)) st = launch_gemm(a, 2, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_COMBINE)) st = launch_finalize(a, s);

@@ -76,6 +76,7 @@ struct GemmP {
   void* act_s;            // fp32 [max_padded, F/128] (FP8) or e8m0 [max_padded, F/32] (MX)
   float* act32;           // BLOCK_M 16, FP8 / MX: fp32 SwiGLU rows [max_padded, F]
   uint16_t* out;          // [T*k, H] bf16
+  const int32_t* pairs;   // paired tiled kernel: pair table (pair_table_kernel)
   float lim;              // SwiGLU clamp (+inf: none)
   int H, F, k, A;
 };
@@ -348,7 +349,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     // expert's next blocks through the last-level cache)
     const int blk = (int)(L / ntn);
     const int nt = (int)(L % ntn);
-    const int e = p.block_expert[blk];
+    // uniform; readfirstlane keeps the weight descriptor in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
 
     // per-lane source offsets of the copy instructions (the K step is added
     // as a uniform offset)
@@ -644,6 +646,298 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 }
 
 // ---------------------------------------------------------------------------
+// Paired tiled kernel (bf16, BLOCK_M = 128, prefill).  A tile is up to two
+// consecutive blocks of one expert (256 rows) x 256 weight rows: each weight
+// byte copied to LDS feeds twice the rows of a 128 x 256 tile, and the copy
+// stream (the limit of the 128-row kernel) carries 1.5x fewer bytes per flop
+// for an expert of two blocks.  Blocks pair up from the start of each
+// expert's run (pair_table_kernel); an expert with an odd number of blocks
+// ends in a single-block tile, whose missing half is neither copied (an
+// empty buffer range returns zeros without touching memory) nor multiplied.
+// 4 waves as 2 x 2, one per SIMD, each 128 rows x 128 weight rows (GEMM1: 64
+// gate rows and the matching 64 up rows); K steps of 64 bytes per row (one
+// 32-wide MFMA step) in a 5-stage ring of 32 KiB stages (all of LDS), four
+// steps ahead of the multiply.
+constexpr int kPairBlock = 128;
+
+// Pair table: tab[0] = number of pairs, tab[1 + j] = first block of pair j
+// with bit 30 set when the pair holds two blocks.  One workgroup walks the
+// blocks 1024 at a time: an inclusive max-scan of the run starts gives each
+// block the first block of its expert's run, a sum-scan numbers the blocks
+// that start a pair (an even distance from that first block).
+__global__ __launch_bounds__(1024) void pair_table_kernel(const int32_t* be, const int32_t* npp, int32_t* tab) {
+  __shared__ int s_max[16];
+  __shared__ int s_cnt[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nblk = *npp / kPairBlock;
+  int carry_first = 0;  // first block of the run that reaches the chunk's start
+  int carry_pairs = 0;
+  for (int c0 = 0; c0 < nblk; c0 += 1024) {
+    const int b = c0 + tid;
+    const bool valid = b < nblk;
+    const int e = valid ? be[b] : -1;
+    const bool first = valid && (b == 0 || be[b - 1] != e);
+    int m = first ? b : -1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(m, off, 64);
+      if (lane >= off) m = max(m, o);
+    }
+    if (lane == 63) s_max[wave] = m;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) m = max(m, s_max[w]);
+    const int fb = max(m, carry_first);
+    const bool start = valid && ((b - fb) & 1) == 0;
+    const uint64_t bal = __ballot(start);
+    const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) s_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0, total = 0, cf = carry_first;
+    for (int w = 0; w < 16; ++w) {
+      const int c = s_cnt[w];
+      before += w < wave ? c : 0;
+      total += c;
+      cf = max(cf, s_max[w]);
+    }
+    if (start) {
+      const bool two = b + 1 < nblk && be[b + 1] == e;
+      tab[1 + carry_pairs + before + pos] = b | (two ? (1 << 30) : 0);
+    }
+    carry_first = cf;
+    carry_pairs += total;
+    __syncthreads();  // s_max / s_cnt are rewritten by the next chunk
+  }
+  if (tid == 0) tab[0] = carry_pairs;
+}
+
+template <bool G1, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
+  constexpr int BB = kPairBlock;  // rows per block
+  constexpr int BMT = 2 * BB;     // rows per tile
+  constexpr int BNW = 256;        // weight rows per tile
+  constexpr int NT = 64 * NW;
+  constexpr int WN = NW / 2;      // waves: 2 along M x WN along N
+  // K steps of 128 bytes per row (two 32-wide MFMA steps): every copy
+  // request is a whole 128-byte line (a CU keeps a fixed number of requests
+  // in flight, so the request size sets its copy rate).  A and B have rings
+  // of their own: A two 32 KiB slots, one step ahead; B (the weights, whose
+  // reads go to HBM) three slots, two steps ahead.
+  constexpr int RB = 128;
+  constexpr int CPR = RB / 16;    // 16-byte chunks per row and step
+  constexpr int KS = RB / 64;     // MFMA steps per K step
+  constexpr int ASZ = BMT * RB;
+  constexpr int BSZ = BNW * RB;
+  constexpr int NA = 2, NB = 3;
+  constexpr int DA = NA - 1, DB = NB - 1;  // steps each ring runs ahead
+  constexpr int FM = 8;             // 16-row fragments per wave (128 rows)
+  constexpr int FN = BNW / WN / 16;  // 16-column fragments per wave
+  constexpr int RW = BMT / NW;       // tile rows each wave copies
+  constexpr int LA = BMT * CPR / NT;  // copy instructions per wave per step (1 KiB each)
+  constexpr int LB = BNW * CPR / NT;
+  constexpr int LS = LA + LB;
+  static_assert(LB <= 63 && (!G1 || FN % 2 == 0) && NA * ASZ + NB * BSZ <= 163840, "rings / vmcnt / gate-up pairs");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave / WN;  // rows [128 wm, +128)
+  const int wn = wave % WN;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int K = G1 ? p.H : p.F;
+  const int N = G1 ? p.F : p.H;
+  const int BNO = G1 ? BNW / 2 : BNW;  // output columns per tile
+  const int ntn = N / BNO;
+  const int npairs = p.pairs[0];
+  const int nblk = *p.npp / BB;
+  const int64_t n_valid = (int64_t)npairs * ntn;
+  const int64_t per = (n_valid + 7) >> 3;
+  const int nk = K / (RB / 2);
+  const int rowbytes = K * 2;
+  const uint8_t* asrc = G1 ? p.x : p.act;
+  const uint8_t* wsrc = G1 ? p.w13 : p.w2;
+  const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
+  const rsrc_t ra = make_rsrc(asrc, (uint64_t)(G1 ? p.A / p.k : nblk * BB) * rowbytes);
+  const rsrc_t rnone = make_rsrc(asrc, 0);  // every read returns zero
+
+  // LDS layout of a slot: 128-byte rows, 16-byte chunk c of row rr at slot
+  // c ^ (rr / 2 % 8), as in gemm_tiled: a fragment read (16 rows x 4
+  // chunks) then hits no bank twice
+  auto lds_off = [](int rr, int c) { return rr * RB + 16 * (c ^ ((rr >> 1) & (CPR - 1))); };
+  // the tile row and chunk whose bytes copy lane `lane` of an instruction
+  // that fills 64 / CPR rows from row0 on (1 KiB, lane l at byte 16 l)
+  auto copy_src = [](int row0, int lane, int& rr, int& c) {
+    rr = row0 + lane / CPR;
+    c = (lane % CPR) ^ ((rr >> 1) & (CPR - 1));
+  };
+  // GEMM1: the first FN / 2 fragments are gate rows, the rest the matching up rows
+  auto frag_lrow = [&](int fn) {
+    return G1 ? (fn < FN / 2 ? wn * (BNW / (2 * WN)) + fn * 16 : BNW / 2 + wn * (BNW / (2 * WN)) + (fn - FN / 2) * 16)
+              : wn * (BNW / WN) + fn * 16;
+  };
+  auto weight_row = [&](int nt, int lrow) {
+    if (G1) return lrow < BNW / 2 ? nt * (BNW / 2) + lrow : p.F + nt * (BNW / 2) + (lrow - BNW / 2);
+    return nt * BNW + lrow;
+  };
+
+  for (int64_t it = blockIdx.x; it < 8 * per; it += gridDim.x) {
+    const int64_t L = xcd_tile(it, per);
+    if (L >= n_valid) continue;
+    // tile values are uniform; readfirstlane keeps them (and the buffer
+    // descriptors made from them) in scalar registers
+    const int pe = __builtin_amdgcn_readfirstlane(p.pairs[1 + (int)(L / ntn)]);
+    const int nt = (int)(L % ntn);
+    const int blk = pe & 0x3FFFFFFF;  // first block of the tile
+    const bool two = (pe >> 30) & 1;
+    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
+    const bool mine = wm == 0 || two;  // this wave's 128 rows exist
+
+    // wave w copies tile rows [RW w, RW w + RW): rows of the second block
+    // come from an empty range when the tile holds one block
+    const bool copy_rows = wave < NW / 2 || two;
+    const rsrc_t rA = copy_rows ? ra : rnone;
+    uint32_t ag[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+      int row, c;
+      copy_src(wave * RW + (64 / CPR) * i, lane, row, c);
+      bool v;
+      const int src = copy_rows ? a_row_index<G1>(p, blk, BB, row, v) : 0;  // padding rows read token 0
+      ag[i] = (uint32_t)src * rowbytes + 16 * c;
+    }
+    const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes, (uint64_t)erows * rowbytes);
+    uint32_t bg[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+      int row, c;
+      copy_src(wave * RW + (64 / CPR) * i, lane, row, c);
+      bg[i] = (uint32_t)weight_row(nt, row) * rowbytes + 16 * c;
+    }
+    // copies of step s (clamped to the last step: past the end a step is
+    // copied again into a slot no later step reads, so every barrier waits
+    // for the same count)
+    auto issue_a = [&](int s) {
+      uint8_t* st = lds + (s % NA) * ASZ;
+      s = s < nk ? s : nk - 1;
+#pragma unroll
+      for (int i = 0; i < LA; ++i) buf2lds16(rA, ag[i], s * RB, st + (wave * RW + (64 / CPR) * i) * RB);
+    };
+    auto issue_b = [&](int s) {
+      uint8_t* st = lds + NA * ASZ + (s % NB) * BSZ;
+      s = s < nk ? s : nk - 1;
+#pragma unroll
+      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * RB, st + (wave * RW + (64 / CPR) * i) * RB);
+    };
+
+    f32x4_t acc[FM][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    struct Frag {
+      bf16x8_t a[FM];
+      bf16x8_t b[FN];
+    };
+    auto rd = [&](int s, int ks, Frag& f) {
+      const uint8_t* As = lds + (s % NA) * ASZ;
+      const uint8_t* Bs = lds + NA * ASZ + (s % NB) * BSZ;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int rr = wm * 128 + fm * 16 + r;
+        f.a[fm] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(rr, 4 * ks + g));
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int rr = frag_lrow(fn) + r;
+        f.b[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rr, 4 * ks + g));
+      }
+    };
+    auto mm = [&](const Frag& f) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(f.a[fm], f.b[fn], acc[fm][fn]);
+    };
+    // Before step sn: this wave's LDS reads are done (lgkmcnt), its copies
+    // of A(sn) and B(sn) have landed (vmcnt: only B(sn + 1), the copies
+    // issued last, may remain), barrier, then A(sn + 1) into the A slot of
+    // step sn - 1 and B(sn + 2) into the B slot of step sn - 1.
+    auto next_step = [&](int sn) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
+      wait_vm<LB>();
+      barrier_no_fence();
+      issue_a(sn + DA);
+      issue_b(sn + DB);
+    };
+
+    __syncthreads();  // the previous tile is done with LDS
+    issue_a(0);
+    issue_b(0);
+    issue_b(1);
+    for (int s = 0; s < nk; ++s) {
+      next_step(s);
+      if (mine) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          Frag f;
+          rd(s, ks, f);
+          mm(f);
+        }
+      }
+    }
+    wait_vm<0>();     // the copies past the last step have landed too
+    __syncthreads();  // every wave is done reading the rings
+
+    // ---------------------------------------------------------------- epilogue
+    const int nrows = two ? BMT : BB;
+    if (G1) {
+      constexpr int BNA = BNW / 2;  // SwiGLU columns per tile
+      uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNA]
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int fa = 0; fa < FN / 2; ++fa)
+            st[(wm * 128 + fm * 16 + 4 * g + i) * BNA + wn * (BNA / WN) + fa * 16 + r] =
+                (uint16_t)f32_to_bf16_bits(swiglu(acc[fm][fa][i], acc[fm][fa + FN / 2][i], p.lim));
+      __syncthreads();
+      constexpr int CH = BNA * 2 / 16;  // 16-byte chunks per tile row
+      for (int idx = tid; idx < nrows * CH; idx += NT) {
+        const int lr = idx / CH;
+        const int c = idx % CH;
+        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNA * 2 + c * 16);
+        *reinterpret_cast<uint4*>(p.act + ((size_t)(blk * BB + lr) * p.F + nt * BNA) * 2 + c * 16) = val;
+      }
+    } else {
+      uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            st[(wm * 128 + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
+                (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
+      __syncthreads();
+      constexpr int CH = BNW * 2 / 16;
+      for (int idx = tid; idx < nrows * CH; idx += NT) {
+        const int lr = idx / CH;
+        const int c = idx % CH;
+        const int sid = p.sorted_ids[blk * BB + lr];
+        if (sid >= p.A) continue;
+        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNW * 2 + c * 16);
+        *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Stream kernel (BLOCK_M = 16, decode).  A weight element is used by at most
 // the 16 rows of one block, so the kernel is a weight stream: what decides
 // its speed is that every CU gets an even share of the weight bytes and keeps
@@ -723,7 +1017,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) void gemm_stream(GemmP p) {
     if (L >= n_valid) continue;
     const int blk = (int)(L / ntn);
     const int nt = (int)(L % ntn);
-    const int e = p.block_expert[blk];
+    // uniform; readfirstlane keeps the weight descriptor in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
     const int sid = p.sorted_ids[blk * 16 + r];
     const bool aval = sid < p.A;
     const int arow_i = G1 ? (aval ? sid / p.k : 0) : blk * 16 + r;
@@ -950,6 +1245,18 @@ moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   return MOE_OK;
 }
 
+#ifndef MOE_PAIR_WAVES
+#define MOE_PAIR_WAVES 8
+#endif
+template <bool G1>
+moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
+  // one workgroup per CU (the ring is all of LDS), each looping over tiles
+  constexpr int NW = MOE_PAIR_WAVES;
+  gemm_pair_bf16<G1, NW><<<tile_grid(max_tiles, 256), 64 * NW, 5 * 32768, s>>>(p);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 template <int F>
 moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   GemmP p;
@@ -967,6 +1274,7 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   p.act_s = a.act_s;
   p.act32 = static_cast<float*>(a.act32);
   p.out = static_cast<uint16_t*>(a.out);
+  p.pairs = static_cast<const int32_t*>(a.pairs);
   p.lim = a.swiglu_limit;
   p.H = a.H; p.F = a.F; p.k = a.k; p.A = a.T * a.k;
   const int64_t mb = align_max_blocks(a.T, a.k, a.E, a.block_m);
@@ -1002,6 +1310,10 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
       if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
       return launch_tiled_one<F, false, 64, 128, 3, NW>(p, t2, s);
     case 128:
+      if (F == F_BF16 && a.pairs) {
+        if (which == 1) return launch_pair_one<true>(p, t1, s);
+        if (a.H % 256 == 0) return launch_pair_one<false>(p, t2 / 2, s);
+      }
       if (which == 1) return launch_tiled_one<F, true, 128, 256, 3, NW>(p, t1, s);
       if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 128, 256, 3, NW>(p, t2 / 2, s);
       return launch_tiled_one<F, false, 128, 128, 3, NW>(p, t2, s);
@@ -1010,6 +1322,19 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
 }
 
 }  // namespace
+
+#ifndef MOE_PAIRED_TILES
+#define MOE_PAIRED_TILES 1
+#endif
+bool ffn_paired(int wformat, int block_m) {
+  return MOE_PAIRED_TILES && wformat == MOE_W_BF16 && block_m == kPairBlock;
+}
+
+moe_status launch_pair_table(const FfnArgs& a, hipStream_t s) {
+  pair_table_kernel<<<1, 1024, 0, s>>>(a.block_expert, a.num_post_padded, static_cast<int32_t*>(a.pairs));
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
 
 moe_status launch_gemm_bf16(const FfnArgs& a, int which, hipStream_t s) { return launch_gemm_fmt<F_BF16>(a, which, s); }
 moe_status launch_gemm_fp8(const FfnArgs& a, int which, hipStream_t s) { return launch_gemm_fmt<F_FP8>(a, which, s); }

@@ -72,6 +72,7 @@ struct FfnArgs {
   void* act_s;     // its scales (fp8 formats)
   void* act32;     // BLOCK_M 16 with fp8 formats: fp32 SwiGLU rows before requantisation
   void* out;       // expert outputs [T*k, H] bf16
+  void* pairs;     // paired tiled GEMMs (ffn_paired): pair table, max_blocks + 1 ints; else null
 };
 
 moe_status ffn_validate(const void* x, int wformat, const void* w13, const void* w13_scale, const void* w2,
@@ -80,6 +81,10 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
                         const int32_t* num_post_padded, int T, int H, int E, int F, int k, int block_m,
                         float swiglu_limit, const void* y);
 size_t ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat);
+// Whether the grouped GEMMs run the paired tiled kernel (two blocks of one
+// expert per tile), which needs the pair table built first.
+bool ffn_paired(int wformat, int block_m);
+moe_status launch_pair_table(const FfnArgs& a, hipStream_t stream);
 void ffn_carve(FfnArgs& a, void* ws);
 moe_status launch_ffn(const FfnArgs& a, hipStream_t stream);
 

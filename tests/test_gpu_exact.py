@@ -50,7 +50,7 @@ def _encode_e2m1(w):
     return codes[:, 0::2] | (codes[:, 1::2] << 4)
 
 
-def build(E, H, F, T, k, seed):
+def build(E, H, F, T, k, seed, kind="uniform"):
     rng = np.random.default_rng(seed)
     x = rng.integers(-4, 5, size=(T, H)).astype(np.float32)
     x[:, 1] = 8.0
@@ -72,7 +72,7 @@ def build(E, H, F, T, k, seed):
         for h in range(H):
             cols = rng.choice(free_f, 2, replace=False)
             w2[e, h, cols] = rng.choice([-1.0, 1.0], 2)
-    ids = make_topk_ids(T, k, E, seed=seed)
+    ids = make_topk_ids(T, k, E, seed=seed, kind=kind)
     w = rng.choice([0.25, 0.5], size=(T, k)).astype(np.float32)
     return x, w13, w2, ids, w
 
@@ -103,12 +103,21 @@ CASES = [("bf16", 256, 256, bm, T) for bm, T in ((16, 5), (16, 300), (32, 300), 
                                                                        (64, 200), (128, 200))]
 
 
-@pytest.mark.parametrize("fmt,H,F,bm,T", CASES)
-def test_expert_ffn_exact(fmt, H, F, bm, T):
+# bf16 at BLOCK_M 128 runs the paired tiles (two blocks of one expert per
+# tile): experts with an even and an odd number of blocks (uniform ids: 375
+# and 500 rows per expert), uneven counts from skewed ids, one expert with
+# one block (the hot expert set leaves the others empty), and a block table
+# longer than one 1024-block chunk of the pair table (checked on a sample).
+PAIRED = [("bf16", 256, 256, 128, 1500, "uniform", None), ("bf16", 512, 384, 128, 2000, "uniform", None),
+          ("bf16", 256, 512, 128, 3000, "skewed", None), ("bf16", 256, 256, 128, 100, "hot", None),
+          ("bf16", 256, 128, 128, 70000, "uniform", 300)]
+
+
+def _run_exact(fmt, H, F, bm, T, kind="uniform", sample=None):
     import mixture_experts_layer_04_amd as moe
     E, k = 8, 2
-    say(f"exact probe {fmt} H={H} F={F} E={E} k={k} T={T} block_m={bm}")
-    x, w13, w2, ids, w = build(E, H, F, T, k, seed=T + bm)
+    say(f"exact probe {fmt} H={H} F={F} E={E} k={k} T={T} block_m={bm} ids={kind}")
+    x, w13, w2, ids, w = build(E, H, F, T, k, seed=T + bm, kind=kind)
     xd, c13, s13, c2, s2 = to_device(fmt, x, w13, w2)
     ids_d = ids.cuda()
     w_d = torch.from_numpy(w).cuda()
@@ -116,7 +125,11 @@ def test_expert_ffn_exact(fmt, H, F, bm, T):
     y = moe.expert_ffn(xd, c13, c2, ids_d, w_d, s, b, n, bm, wformat=fmt, w13_scale=s13, w2_scale=s2)
     torch.cuda.synchronize()
     weights = offn.ExpertWeights(fmt, to_numpy(c13), to_numpy(c2), to_numpy(s13), to_numpy(s2))
-    ref, _ = offn.layer(to_numpy(xd), {"ids": ids.numpy(), "weights": w}, weights, E)
+    tokens = None
+    if sample is not None:
+        tokens = np.sort(np.random.default_rng(T).choice(T, sample, replace=False))
+        tokens[-1] = T - 1
+    ref, _ = offn.layer(to_numpy(xd), {"ids": ids.numpy(), "weights": w}, weights, E, tokens=tokens)
     # every true output is a multiple of 8; the float64 oracle is off by
     # ~1e-11 because it takes silu(32) = 32 (1 - 1.3e-14), so its nearest
     # integer is the exact value
@@ -124,5 +137,17 @@ def test_expert_ffn_exact(fmt, H, F, bm, T):
     assert np.max(np.abs(ref - exact)) < 1e-6 and np.all(exact % 8 == 0) and np.any(exact != 0)
     # exact equality of values (a zero may carry either sign)
     got = fm.bf16_bits_to_f64(to_numpy(y))
+    if tokens is not None:
+        got = got[tokens]
     bad = np.argwhere(got != exact)
     assert bad.size == 0, f"{len(bad)} of {got.size} outputs differ, first at {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("fmt,H,F,bm,T", CASES)
+def test_expert_ffn_exact(fmt, H, F, bm, T):
+    _run_exact(fmt, H, F, bm, T)
+
+
+@pytest.mark.parametrize("fmt,H,F,bm,T,kind,sample", PAIRED)
+def test_expert_ffn_exact_paired_tiles(fmt, H, F, bm, T, kind, sample):
+    _run_exact(fmt, H, F, bm, T, kind, sample)
