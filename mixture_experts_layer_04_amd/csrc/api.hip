@@ -143,6 +143,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   a.swiglu_limit = swiglu_limit;
   a.stages = MOE_STAGE_ALL;
   a.y = y;
+  a.ctrl = b + L.ctrl;  // the FFN's own region moves with the shapes; counters stay here
   ffn_carve(a, b + L.ffn);
   return launch_ffn(a, stream);
 }

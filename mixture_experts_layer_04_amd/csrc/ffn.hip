@@ -175,6 +175,7 @@ extern "C" moe_status moe_expert_ffn_stages(const void* x, int wformat, const vo
   a.swiglu_limit = swiglu_limit;
   a.stages = stages;
   a.y = y;
+  a.ctrl = workspace;
   ffn_carve(a, workspace);
   return launch_ffn(a, stream);
 }

@@ -77,6 +77,7 @@ struct GemmP {
   float* act32;           // BLOCK_M 16, FP8 / MX: fp32 SwiGLU rows [max_padded, F]
   uint16_t* out;          // [T*k, H] bf16
   const int32_t* pairs;   // paired tiled kernel: pair table (pair_table_kernel)
+  int* queue;             // paired tiled kernel: 8 XCD tile counters + done count, zero on entry and exit
   float lim;              // SwiGLU clamp (+inf: none)
   int H, F, k, A;
 };
@@ -783,9 +784,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
     return nt * BNW + lrow;
   };
 
-  for (int64_t it = blockIdx.x; it < 8 * per; it += gridDim.x) {
-    const int64_t L = xcd_tile(it, per);
-    if (L >= n_valid) continue;
+  // Tiles are handed out dynamically: XCD x (workgroups are dealt to the
+  // XCDs round-robin) owns the contiguous run [x per, x per + per) of
+  // logical tiles, and each of its workgroups takes the next one from the
+  // XCD's counter when it is done with the last, so the CUs of an XCD end
+  // within one tile of each other.  The index goes through the first LDS
+  // word while the rings are idle.
+  const int xcd = blockIdx.x & 7;
+  for (;;) {
+    __syncthreads();  // the previous tile (and the last index read) is done with LDS
+    if (tid == 0) *reinterpret_cast<volatile int*>(lds) = atomicAdd(p.queue + xcd, 1);
+    __syncthreads();
+    const int j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(lds));
+    __syncthreads();  // every wave has the index before the copies overwrite it
+    const int64_t L = (int64_t)xcd * per + j;
+    if (j >= per || L >= n_valid) break;
     // tile values are uniform; readfirstlane keeps them (and the buffer
     // descriptors made from them) in scalar registers
     const int pe = __builtin_amdgcn_readfirstlane(p.pairs[1 + (int)(L / ntn)]);
@@ -874,7 +887,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
       issue_b(sn + DB);
     };
 
-    __syncthreads();  // the previous tile is done with LDS
     issue_a(0);
     issue_b(0);
     issue_b(1);
@@ -934,6 +946,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
         *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
       }
     }
+  }
+  // the last workgroup to finish leaves the counters at zero for the next
+  // launch (every workgroup has made its last take before it counts itself)
+  if (tid == 0 && atomicAdd(p.queue + 8, 1) == (int)gridDim.x - 1) {
+#pragma unroll
+    for (int x = 0; x < 9; ++x) p.queue[x] = 0;
   }
 }
 
@@ -1275,6 +1293,7 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   p.act32 = static_cast<float*>(a.act32);
   p.out = static_cast<uint16_t*>(a.out);
   p.pairs = static_cast<const int32_t*>(a.pairs);
+  p.queue = reinterpret_cast<int*>(static_cast<char*>(a.ctrl) + kTileQueueOffset);
   p.lim = a.swiglu_limit;
   p.H = a.H; p.F = a.F; p.k = a.k; p.A = a.T * a.k;
   const int64_t mb = align_max_blocks(a.T, a.k, a.E, a.block_m);

@@ -15,10 +15,13 @@ namespace moe {
 //   [0, 4)            sticky alignment error bits
 //   [4, 8)            alignment counter (multi-workgroup path)
 //   [8, 12)           fused route + align counter (token tiles done)
+//   [16, 52)          grouped GEMM tile queues: one per XCD, then the
+//                     count of workgroups done
 //   [256, kCtrlBytes) one counter per router token tile
 constexpr size_t kCtrlBytes = 65536;
 constexpr size_t kAlignCounterOffset = 4;
 constexpr size_t kFusedCounterOffset = 8;
+constexpr size_t kTileQueueOffset = 16;
 constexpr size_t kCounterOffset = 256;
 constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);
 
@@ -73,6 +76,7 @@ struct FfnArgs {
   void* act32;     // BLOCK_M 16 with fp8 formats: fp32 SwiGLU rows before requantisation
   void* out;       // expert outputs [T*k, H] bf16
   void* pairs;     // paired tiled GEMMs (ffn_paired): pair table, max_blocks + 1 ints; else null
+  void* ctrl;      // control block of the caller's workspace (tile queues)
 };
 
 moe_status ffn_validate(const void* x, int wformat, const void* w13, const void* w13_scale, const void* w2,

@@ -175,7 +175,9 @@ def test_layer_shapes_share_one_workspace():
     import mixture_experts_layer_04_amd as moe
     shapes = [(dict(F=256), 100, 16), (dict(E=16, k=4, H=256, F=128, scoring="sigmoid", has_bias=True, n_group=4,
                                           topk_group=2, routed_scale=2.5), 64, 16),
-              (dict(F=256), 3, 0), (dict(E=16, k=4, H=256, F=128), 17, 0), (dict(F=256), 100, 16)]
+              (dict(F=256), 3, 0), (dict(E=16, k=4, H=256, F=128), 17, 0), (dict(F=256), 100, 16),
+              # paired bf16 tiles with their tile queues, at two shapes
+              (dict(F=256), 300, 128), (dict(E=16, k=4, H=256, F=128), 700, 128), (dict(F=256), 300, 128)]
     shared = torch.zeros(1 << 26, dtype=torch.uint8, device="cuda")
     for over, T, bm in shapes:
         cfg = get_config("toy", **over)
@@ -191,6 +193,7 @@ def test_layer_shapes_share_one_workspace():
         y_ref = moe.layer(*args, ws=fresh, **kw)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), (over, T, bm)
+        assert int(shared[:65536].count_nonzero()) == 0, "control block not left at zero"
 
 
 SHARED = [("toy", {}, 16, 0), ("toy", dict(F=256), 100, 16), ("toy", dict(F=256), 300, 64),
