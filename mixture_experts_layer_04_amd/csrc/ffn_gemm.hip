@@ -77,7 +77,7 @@ struct GemmP {
   float* act32;           // BLOCK_M 16, FP8 / MX: fp32 SwiGLU rows [max_padded, F]
   uint16_t* out;          // [T*k, H] bf16
   const int32_t* pairs;   // paired tiled kernel: pair table (pair_table_kernel)
-  int* queue;             // paired tiled kernel: 8 XCD tile counters + done count, zero on entry and exit
+  int* queue;             // tiled kernels: 8 XCD tile counters + done count, zero on entry and exit
   float lim;              // SwiGLU clamp (+inf: none)
   int H, F, k, A;
 };
@@ -342,9 +342,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     return nt * BNW + lrow;
   };
 
-  for (int64_t it = blockIdx.x; it < 8 * per; it += gridDim.x) {
-    const int64_t L = xcd_tile(it, per);
-    if (L >= n_valid) continue;
+  // Tiles: XCD x (workgroups are dealt to the XCDs round-robin) owns the
+  // contiguous run [x per, x per + per) of logical tiles.  A workgroup's
+  // first tile is its index among the XCD's workgroups; when the XCD has
+  // more tiles than workgroups, each takes the next one from the XCD's
+  // counter when it is done with the last, so the CUs of an XCD end within
+  // one tile of each other.  The index goes through the first LDS word
+  // while the ring is idle.
+  const int xcd = blockIdx.x & 7;
+  const int wpx = (int)(gridDim.x >> 3);  // workgroups per XCD
+  const bool dyn = per > wpx;
+  int j = (int)(blockIdx.x >> 3);
+  for (;; ) {
+    const int64_t L = (int64_t)xcd * per + j;
+    if (j >= per || L >= n_valid) break;
     // block-major: the N tiles of a block follow each other (its A rows stay
     // in the L2 for all of them; the weight tiles are shared with the
     // expert's next blocks through the last-level cache)
@@ -500,7 +511,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
       issue(sn + D < nk ? sn + D : nk - 1, (sn + D) % NS);
     };
 
-    __syncthreads();  // the previous tile is done with LDS
 #pragma unroll
     for (int s = 0; s < D; ++s) issue(s < nk ? s : nk - 1, s % NS);
     if constexpr (F == F_BF16) {
@@ -537,6 +547,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
         mm(f0);
       }
     }
+    wait_vm<0>();     // the copies past the last step have landed too
     __syncthreads();  // every wave is done reading the stage buffers
 
     // ---------------------------------------------------------------- epilogue
@@ -643,6 +654,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
         *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
       }
     }
+    if (!dyn) break;
+    __syncthreads();  // this tile (and the last index read) is done with LDS
+    if (tid == 0) *reinterpret_cast<volatile int*>(lds) = wpx + atomicAdd(p.queue + xcd, 1);
+    __syncthreads();
+    j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(lds));
+    __syncthreads();  // every wave has the index before the copies overwrite it
+  }
+  // the last workgroup to finish leaves the counters at zero for the next
+  // launch (every workgroup has made its last take before it counts itself)
+  if (dyn && tid == 0 && atomicAdd(p.queue + 8, 1) == (int)gridDim.x - 1) {
+#pragma unroll
+    for (int x = 0; x < 9; ++x) p.queue[x] = 0;
   }
 }
 
@@ -784,19 +807,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
     return nt * BNW + lrow;
   };
 
-  // Tiles are handed out dynamically: XCD x (workgroups are dealt to the
-  // XCDs round-robin) owns the contiguous run [x per, x per + per) of
-  // logical tiles, and each of its workgroups takes the next one from the
-  // XCD's counter when it is done with the last, so the CUs of an XCD end
-  // within one tile of each other.  The index goes through the first LDS
-  // word while the rings are idle.
+  // Tiles: XCD x (workgroups are dealt to the XCDs round-robin) owns the
+  // contiguous run [x per, x per + per) of logical tiles.  A workgroup's
+  // first tile is its index among the XCD's workgroups; when the XCD has
+  // more tiles than workgroups, each takes the next one from the XCD's
+  // counter when it is done with the last, so the CUs of an XCD end within
+  // one tile of each other.  The index goes through the first LDS word
+  // while the ring is idle.
   const int xcd = blockIdx.x & 7;
-  for (;;) {
-    __syncthreads();  // the previous tile (and the last index read) is done with LDS
-    if (tid == 0) *reinterpret_cast<volatile int*>(lds) = atomicAdd(p.queue + xcd, 1);
-    __syncthreads();
-    const int j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(lds));
-    __syncthreads();  // every wave has the index before the copies overwrite it
+  const int wpx = (int)(gridDim.x >> 3);  // workgroups per XCD
+  const bool dyn = per > wpx;
+  int j = (int)(blockIdx.x >> 3);
+  for (;; ) {
     const int64_t L = (int64_t)xcd * per + j;
     if (j >= per || L >= n_valid) break;
     // tile values are uniform; readfirstlane keeps them (and the buffer
@@ -946,10 +968,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
         *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
       }
     }
+    if (!dyn) break;
+    __syncthreads();  // this tile (and the last index read) is done with LDS
+    if (tid == 0) *reinterpret_cast<volatile int*>(lds) = wpx + atomicAdd(p.queue + xcd, 1);
+    __syncthreads();
+    j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(lds));
+    __syncthreads();  // every wave has the index before the copies overwrite it
   }
   // the last workgroup to finish leaves the counters at zero for the next
   // launch (every workgroup has made its last take before it counts itself)
-  if (tid == 0 && atomicAdd(p.queue + 8, 1) == (int)gridDim.x - 1) {
+  if (dyn && tid == 0 && atomicAdd(p.queue + 8, 1) == (int)gridDim.x - 1) {
 #pragma unroll
     for (int x = 0; x < 9; ++x) p.queue[x] = 0;
   }
@@ -1258,7 +1286,10 @@ moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   using T = Tr<F>;
   const size_t sc = (F == F_BF16) ? 0 : (size_t)((BM + BNW + 64 * NW - 1) / (64 * NW)) * 64 * NW * 4;
   const size_t lds = (size_t)NS * ((size_t)BM * 128 + (size_t)BNW * T::BROW + sc);
-  gemm_tiled<F, G1, BM, BNW, NS, NW><<<tile_grid(max_tiles, 512), 64 * NW, lds, s>>>(p);
+  // the workgroups resident at once (each loops over tiles)
+  static int cache[64] = {0};
+  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_tiled<F, G1, BM, BNW, NS, NW>), 64 * NW, lds, cache);
+  gemm_tiled<F, G1, BM, BNW, NS, NW><<<tile_grid(max_tiles, wgs), 64 * NW, lds, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -1270,7 +1301,9 @@ template <bool G1>
 moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   // one workgroup per CU (the ring is all of LDS), each looping over tiles
   constexpr int NW = MOE_PAIR_WAVES;
-  gemm_pair_bf16<G1, NW><<<tile_grid(max_tiles, 256), 64 * NW, 5 * 32768, s>>>(p);
+  static int cache[64] = {0};
+  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_bf16<G1, NW>), 64 * NW, 5 * 32768, cache);
+  gemm_pair_bf16<G1, NW><<<tile_grid(max_tiles, wgs), 64 * NW, 5 * 32768, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
