@@ -126,7 +126,7 @@ const char* moe_status_str(moe_status s);
  * (the gate split exactly into three bf16 planes on matrix cores) in one
  * fixed order for every T: a token's logits and choice do not depend on the
  * batch it is in ([Router] §9).  Scores, keys and weights are fp32.
- * Constraints: 0 <= T <= 261120, H >= 128 and a multiple of 128,
+ * Constraints: 0 <= T <= 2^24, H >= 128 and a multiple of 128,
  * 1 <= k <= E <= 1024, k <= 16; n_group divides E, E/n_group >= 2 when n_group > 1,
  * 1 <= topk_group <= n_group, k <= topk_group * E / n_group.
  * ------------------------------------------------------------------------ */

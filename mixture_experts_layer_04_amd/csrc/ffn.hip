@@ -29,12 +29,15 @@ struct FinP {
   int H, E, k;
 };
 
+// grid (T, column splits): a workgroup takes every gridDim.y-th run of 2048
+// columns of token blockIdx.x (at small T the columns of a token are split
+// over several workgroups, so each thread makes one pass)
 template <int KT>  // = k
 __global__ __launch_bounds__(256) void finalize_kernel(FinP p) {
   const int t = blockIdx.x;
   const int32_t* ids = p.ids + (size_t)t * p.k;
   const float* w = p.w + (size_t)t * p.k;
-  for (int h = threadIdx.x * 8; h < p.H; h += 256 * 8)
+  for (int h = (blockIdx.y * 256 + threadIdx.x) * 8; h < p.H; h += gridDim.y * 256 * 8)
     *reinterpret_cast<uint4*>(p.y + (size_t)t * p.H + h) = combine8<KT>(p.out, ids, w, t, h, p.H, p.E, KT);
 }
 
@@ -47,9 +50,10 @@ moe_status launch_finalize(const FfnArgs& a, hipStream_t s) {
   p.w = a.topk_weights;
   p.y = static_cast<uint16_t*>(a.y);
   p.H = a.H; p.E = a.E; p.k = a.k;
+  const dim3 grid(a.T, a.T < 512 ? (a.H + 2047) / 2048 : 1);
   switch (a.k) {
 #define MOE_FIN(K) \
-  case K: finalize_kernel<K><<<a.T, 256, 0, s>>>(p); break;
+  case K: finalize_kernel<K><<<grid, 256, 0, s>>>(p); break;
     MOE_FIN(1) MOE_FIN(2) MOE_FIN(3) MOE_FIN(4) MOE_FIN(5) MOE_FIN(6) MOE_FIN(7) MOE_FIN(8)
     MOE_FIN(9) MOE_FIN(10) MOE_FIN(11) MOE_FIN(12) MOE_FIN(13) MOE_FIN(14) MOE_FIN(15) MOE_FIN(16)
 #undef MOE_FIN

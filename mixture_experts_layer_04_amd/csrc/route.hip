@@ -47,6 +47,8 @@ constexpr int KCH = 128;          // K chunk
 constexpr int CPG = 4;            // chunks per group
 constexpr int SMALL_T_MAX = 256;  // largest T routed with the decode layout
 constexpr int PROW = 104;         // LDS plane row (bf16): hi[32] mid[32] lo[32] pad[8]
+// the decode layout's election counters: one per 16-token tile
+static_assert(SMALL_T_MAX / 16 <= kMaxCounters, "router counters");
 
 struct RouteParams {
   const uint16_t* x;
@@ -260,16 +262,18 @@ __device__ __forceinline__ void sum_groups(const RouteParams& p, int t, float (&
     ec[s] = min(s * kWave + lane, p.E - 1);
     l[s] = p.part[(size_t)t * p.E + ec[s]];
   }
-  for (int j0 = 1; j0 < p.NG; j0 += 8) {
-    float pv[8][SLOTS];
+  // U groups' sums in flight at once (64 VGPRs of them)
+  constexpr int U = SLOTS <= 4 ? 16 : (64 / SLOTS < 4 ? 4 : 64 / SLOTS);
+  for (int j0 = 1; j0 < p.NG; j0 += U) {
+    float pv[U][SLOTS];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int jj = min(j0 + u, p.NG - 1);
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) pv[u][s] = p.part[((size_t)jj * p.T + t) * p.E + ec[s]];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < U; ++u)
       if (j0 + u < p.NG) {
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s) l[s] += pv[u][s];
@@ -552,14 +556,14 @@ size_t route_workspace_size(int T, int H, int E) {
 
 moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
                           int topk_group, int scoring, const int32_t* ids, const float* w) {
-  if (T < 0 || H < 128 || H % 128 != 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return MOE_E_INVAL;
+  if (T < 0 || T > (1 << 24) || H < 128 || H % 128 != 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E)
+    return MOE_E_INVAL;
   if (scoring != MOE_SOFTMAX && scoring != MOE_SIGMOID && scoring != MOE_SQRTSOFTPLUS) return MOE_E_INVAL;
   if (n_group < 1 || n_group > 64 || E % n_group != 0) return MOE_E_INVAL;
   if (n_group > 1 && (E / n_group < 2)) return MOE_E_INVAL;
   if (topk_group < 1 || topk_group > n_group) return MOE_E_INVAL;
   if ((int64_t)k > (int64_t)topk_group * (E / n_group)) return MOE_E_INVAL;
   if (T > 0 && (!x || !gate || !ids || !w)) return MOE_E_INVAL;
-  if (ceil_div(T, 16) > kMaxCounters) return MOE_E_INVAL;
   return MOE_OK;
 }
 
