@@ -131,9 +131,6 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   int32_t* bexp = reinterpret_cast<int32_t*>(b + L.bexp);
   int32_t* npp = reinterpret_cast<int32_t*>(b + L.npp);
 
-  st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
-                          n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream);
-  if (st != MOE_OK) return st;
   FfnArgs a;
   a.x = x; a.wformat = wformat;
   a.w13 = w13; a.w13_scale = w13_scale; a.w2 = w2; a.w2_scale = w2_scale;
@@ -145,6 +142,13 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   a.y = y;
   a.ctrl = b + L.ctrl;  // the FFN's own region moves with the shapes; counters stay here
   ffn_carve(a, b + L.ffn);
+  // at decode the router quantises x for the fp8 formats on the way (one
+  // launch fewer)
+  const int qfmt = wformat == MOE_W_FP8_BLOCK128 ? 1 : wformat == MOE_W_MXFP4 ? 2 : 0;
+  a.x_ready = qfmt != 0 && route_quantizes_x(T, E);
+  st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+                          n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream, a.xq, a.xs, qfmt);
+  if (st != MOE_OK) return st;
   return launch_ffn(a, stream);
 }
 

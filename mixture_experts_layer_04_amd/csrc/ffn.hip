@@ -145,7 +145,7 @@ static moe_status launch_gemm(const FfnArgs& a, int which, hipStream_t s) {
 moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
   moe_status st = MOE_OK;
-  if ((a.stages & MOE_STAGE_QUANT) && a.wformat != MOE_W_BF16) st = launch_quant_x(a, s);
+  if ((a.stages & MOE_STAGE_QUANT) && a.wformat != MOE_W_BF16 && !a.x_ready) st = launch_quant_x(a, s);
   if (st == MOE_OK && a.pairs && (a.stages & MOE_STAGE_QUANT)) st = launch_pair_table(a, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM1)) st = launch_gemm(a, 1, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM2)) st = launch_gemm(a, 2, s);
@@ -178,6 +178,7 @@ extern "C" moe_status moe_expert_ffn_stages(const void* x, int wformat, const vo
   a.T = T; a.H = H; a.E = E; a.F = F; a.k = k; a.block_m = block_m;
   a.swiglu_limit = swiglu_limit;
   a.stages = stages;
+  a.x_ready = false;
   a.y = y;
   a.ctrl = workspace;
   ffn_carve(a, workspace);

@@ -55,6 +55,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace moe {
 
@@ -138,29 +139,6 @@ __device__ __forceinline__ float swiglu(float g, float u, float lim) {
   return g / (1.f + expf(-g)) * u;
 }
 
-// e4m3 (OCP) of v, v already within [-448, 448]; round to nearest even
-__device__ __forceinline__ uint32_t to_e4m3(float v) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xFFu;
-}
-__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-  return (uint32_t)hi;
-}
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
-
-// Power-of-two scale >= v (v > 0) as its e8m0 code; 127 (2^0) for v == 0.
-__device__ __forceinline__ uint32_t e8m0_at_least(float v) {
-  if (!(v > 0.f)) return 127u;
-  const uint32_t u = __float_as_uint(v);
-  uint32_t e = (u >> 23) & 0xFFu;
-  if (e == 0u) return 1u;                 // below the normal range: smallest code used
-  if ((u & 0x7FFFFFu) != 0u) e += 1u;     // not a power of two: round up
-  return e > 254u ? 254u : e;
-}
-__device__ __forceinline__ float e8m0_value(uint32_t code) { return __uint_as_float(code << 23); }
-__device__ __forceinline__ float e8m0_inv(uint32_t code) { return __uint_as_float((254u - code) << 23); }
-
 // ---------------------------------------------------------------------------
 // Activation quantisation of x (FP8: per 128, fp32 scale amax/448;
 // MX: per 32, e8m0 scale pow2_at_least(amax/448)).  One workgroup per token,
@@ -181,11 +159,11 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, uint8_t
     for (int off = 1; off < GL; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
     float inv;
     if (F == F_FP8) {
-      const float s = m > 0.f ? m / 448.f : 1.f;
+      const float s = fp8_group_scale(m);
       inv = 1.f / s;
       if ((lane & 15) == 0) static_cast<float*>(xs)[(size_t)t * (H / 128) + h / 128] = s;
     } else {
-      const uint32_t c = e8m0_at_least(m / 448.f);
+      const uint32_t c = mx_group_code(m);
       inv = e8m0_inv(c);
       if ((lane & 3) == 0) static_cast<uint8_t*>(xs)[(size_t)t * (H / 32) + h / 32] = (uint8_t)c;
     }
@@ -595,7 +573,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
             float amax = xch[lr];
 #pragma unroll
             for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, xch[w2 * BM + lr]);
-            const float sc = amax > 0.f ? amax / 448.f : 1.f;
+            const float sc = fp8_group_scale(amax);
             const float inv = 1.f / sc;
             if (wn == 0 && r == 0) act_s[(size_t)(blk * BM + lr) * (p.F / 128) + nt] = sc;
 #pragma unroll
@@ -614,7 +592,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
               float mm = fmaxf(fabsf(v[fm][2 * gp][i]), fabsf(v[fm][2 * gp + 1][i]));
 #pragma unroll
               for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
-              const uint32_t c = e8m0_at_least(mm / 448.f);
+              const uint32_t c = mx_group_code(mm);
               const float inv = e8m0_inv(c);
               const int lc = lcol0 + gp * 32;
               if (r == 0) act_s[(size_t)(blk * BM + lr) * (p.F / 32) + (nt * BNA + lc) / 32] = (uint8_t)c;
@@ -1224,11 +1202,11 @@ __global__ __launch_bounds__(256) void requant_act_kernel(GemmP p) {
       for (int off = 1; off < GL; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
       float inv;
       if (F == F_FP8) {
-        const float sc = m > 0.f ? m / 448.f : 1.f;
+        const float sc = fp8_group_scale(m);
         inv = 1.f / sc;
         if ((lane & 15) == 0) static_cast<float*>(p.act_s)[(size_t)row * (p.F / 128) + c / 128] = sc;
       } else {
-        const uint32_t code = e8m0_at_least(m / 448.f);
+        const uint32_t code = mx_group_code(m);
         inv = e8m0_inv(code);
         if ((lane & 3) == 0) static_cast<uint8_t*>(p.act_s)[(size_t)row * (p.F / 32) + c / 32] = (uint8_t)code;
       }

@@ -37,10 +37,14 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
 // two launches and launch_align.
 // n_shared = 1: slot k of every token is the shared expert (id E, weight 1),
 // ids / weights rows hold k + 1 slots and the alignment covers E + 1 experts.
+// qfmt 1 (FP8) / 2 (MX): where route_quantizes_x(T, E), the router also
+// quantises x into xq / xs as the FFN's activation stage would; 0: no.
 moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
-                              int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream);
+                              int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
+                              void* xq, void* xs, int qfmt);
+bool route_quantizes_x(int T, int E);
 size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared);
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,
@@ -67,6 +71,7 @@ struct FfnArgs {
   int T, H, E, F, k, block_m;
   float swiglu_limit;  // +inf: no clamp
   int stages;      // bit mask of MOE_STAGE_* to run
+  bool x_ready;    // xq / xs already hold the quantised x (the router wrote them)
   void* y;
   // workspace regions
   void* xq;        // quantised x (fp8 formats)

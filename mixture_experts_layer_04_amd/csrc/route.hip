@@ -38,6 +38,7 @@
 #include "align_block.h"
 #include "common.h"
 #include "launch.h"
+#include "quant.h"
 
 namespace moe {
 
@@ -64,6 +65,12 @@ struct RouteParams {
   int n_shared;  // 1: slot k of every token is the shared expert (id E, weight 1)
   int ks;        // ids / weights row stride, k + n_shared
   float scale;
+  // decode layout in a layer call: also quantise x for the FP8 (1) or MX (2)
+  // expert GEMMs into xq [T, H] e4m3 and xs (fp32 [T, H/128] or e8m0
+  // [T, H/32]); 0: not
+  uint8_t* xq;
+  void* xs;
+  int qfmt;
   int NF, NC, NG;
 };
 
@@ -287,6 +294,63 @@ __device__ __forceinline__ void sum_groups(const RouteParams& p, int t, float (&
   }
 }
 
+// Activation quantisation of one 128-wide K chunk of token t, from the x
+// fragments a wave holds for its MFMA steps (lane (r, q) holds x[t, c*128 +
+// 32 s + 8 q .. +8] for s < 4): for FP8 the chunk is one group, for MX each
+// s is one group of 32.  Same arithmetic as the quantisation kernel.
+__device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv, int c, int q,
+                                            const bf16x8_t (&a)[4]) {
+  float v[4][8];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4_t u = __builtin_bit_cast(u32x4_t, a[s]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[s][2 * i] = bf16_lo(u[i]);
+      v[s][2 * i + 1] = bf16_hi(u[i]);
+    }
+  }
+  uint8_t* xq = p.xq + (size_t)t * p.H + c * KCH + 8 * q;
+  auto store8 = [&](int s, float inv) {
+    uint2 w;
+    w.x = pack4_e4m3(clamp448(v[s][0] * inv), clamp448(v[s][1] * inv), clamp448(v[s][2] * inv),
+                     clamp448(v[s][3] * inv));
+    w.y = pack4_e4m3(clamp448(v[s][4] * inv), clamp448(v[s][5] * inv), clamp448(v[s][6] * inv),
+                     clamp448(v[s][7] * inv));
+    *reinterpret_cast<uint2*>(xq + 32 * s) = w;
+  };
+  if (p.qfmt == 1) {
+    float m = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[s][i]));
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));  // the 4 lanes of a token row
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const float sc = fp8_group_scale(m);
+    const float inv = 1.f / sc;
+    if (tv) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) store8(s, inv);
+      if (q == 0) static_cast<float*>(p.xs)[(size_t)t * (p.H / KCH) + c] = sc;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[s][i]));
+      m = fmaxf(m, __shfl_xor(m, 16, kWave));
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      const uint32_t code = mx_group_code(m);
+      if (tv) {
+        store8(s, e8m0_inv(code));
+        if (q == 0) static_cast<uint8_t*>(p.xs)[(size_t)t * (p.H / 32) + c * 4 + s] = (uint8_t)code;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token
 // tiles.  FUSE: the last token tile also aligns (dynamic LDS of
@@ -328,6 +392,8 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
       split8(g0[s], g1[s], bh, bm, bl);
       acc = mfma3(a[s], bh, bm, bl, acc);
     }
+    // the workgroups of expert fragment 0 cover every chunk of the tile once
+    if (p.qfmt != 0 && f == 0) quant_chunk(p, t, tv, c, q, a);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][4 * q + i][r] = acc[i];
@@ -571,7 +637,8 @@ namespace {
 moe_status route_launch(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int n_shared, int32_t* ids, float* weights, float* logits_out, void* ws,
-                        const AlignParams* ap, hipStream_t stream) {
+                        const AlignParams* ap, hipStream_t stream, void* xq = nullptr, void* xs = nullptr,
+                        int qfmt = 0) {
   RouteParams p;
   p.x = static_cast<const uint16_t*>(x);
   p.gate = gate;
@@ -588,6 +655,14 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.n_group = n_group; p.topk_group = topk_group;
   p.scoring = scoring; p.renorm = renormalize != 0;
   p.scale = routed_scale;
+  p.xq = nullptr;
+  p.xs = nullptr;
+  p.qfmt = 0;
+  if (!use_large(T, E) && qfmt != 0) {
+    p.xq = static_cast<uint8_t*>(xq);
+    p.xs = xs;
+    p.qfmt = qfmt;
+  }
   p.NF = ceil_div(E, 16);
   p.NC = H / KCH;
   p.NG = ceil_div(p.NC, CPG);
@@ -614,17 +689,20 @@ size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
   return r > a ? r : a;
 }
 
+bool route_quantizes_x(int T, int E) { return !use_large(T, E); }
+
 moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
-                              int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream) {
+                              int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
+                              void* xq, void* xs, int qfmt) {
   // the alignment sees the shared expert as expert E and slot k
   const int Ea = E + n_shared, ka = k + n_shared;
   if (T == 0) return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
   if (!use_large(T, E)) {
     const AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
     return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
-                        n_shared, ids, weights, nullptr, ws, &ap, stream);
+                        n_shared, ids, weights, nullptr, ws, &ap, stream, xq, xs, qfmt);
   }
   moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
                                routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream);
@@ -670,7 +748,7 @@ extern "C" moe_status moe_route_align(const void* x, const float* gate, const fl
   if (workspace_bytes < route_align_workspace_size(T, H, E, k, n_shared)) return MOE_E_WORKSPACE;
   return launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                             n_shared, block_m, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded,
-                            workspace, stream);
+                            workspace, stream, nullptr, nullptr, 0);
 }
 
 extern "C" size_t moe_route_align_workspace_size(int T, int H, int E, int k, int n_shared) {

@@ -128,13 +128,28 @@ def test_layer_full_size_sampled(name, T):
     check_layer(cfg, T, 0, sample=4 if cfg.wformat != "bf16" else 6)
 
 
-def test_expert_ffn_matches_layer():
+MATCH = [("toy", dict(F=256), 200, 32), ("toy", dict(F=256), 300, 128),
+         ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 37, 16),
+         ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 250, 32),
+         ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 300, 32),
+         ("dsv4", dict(E=16, H=512, F=512, k=4), 37, 16), ("dsv4", dict(E=16, H=1024, F=512, k=4), 200, 64),
+         ("dsv4", dict(E=16, H=1024, F=512, k=4), 400, 64)]
+
+
+@pytest.mark.parametrize("name,over,T,bm", MATCH)
+def test_expert_ffn_matches_layer(name, over, T, bm):
+    """moe_layer gives the bits of moe_align + moe_expert_ffn on its routing.
+    For the fp8 formats at T <= 256 the layer's router quantises x on the way
+    and the FFN skips its quantisation kernel; above that both quantise in
+    the FFN."""
     import mixture_experts_layer_04_amd as moe
-    cfg = get_config("toy", F=256)
-    x, W, y, ids, w, _ = check_layer(cfg, 200, 32)
-    s, b, n = moe.align(ids, cfg.E, 32)
-    y2 = moe.expert_ffn(x, W["w13"], W["w2"], ids, w, s, b, n, 32)
-    assert torch.equal(y, y2)
+    cfg = get_config(name, **over)
+    x, W, y, ids, w, _ = check_layer(cfg, T, bm)
+    s, b, n = moe.align(ids, cfg.E, bm)
+    y2 = moe.expert_ffn(x, W["w13"], W["w2"], ids, w, s, b, n, bm, wformat=cfg.wformat,
+                        w13_scale=W["w13_scale"], w2_scale=W["w2_scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
 def test_layer_graph_capture_and_determinism():
