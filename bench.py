@@ -81,7 +81,7 @@ def touched_experts(cfg, T):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("ffn_gemm.hip", "common.h", "launch.h"):
+    for f in ("ffn_gemm.hip", "common.h", "launch.h", "quant.h"):
         with open(os.path.join(ROOT, "mixture_experts_layer_04_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
