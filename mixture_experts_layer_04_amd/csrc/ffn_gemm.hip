@@ -102,7 +102,7 @@ struct Tr<F_FP8> {
 template <>
 struct Tr<F_MX> {
   static constexpr int AB = 1;
-  static constexpr int KSTEP = 128;
+  static constexpr int KSTEP = 128;    // per MFMA step; the tiled kernel can take KMX = 2 of them per K step
   static constexpr int BROW = 64;
   static constexpr int BNA_STREAM = 32;
 };
@@ -263,28 +263,50 @@ __device__ __forceinline__ int swz(int c, int row) {
   return c ^ ((row / (16 / CPR)) & (CPR - 1));
 }
 
-template <int F, bool G1, int BM, int BNW, int NS, int NW>
+// Slot of B chunk c of tile row rr: 128-byte rows as the A rows; 64-byte
+// rows (MX with one MFMA step per K step) c ^ (rr / 2 % 4) (measured on
+// gfx950: with it a fragment read of 16 rows hits no LDS bank twice, with
+// c ^ (rr / 4 % 4) it did)
+template <int CPRB>
+__device__ __forceinline__ int bswz(int c, int rr) {
+  return CPRB == 8 ? swz<8>(c, rr) : c ^ ((rr >> 1) & 3);
+}
+
+template <int F, bool G1, int BM, int BNW, int NS, int NW, int KMX>
 __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
   using T = Tr<F>;
-  constexpr int CPRB = T::BROW / 16;   // 16-byte chunks per B row and step
-  constexpr int ASZ = BM * 128;
-  constexpr int BSZ = BNW * T::BROW;
+  // MX with KMX = 2: a K step holds two 128-K MFMA steps, so a weight row's
+  // step is a whole 128-byte line (a CU keeps a fixed number of copy
+  // requests in flight, so full lines copy faster); the A rows (256 bytes)
+  // sit in two 128-byte planes, one per MFMA step, with two scale words
+  // per row
+  constexpr int KSQ = (F == F_MX) ? KMX : 1;  // MFMA steps per K step (FP8 / MX)
+  constexpr int APL = KSQ;                    // A planes
+  constexpr int BROW = T::BROW * KSQ;         // B bytes per row and step
+  constexpr int KSTEP = T::KSTEP * KSQ;
+  constexpr int CPRB = BROW / 16;             // 16-byte chunks per B row and step
+  constexpr int ASZ = APL * BM * 128;
+  constexpr int BSZ = BNW * BROW;
   constexpr int WN = NW / 2;           // waves: 2 along M x WN along N
   constexpr int NT = 64 * NW;          // threads
   constexpr int FM = BM / 32;
   constexpr int FN = BNW / WN / 16;
-  constexpr int LA = BM * 8 / NT;      // A copy instructions per wave per step
+  constexpr int LA = APL * BM * 8 / NT;  // A copy instructions per wave per step
   constexpr int LB = BNW * CPRB / NT;  // B copy instructions per wave per step
   static_assert(LA >= 1 && LB >= 1 && (!G1 || FN % 2 == 0), "tile too small for the wave count");
-  // scales (FP8, MX): one 4-byte word per tile row (A: the row's scale(s) of
-  // the step, B: the weight row's) copied with the data; every wave issues
-  // the same number of copies, the slots past BM + BNW are never read
-  constexpr int LSC = (F == F_BF16) ? 0 : (BM + BNW + NT - 1) / NT;
+  // scales (FP8, MX): one 4-byte word per tile row and MFMA step (A: the
+  // row's scale(s), B: the weight row's) copied with the data, MFMA step w
+  // in scale plane w; every wave issues the same number of copies, the slots
+  // past BM + BNW are never read
+  constexpr int LSC1 = (F == F_BF16) ? 0 : (BM + BNW + NT - 1) / NT;  // copies per plane
+  constexpr int LSC = LSC1 * KSQ;
+  constexpr int SCPL = LSC1 * NT * 4;  // bytes per scale plane
   constexpr int LS = LA + LB + LSC;
-  constexpr int SCSZ = LSC * NT * 4;
+  constexpr int SCSZ = SCPL * KSQ;
   constexpr int SSZ = ASZ + BSZ + SCSZ;
   constexpr int D = NS - 1;            // steps in flight ahead of the multiply
   static_assert(LS * (D > 1 ? D - 1 : 1) <= 63, "vmcnt range");
+  static_assert(NS * SSZ <= 163840, "the ring must fit in LDS");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -301,7 +323,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
   const int nblk = *p.npp / BM;
   const int64_t n_valid = (int64_t)nblk * ntn;
   const int64_t per = (n_valid + 7) >> 3;
-  const int nk = K / T::KSTEP;
+  const int nk = K / KSTEP;
   const int rowbytes_a = K * T::AB;
   const int rowbytes_b = (F == F_MX) ? K / 2 : K * T::AB;
   const uint8_t* asrc = G1 ? p.x : p.act;
@@ -344,31 +366,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 
     // per-lane source offsets of the copy instructions (the K step is added
     // as a uniform offset)
+    // copy i: A plane i % APL, rows wave * BM / NW + 8 (i / APL) ..
     uint32_t ag[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int row = wave * (BM / NW) + 8 * i + (lane >> 3);
+      const int row = wave * (BM / NW) + 8 * (i / APL) + (lane >> 3);
       bool v;
       const int src = a_row_index<G1>(p, blk, BM, row, v);  // padding rows read token 0; never used
-      ag[i] = (uint32_t)src * rowbytes_a + 16 * swz<8>(lane & 7, row);
+      ag[i] = (uint32_t)src * rowbytes_a + 128 * (i % APL) + 16 * swz<8>(lane & 7, row);
     }
     const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes_b, (uint64_t)erows * rowbytes_b);
     uint32_t bg[LB];
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       const int row = (wave * LB + i) * (64 / CPRB) + lane / CPRB;
-      bg[i] = (uint32_t)weight_row(nt, row) * rowbytes_b + 16 * swz<CPRB>(lane % CPRB, row);
+      bg[i] = (uint32_t)weight_row(nt, row) * rowbytes_b + 16 * bswz<CPRB>(lane % CPRB, row);
     }
-    // scale words: slot q = (i * NW + wave) * 64 + lane of copy i; q < BM: A
-    // row q, q < BM + BNW: B row q - BM.  Per step the source advances by
-    // sc_step bytes.
+    // scale words: copy i fills plane i / LSC1, slot q = ((i % LSC1) * NW +
+    // wave) * 64 + lane; q < BM: A row q, q < BM + BNW: B row q - BM.  Per
+    // step the source advances by sc_step bytes.
     const uint8_t* scg[LSC > 0 ? LSC : 1];
     int sc_step[LSC > 0 ? LSC : 1];
     if (F != F_BF16) {
       const int kblocks = K / 128;  // FP8: one fp32 scale per 128 K; MX: 4 e8m0 per 128 K
 #pragma unroll
       for (int i = 0; i < LSC; ++i) {
-        const int q = (i * NW + wave) * 64 + lane;
+        const int q = ((i % LSC1) * NW + wave) * 64 + lane;
+        const int pl = i / LSC1;
         if (q < BM) {
           bool v;
           const int src = a_row_index<G1>(p, blk, BM, q, v);
@@ -376,8 +400,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
             scg[i] = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s) + ((size_t)src * kblocks) * 4;
             sc_step[i] = 4;
           } else {
-            scg[i] = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s) + (size_t)src * (K / 32);
-            sc_step[i] = 4;
+            scg[i] = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s) + (size_t)src * (K / 32) + 4 * pl;
+            sc_step[i] = 4 * KSQ;
           }
         } else {
           const int lrow = q < BM + BNW ? q - BM : 0;
@@ -387,8 +411,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
                      (((size_t)e * (erows / 128) + wr / 128) * kblocks) * 4;
             sc_step[i] = 4;
           } else {
-            scg[i] = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s) + ((size_t)e * erows + wr) * (K / 32);
-            sc_step[i] = 4;
+            scg[i] = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s) + ((size_t)e * erows + wr) * (K / 32) + 4 * pl;
+            sc_step[i] = 4 * KSQ;
           }
         }
       }
@@ -397,11 +421,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
     auto issue = [&](int s, int slot) {
       uint8_t* st = lds + slot * SSZ;
 #pragma unroll
-      for (int i = 0; i < LA; ++i) buf2lds16(ra, ag[i], s * 128, st + (wave * (BM / NW) + 8 * i) * 128);
+      for (int i = 0; i < LA; ++i)
+        buf2lds16(ra, ag[i], s * 128 * APL, st + (i % APL) * BM * 128 + (wave * (BM / NW) + 8 * (i / APL)) * 128);
 #pragma unroll
-      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * T::BROW, st + ASZ + (wave * LB + i) * (64 / CPRB) * T::BROW);
+      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * BROW, st + ASZ + (wave * LB + i) * (64 / CPRB) * BROW);
 #pragma unroll
-      for (int i = 0; i < LSC; ++i) g2lds4(scg[i] + (size_t)s * sc_step[i], st + ASZ + BSZ + (i * NW + wave) * 256);
+      for (int i = 0; i < LSC; ++i)
+        g2lds4(scg[i] + (size_t)s * sc_step[i], st + ASZ + BSZ + (i / LSC1) * SCPL + ((i % LSC1) * NW + wave) * 256);
     };
 
     f32x4_t acc[FM][FN];
@@ -411,7 +437,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
       for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // Operand fragments of one MFMA sub-step, read from a ring slot.  BF16
-    // has two 32-wide sub-steps per 64-element step; FP8 / MX one per step.
+    // has two 32-wide sub-steps per 64-element step, MX two 128-wide ones per
+    // 256-element step, FP8 one.
     struct Frag {
       typename SOp<F>::A af[FM];
       typename SOp<F>::B bfr[FN];
@@ -421,9 +448,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
       int sb[FN];        // MX: weight e8m0
     };
     auto rd = [&](int s, int ks, Frag& f) {
-      const uint8_t* As = lds + (s % NS) * SSZ;
-      const uint8_t* Bs = As + ASZ;
-      const uint8_t* Ss = Bs + BSZ;
+      const uint8_t* Bs = lds + (s % NS) * SSZ + ASZ;
+      const uint8_t* As = lds + (s % NS) * SSZ + (F == F_MX ? ks * BM * 128 : 0);
+      const uint8_t* Ss = Bs + BSZ + (F == F_MX ? ks * SCPL : 0);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
         const int rr = wm * (BM / 2) + fm * 16 + r;
@@ -453,7 +480,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
           f.bfr[fn] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           f.wsc[fn] = reinterpret_cast<const float*>(Ss)[BM + frag_lrow(fn)];
         } else {
-          f.bfr[fn] = *reinterpret_cast<const i32x4_t*>(Bs + rr * 64 + 16 * swz<4>(g, rr));
+          f.bfr[fn] = *reinterpret_cast<const i32x4_t*>(Bs + rr * BROW + 16 * bswz<CPRB>(ks * 4 + g, rr));
           f.sb[fn] = (int)Ss[(BM + rr) * 4 + g];
         }
       }
@@ -516,13 +543,16 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
       mm(f0);
       mm(f1);
     } else {
-      // one sub-step per step; a second fragment buffer does not fit the
-      // register file next to the accumulators at BLOCK_M 128
+      // one fragment buffer; a second does not fit the register file next
+      // to the accumulators at BLOCK_M 128
       for (int s = 0; s < nk; ++s) {
-        Frag f0;
         next_step(s);
-        rd(s, 0, f0);
-        mm(f0);
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+          Frag f0;
+          rd(s, ks, f0);
+          mm(f0);
+        }
       }
     }
     wait_vm<0>();     // the copies past the last step have landed too
@@ -1259,15 +1289,17 @@ void launch_stream_one(const GemmP& p, int64_t max_blocks, int N, hipStream_t s)
   gemm_stream<F, G1, FN><<<tile_grid(max_blocks * (N / BNO), wgs), 64 * kStreamWaves, lds, s>>>(p);
 }
 
-template <int F, bool G1, int BM, int BNW, int NS, int NW = 4>
+template <int F, bool G1, int BM, int BNW, int NS, int NW = 4, int KMX = 1>
 moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   using T = Tr<F>;
-  const size_t sc = (F == F_BF16) ? 0 : (size_t)((BM + BNW + 64 * NW - 1) / (64 * NW)) * 64 * NW * 4;
-  const size_t lds = (size_t)NS * ((size_t)BM * 128 + (size_t)BNW * T::BROW + sc);
+  constexpr int KSQ = (F == F_MX) ? KMX : 1;  // as in gemm_tiled
+  const size_t sc = (F == F_BF16) ? 0 : (size_t)KSQ * ((BM + BNW + 64 * NW - 1) / (64 * NW)) * 64 * NW * 4;
+  const size_t lds = (size_t)NS * ((size_t)KSQ * BM * 128 + (size_t)BNW * T::BROW * KSQ + sc);
   // the workgroups resident at once (each loops over tiles)
   static int cache[64] = {0};
-  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_tiled<F, G1, BM, BNW, NS, NW>), 64 * NW, lds, cache);
-  gemm_tiled<F, G1, BM, BNW, NS, NW><<<tile_grid(max_tiles, wgs), 64 * NW, lds, s>>>(p);
+  const int wgs =
+      resident_wgs(reinterpret_cast<const void*>(&gemm_tiled<F, G1, BM, BNW, NS, NW, KMX>), 64 * NW, lds, cache);
+  gemm_tiled<F, G1, BM, BNW, NS, NW, KMX><<<tile_grid(max_tiles, wgs), 64 * NW, lds, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -1334,18 +1366,24 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   // or slower for MX)
   constexpr int NW = (F == F_MX) ? 4 : MOE_TILED_WAVES;
   switch (a.block_m) {
-    case 32: return which == 1 ? launch_tiled_one<F, true, 32, 256, 3>(p, t1, s) : launch_tiled_one<F, false, 32, 128, 3>(p, t2, s);
+    case 32:  // MX: 256-wide K steps (measured: faster here; at 64 and 128 rows slower, one workgroup per CU)
+      return which == 1 ? launch_tiled_one<F, true, 32, 256, 3, 4, 2>(p, t1, s)
+                        : launch_tiled_one<F, false, 32, 128, 3, 4, 2>(p, t2, s);
     case 64:
       if (which == 1) return launch_tiled_one<F, true, 64, 256, (F == F_BF16 ? 4 : 3), NW>(p, t1, s);
-      if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
+      if constexpr (F == F_BF16)
+        if (a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
       return launch_tiled_one<F, false, 64, 128, 3, NW>(p, t2, s);
     case 128:
-      if (F == F_BF16 && a.pairs) {
-        if (which == 1) return launch_pair_one<true>(p, t1, s);
-        if (a.H % 256 == 0) return launch_pair_one<false>(p, t2 / 2, s);
+      if constexpr (F == F_BF16) {
+        if (a.pairs) {
+          if (which == 1) return launch_pair_one<true>(p, t1, s);
+          if (a.H % 256 == 0) return launch_pair_one<false>(p, t2 / 2, s);
+        }
       }
       if (which == 1) return launch_tiled_one<F, true, 128, 256, 3, NW>(p, t1, s);
-      if (F == F_BF16 && a.H % 256 == 0) return launch_tiled_one<F, false, 128, 256, 3, NW>(p, t2 / 2, s);
+      if constexpr (F == F_BF16)
+        if (a.H % 256 == 0) return launch_tiled_one<F, false, 128, 256, 3, NW>(p, t2 / 2, s);
       return launch_tiled_one<F, false, 128, 128, 3, NW>(p, t2, s);
   }
   return MOE_E_INVAL;
