@@ -30,8 +30,8 @@
 //    token tile to finish (a second agent-scope counter) then runs the
 //    one-workgroup block alignment over all T*k assignments.
 //  * large T (prefill, T > 256, where a second launch is cheap next to the
-//    layer): a tiled logits kernel (64 tokens x 64 experts per workgroup,
-//    each gate value split once per 64 tokens into LDS planes) writes fp32
+//    layer): a tiled logits kernel (128 tokens x 64 experts per workgroup,
+//    each gate value split once per 128 tokens into LDS planes) writes fp32
 //    logits, then a row-parallel kernel runs the same selection, one wave per
 //    token.
 
@@ -458,13 +458,16 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
 }
 
 // ---------------------------------------------------------------------------
-// Prefill layout, first kernel: the group sum G_j of a 64-token x 64-expert
+// Prefill layout, first kernel: the group sum G_j of a 128-token x 64-expert
 // tile for one K group j (4 chunks of 128), written to part[j][t][e].
-// 4 waves as 2 x 2, each 32 tokens x 32 experts (2 x 2 fragments).  Per
+// 4 waves as 2 x 2, each 64 tokens x 32 experts (4 x 2 fragments).  Per
 // 32-wide K step the 256 threads split the tile's 64 x 32 gate values once
-// into LDS planes (each gate value is split once per 64 tokens); the gate
-// and x values of the next PF steps are in flight meanwhile.
-constexpr int LT = 64;  // tokens per tile
+// into LDS planes (each gate value is split once per 128 tokens: the split
+// and its two barriers per step cost more than the step's multiplies at
+// 64 tokens); the gate and x values of the next PF steps are in flight
+// meanwhile.
+constexpr int TFR = 4;             // token fragments per wave
+constexpr int LT = 2 * 16 * TFR;   // tokens per tile
 constexpr int LE = 64;  // experts per tile
 constexpr int PF = 4;   // steps loaded ahead
 
@@ -491,18 +494,18 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
   const bool sv1 = e0 + se + 32 < p.E;
   const float* g0p = p.gate + (size_t)min(e0 + se, p.E - 1) * p.H + k0 + sk;
   const float* g1p = p.gate + (size_t)min(e0 + se + 32, p.E - 1) * p.H + k0 + sk;
-  const uint16_t* xr[2];
-  bool tv[2];
+  const uint16_t* xr[TFR];
+  bool tv[TFR];
 #pragma unroll
-  for (int tf = 0; tf < 2; ++tf) {
-    const int t = t0 + wm * 32 + tf * 16 + r;
+  for (int tf = 0; tf < TFR; ++tf) {
+    const int t = t0 + wm * (LT / 2) + tf * 16 + r;
     tv[tf] = t < p.T;
     xr[tf] = p.x + (size_t)(tv[tf] ? t : 0) * p.H + k0 + q * 8;
   }
 
-  f32x4_t part[2][2], grp[2][2];
+  f32x4_t part[TFR][2], grp[TFR][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < TFR; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       part[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -511,13 +514,13 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
 
   // register ring of PF steps (past the last step: the last step again)
   float4 rg0[PF], rg1[PF];
-  bf16x8_t rx[PF][2];
+  bf16x8_t rx[PF][TFR];
   auto load = [&](int st, int slot) {
     const int kb = min(st, nsteps - 1) * 32;
     rg0[slot] = *reinterpret_cast<const float4*>(g0p + kb);
     rg1[slot] = *reinterpret_cast<const float4*>(g1p + kb);
 #pragma unroll
-    for (int tf = 0; tf < 2; ++tf) rx[slot][tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
+    for (int tf = 0; tf < TFR; ++tf) rx[slot][tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
   };
 #pragma unroll
   for (int u = 0; u < PF; ++u) load(u, u);
@@ -529,9 +532,9 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
       if (st >= nsteps) break;
       const float4 g0 = sv0 ? rg0[u] : make_float4(0.f, 0.f, 0.f, 0.f);
       const float4 g1 = sv1 ? rg1[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-      bf16x8_t a[2];
+      bf16x8_t a[TFR];
 #pragma unroll
-      for (int tf = 0; tf < 2; ++tf) a[tf] = tv[tf] ? rx[u][tf] : bf16x8_t{};
+      for (int tf = 0; tf < TFR; ++tf) a[tf] = tv[tf] ? rx[u][tf] : bf16x8_t{};
       load(st + PF, u);
       __syncthreads();  // the previous step's planes are consumed
       {
@@ -555,12 +558,12 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
         const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(pr + 32);
         const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pr + 64);
 #pragma unroll
-        for (int tf = 0; tf < 2; ++tf) part[tf][ef] = mfma3(a[tf], bh, bm, bl, part[tf][ef]);
+        for (int tf = 0; tf < TFR; ++tf) part[tf][ef] = mfma3(a[tf], bh, bm, bl, part[tf][ef]);
       }
       if ((st & 3) == 3 || st == nsteps - 1) {  // end of a chunk: G_j += P_c (P_c from zero)
         const bool first = st < 4;
 #pragma unroll
-        for (int tf = 0; tf < 2; ++tf)
+        for (int tf = 0; tf < TFR; ++tf)
 #pragma unroll
           for (int ef = 0; ef < 2; ++ef) {
             grp[tf][ef] = first ? part[tf][ef] : grp[tf][ef] + part[tf][ef];
@@ -570,12 +573,12 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
     }
   }
 #pragma unroll
-  for (int tf = 0; tf < 2; ++tf)
+  for (int tf = 0; tf < TFR; ++tf)
 #pragma unroll
     for (int ef = 0; ef < 2; ++ef)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const int t = t0 + wm * 32 + tf * 16 + 4 * q + ii;
+        const int t = t0 + wm * (LT / 2) + tf * 16 + 4 * q + ii;
         const int e = e0 + wn * 32 + ef * 16 + r;
         if (t < p.T && e < p.E) p.part[((size_t)j * p.T + t) * p.E + e] = grp[tf][ef][ii];
       }
