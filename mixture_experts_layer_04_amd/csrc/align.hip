@@ -32,7 +32,10 @@ namespace {
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void align_kernel(AlignParams p) {
   extern __shared__ int smem[];
-  align_block<NW>(p, smem);
+  if (p.A <= 64)
+    align_tiny<NW>(p);
+  else
+    align_block<NW>(p, smem);
 }
 
 // ---------------------------------------------------------------------------

@@ -109,6 +109,95 @@ __device__ __forceinline__ bool count_segment(const int32_t* ids, int* hist, int
   return bad;
 }
 
+// Alignment of at most 64 assignments (decode) in one workgroup of NW waves.
+// Wave 0 holds one assignment per lane: lanes with equal ids find each
+// other with one ballot per id bit, so each lane knows its expert's count
+// and its rank among them (lower assignment index first); the lowest lane
+// of an expert counts the other experts' lanes with lower ids, which places
+// the expert in the sorted list of distinct experts, and sums their padded
+// counts, which is its first slot.  The list (first slot, count, id) goes
+// to LDS; then every slot is written exactly once: an assignment by its
+// lane, any other slot below the padded length by the thread that finds it
+// in the list (padding of an expert) or past it (sentinel), so no store
+// has to wait for another.  Same outputs as align_block.
+template <int NW>
+__device__ __forceinline__ void align_tiny(const AlignParams& p) {
+  __shared__ int l_start[65];  // first slot of the d-th distinct expert; [D] = padded length
+  __shared__ int l_count[64];
+  __shared__ int l_id[64];
+  __shared__ int l_d;          // D, the number of distinct experts
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int NT = NW * 64;
+  const int A = p.A;
+  const int E = p.E;
+  if (tid < 64) {
+    const int id0 = lane < A ? p.ids[lane] : -1;
+    const bool valid = id0 >= 0 && id0 < E;
+    if (__ballot(lane < A && !valid && id0 != -1) != 0ull && lane == 0) atomicOr(p.err, 1);
+    const int id = valid ? id0 : 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < p.nbits; ++b) {
+      const bool bit = (id >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(m & lt);
+    const int cnt = __popcll(m);
+    const bool lead = valid && rank == 0;
+    const int padded = (cnt + p.bm - 1) / p.bm * p.bm;
+    // distinct experts with lower ids than this lane's and their padded counts
+    int before = 0, start = 0;
+    const uint64_t leaders = __ballot(lead);
+    for (uint64_t rest = leaders; rest != 0ull; rest &= rest - 1ull) {
+      const int j = __ffsll((unsigned long long)rest) - 1;
+      const int idj = __shfl(id, j, 64);
+      const int pj = __shfl(padded, j, 64);
+      if (idj < id) {
+        before += 1;
+        start += pj;
+      }
+    }
+    int total = lead ? padded : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off, 64);
+    if (lead) {
+      l_start[before] = start;
+      l_count[before] = cnt;
+      l_id[before] = id;
+    }
+    if (lane == 0) {
+      l_d = __popcll(leaders);
+      l_start[__popcll(leaders)] = total;
+      p.num_post_padded[0] = total;
+    }
+    // every lane of an expert computed its first slot (start); plus the rank
+    if (valid) p.sorted_ids[start + rank] = lane;
+  }
+  __syncthreads();
+  const int D = l_d;
+  const int total = l_start[D];
+  // the distinct expert whose padded range holds slot i (i < total)
+  auto owner = [&](int i) {
+    int lo = 0, hi = D;  // last d with l_start[d] <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (l_start[mid] <= i) lo = mid; else hi = mid;
+    }
+    return lo;
+  };
+  for (int i = tid; i < p.max_padded; i += NT) {
+    if (i < total) {
+      const int d = owner(i);
+      if (i - l_start[d] < l_count[d]) continue;  // an assignment's slot
+    }
+    p.sorted_ids[i] = A;
+  }
+  const int nb = total / p.bm;
+  for (int b = tid; b < p.max_blocks; b += NT) p.block_expert[b] = b < nb ? l_id[owner(b * p.bm)] : -1;
+}
+
 // The whole alignment in one workgroup of NW waves (threadIdx.x < NW * 64);
 // smem holds (NW * E + E + 1) ints.  Every slot first gets the sentinel
 // (coalesced stores); the placement overwrites the assignment slots after a

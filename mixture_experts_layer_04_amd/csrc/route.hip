@@ -354,7 +354,8 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
 // ---------------------------------------------------------------------------
 // Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token
 // tiles.  FUSE: the last token tile also aligns (dynamic LDS of
-// (5 E + 1) ints); with a single token tile, from the ids it keeps in LDS.
+// (5 E + 1) ints, E counting the shared expert); with a single token tile,
+// from the ids it keeps in LDS (one wave for at most 64 assignments).
 template <int SLOTS, bool FUSE>
 __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap) {
   const int wave = threadIdx.x >> 6;
@@ -438,7 +439,10 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
       __syncthreads();
       AlignParams lp = ap;
       lp.ids = s_ids;
-      align_block<4>(lp, smem);
+      if (lp.A <= 64)
+        align_tiny<4>(lp);
+      else
+        align_block<4>(lp, smem);
       return;
     }
     wait_wave_stores();  // every wave stored ids of this tile
@@ -607,8 +611,8 @@ moe_status launch_slots(const RouteParams& p, const AlignParams* ap, hipStream_t
     route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
   } else {
     dim3 grid(p.NF * p.NG, ceil_div(p.T, 16));
-    if (ap)
-      route_small<SLOTS, true><<<grid, 256, (5 * (size_t)p.E + 1) * sizeof(int), stream>>>(p, *ap);
+    if (ap)  // align_block's LDS: (4 waves + 1) x the alignment's experts (E + n_shared) + 1
+      route_small<SLOTS, true><<<grid, 256, (5 * (size_t)ap->E + 1) * sizeof(int), stream>>>(p, *ap);
     else
       route_small<SLOTS, false><<<grid, 256, 0, stream>>>(p, AlignParams{});
   }

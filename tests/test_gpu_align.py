@@ -39,6 +39,9 @@ CASES = [
     (2048, 8, 256, 64, "skewed"), (37, 3, 1024, 32, "uniform"), (333, 8, 600, 16, "skewed"),
     (100, 4, 16, 16, "hot"), (5000, 2, 8, 128, "uniform"), (16, 2, 8, 16, "uniform"),
     (1, 1, 1, 16, "uniform"), (77, 6, 256, 1, "uniform"),
+    # the one-wave path (at most 64 assignments) and just past it
+    (8, 8, 128, 16, "uniform"), (8, 8, 64, 16, "hot"), (64, 1, 1024, 32, "uniform"), (7, 2, 16, 1, "skewed"),
+    (32, 2, 8, 128, "hot"), (13, 5, 1024, 16, "uniform"), (65, 1, 4, 16, "uniform"),
     # around the switch to the multi-workgroup path (12288 assignments)
     (12287, 1, 64, 16, "uniform"), (6144, 2, 64, 16, "skewed"), (1536, 8, 1024, 16, "uniform"),
     (65536, 8, 256, 128, "uniform"), (13000, 1, 1, 64, "uniform"),
