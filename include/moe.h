@@ -42,7 +42,8 @@
  *    not a multiple of its scale block) returns MOE_E_UNSUPPORTED.  A launch
  *    failure reported by the HIP runtime returns MOE_E_HIP.  T = 0 is a valid
  *    no-op that returns MOE_OK.
- *  - The library is stateless and re-entrant.
+ *  - The library is re-entrant and keeps no state between calls apart from
+ *    per-device occupancy figures it queries once (thread-safe).
  */
 #ifndef MOE_H
 #define MOE_H

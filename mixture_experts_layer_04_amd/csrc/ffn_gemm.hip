@@ -51,6 +51,7 @@
 // tiles, so a block's A rows are read from HBM once and the weight tiles of
 // an expert are reused by its following blocks.
 
+#include <atomic>
 #include <cmath>
 
 #include "common.h"
@@ -1264,18 +1265,21 @@ int stream_fn(int T, int k, int E, int N, bool g1) {
 
 // Workgroups of `kernel` that fit on the current device at once (CUs x
 // occupancy), as a multiple of 8.  `cache` (one per kernel, indexed by
-// device) keeps the answer.
-int resident_wgs(const void* kernel, int threads, size_t lds, int* cache) {
+// device) keeps the answer; concurrent first calls compute the same value,
+// so relaxed atomics suffice.
+int resident_wgs(const void* kernel, int threads, size_t lds, std::atomic<int>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu <= 0)
       per_cu = 1;
-    cache[dev] = (cus * per_cu + 7) / 8 * 8;
+    v = (cus * per_cu + 7) / 8 * 8;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 template <int F, bool G1, int FN>
@@ -1284,7 +1288,7 @@ void launch_stream_one(const GemmP& p, int64_t max_blocks, int N, hipStream_t s)
   const size_t lds = (size_t)kStreamWaves * 16 * (FN * 16 + 1) * sizeof(float);
   // every workgroup resident at once: a workgroup that finds no tile exits
   // at once instead of holding a slot that a tile could use
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_stream<F, G1, FN>), 64 * kStreamWaves, lds, cache);
   gemm_stream<F, G1, FN><<<tile_grid(max_blocks * (N / BNO), wgs), 64 * kStreamWaves, lds, s>>>(p);
 }
@@ -1296,7 +1300,7 @@ moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   const size_t sc = (F == F_BF16) ? 0 : (size_t)KSQ * ((BM + BNW + 64 * NW - 1) / (64 * NW)) * 64 * NW * 4;
   const size_t lds = (size_t)NS * ((size_t)KSQ * BM * 128 + (size_t)BNW * T::BROW * KSQ + sc);
   // the workgroups resident at once (each loops over tiles)
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   const int wgs =
       resident_wgs(reinterpret_cast<const void*>(&gemm_tiled<F, G1, BM, BNW, NS, NW, KMX>), 64 * NW, lds, cache);
   gemm_tiled<F, G1, BM, BNW, NS, NW, KMX><<<tile_grid(max_tiles, wgs), 64 * NW, lds, s>>>(p);
@@ -1311,7 +1315,7 @@ template <bool G1>
 moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   // one workgroup per CU (the ring is all of LDS), each looping over tiles
   constexpr int NW = MOE_PAIR_WAVES;
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64];
   const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_bf16<G1, NW>), 64 * NW, 5 * 32768, cache);
   gemm_pair_bf16<G1, NW><<<tile_grid(max_tiles, wgs), 64 * NW, 5 * 32768, s>>>(p);
   MOE_CHECK_LAUNCH();
