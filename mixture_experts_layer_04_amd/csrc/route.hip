@@ -410,7 +410,11 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
       for (int w = 1; w < nc; ++w) gsum += red[w][tl][el];
       const int t = t0 + tl;
       const int e = f * 16 + el;
-      if (t < p.T && e < p.E) p.part[((size_t)j * p.T + t) * p.E + e] = gsum;
+      // written through to memory (system scope): the election's release
+      // then has fewer dirty L2 lines to write back (measured: the router
+      // alone 0.3-1 us faster)
+      if (t < p.T && e < p.E)
+        __hip_atomic_store(p.part + ((size_t)j * p.T + t) * p.E + e, gsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
   __syncthreads();  // only wave 0 (thread 0's wave) stored group sums
