@@ -679,32 +679,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 }
 
 // ---------------------------------------------------------------------------
-// Paired tiled kernel (bf16, BLOCK_M = 128, prefill).  A tile is up to two
-// consecutive blocks of one expert (256 rows) x 256 weight rows: each weight
-// byte copied to LDS feeds twice the rows of a 128 x 256 tile, and the copy
-// stream (the limit of the 128-row kernel) carries 1.5x fewer bytes per flop
-// for an expert of two blocks.  Blocks pair up from the start of each
-// expert's run (pair_table_kernel); an expert with an odd number of blocks
-// ends in a single-block tile, whose missing half is neither copied (an
-// empty buffer range returns zeros without touching memory) nor multiplied.
-// 4 waves as 2 x 2, one per SIMD, each 128 rows x 128 weight rows (GEMM1: 64
-// gate rows and the matching 64 up rows); K steps of 64 bytes per row (one
-// 32-wide MFMA step) in a 5-stage ring of 32 KiB stages (all of LDS), four
-// steps ahead of the multiply.
-constexpr int kPairBlock = 128;
+// Paired tiled kernel (bf16, BLOCK_M = 64 or 128, prefill).  A tile is up to
+// two consecutive blocks of one expert (2 BLOCK_M rows) x 256 weight rows:
+// each weight byte copied to LDS feeds twice the rows of a BLOCK_M x 256
+// tile, and the copy stream (what limits the tiled kernels: a CU keeps a
+// fixed number of line requests in flight) carries fewer bytes per flop.
+// Blocks pair up from the start of each expert's run (pair_table_kernel); an
+// expert with an odd number of blocks ends in a single-block tile, whose
+// missing half is neither copied (an empty buffer range returns zeros
+// without touching memory) nor multiplied.  8 waves as 2 x 4, two per SIMD,
+// each one block's rows x 64 weight rows (GEMM1: 32 gate rows and the
+// matching 32 up rows), one fragment set; K steps of 128 bytes per row (two
+// 32-wide MFMA steps) with separate LDS rings for A (two slots, one step
+// ahead) and B (three slots, two steps ahead).
 
 // Pair table: tab[0] = number of pairs, tab[1 + j] = first block of pair j
 // with bit 30 set when the pair holds two blocks.  One workgroup walks the
 // blocks 1024 at a time: an inclusive max-scan of the run starts gives each
 // block the first block of its expert's run, a sum-scan numbers the blocks
 // that start a pair (an even distance from that first block).
-__global__ __launch_bounds__(1024) void pair_table_kernel(const int32_t* be, const int32_t* npp, int32_t* tab) {
+__global__ __launch_bounds__(1024) void pair_table_kernel(const int32_t* be, const int32_t* npp, int bm,
+                                                          int32_t* tab) {
   __shared__ int s_max[16];
   __shared__ int s_cnt[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int nblk = *npp / kPairBlock;
+  const int nblk = *npp / bm;
   int carry_first = 0;  // first block of the run that reaches the chunk's start
   int carry_pairs = 0;
   for (int c0 = 0; c0 < nblk; c0 += 1024) {
@@ -745,9 +746,8 @@ __global__ __launch_bounds__(1024) void pair_table_kernel(const int32_t* be, con
   if (tid == 0) tab[0] = carry_pairs;
 }
 
-template <bool G1, int NW>
+template <bool G1, int NW, int BB>  // BB: rows per block (64 or 128)
 __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
-  constexpr int BB = kPairBlock;  // rows per block
   constexpr int BMT = 2 * BB;     // rows per tile
   constexpr int BNW = 256;        // weight rows per tile
   constexpr int NT = 64 * NW;
@@ -764,9 +764,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
   constexpr int BSZ = BNW * RB;
   constexpr int NA = 2, NB = 3;
   constexpr int DA = NA - 1, DB = NB - 1;  // steps each ring runs ahead
-  constexpr int FM = 8;             // 16-row fragments per wave (128 rows)
+  constexpr int FM = BB / 16;        // 16-row fragments per wave (one block's rows)
   constexpr int FN = BNW / WN / 16;  // 16-column fragments per wave
-  constexpr int RW = BMT / NW;       // tile rows each wave copies
+  constexpr int RW = BMT / NW;       // A rows each wave copies
+  constexpr int RWB = BNW / NW;      // weight rows each wave copies
   constexpr int LA = BMT * CPR / NT;  // copy instructions per wave per step (1 KiB each)
   constexpr int LB = BNW * CPR / NT;
   constexpr int LS = LA + LB;
@@ -776,7 +777,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave / WN;  // rows [128 wm, +128)
+  const int wm = wave / WN;  // rows [BB wm, +BB): the tile's first or second block
   const int wn = wave % WN;
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
     const int blk = pe & 0x3FFFFFFF;  // first block of the tile
     const bool two = (pe >> 30) & 1;
     const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
-    const bool mine = wm == 0 || two;  // this wave's 128 rows exist
+    const bool mine = wm == 0 || two;  // this wave's block exists
 
     // wave w copies tile rows [RW w, RW w + RW): rows of the second block
     // come from an empty range when the tile holds one block
@@ -857,7 +858,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
       int row, c;
-      copy_src(wave * RW + (64 / CPR) * i, lane, row, c);
+      copy_src(wave * RWB + (64 / CPR) * i, lane, row, c);
       bg[i] = (uint32_t)weight_row(nt, row) * rowbytes + 16 * c;
     }
     // copies of step s (clamped to the last step: past the end a step is
@@ -873,7 +874,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
       uint8_t* st = lds + NA * ASZ + (s % NB) * BSZ;
       s = s < nk ? s : nk - 1;
 #pragma unroll
-      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * RB, st + (wave * RW + (64 / CPR) * i) * RB);
+      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * RB, st + (wave * RWB + (64 / CPR) * i) * RB);
     };
 
     f32x4_t acc[FM][FN];
@@ -891,7 +892,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
       const uint8_t* Bs = lds + NA * ASZ + (s % NB) * BSZ;
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) {
-        const int rr = wm * 128 + fm * 16 + r;
+        const int rr = wm * BB + fm * 16 + r;
         f.a[fm] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(rr, 4 * ks + g));
       }
 #pragma unroll
@@ -946,7 +947,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int fa = 0; fa < FN / 2; ++fa)
-            st[(wm * 128 + fm * 16 + 4 * g + i) * BNA + wn * (BNA / WN) + fa * 16 + r] =
+            st[(wm * BB + fm * 16 + 4 * g + i) * BNA + wn * (BNA / WN) + fa * 16 + r] =
                 (uint16_t)f32_to_bf16_bits(swiglu(acc[fm][fa][i], acc[fm][fa + FN / 2][i], p.lim));
       __syncthreads();
       constexpr int CH = BNA * 2 / 16;  // 16-byte chunks per tile row
@@ -964,7 +965,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn)
-            st[(wm * 128 + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
+            st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
                 (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
       __syncthreads();
       constexpr int CH = BNW * 2 / 16;
@@ -1311,13 +1312,14 @@ moe_status launch_tiled_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
 #ifndef MOE_PAIR_WAVES
 #define MOE_PAIR_WAVES 8
 #endif
-template <bool G1>
+template <bool G1, int BB>
 moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
-  // one workgroup per CU (the ring is all of LDS), each looping over tiles
+  // one workgroup per CU (the rings are all of LDS at BB = 128), each looping over tiles
   constexpr int NW = MOE_PAIR_WAVES;
+  constexpr size_t lds = (size_t)2 * (2 * BB) * 128 + (size_t)3 * 256 * 128;  // A: 2 slots, B: 3 slots
   static std::atomic<int> cache[64];
-  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_bf16<G1, NW>), 64 * NW, 5 * 32768, cache);
-  gemm_pair_bf16<G1, NW><<<tile_grid(max_tiles, wgs), 64 * NW, 5 * 32768, s>>>(p);
+  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_bf16<G1, NW, BB>), 64 * NW, lds, cache);
+  gemm_pair_bf16<G1, NW, BB><<<tile_grid(max_tiles, wgs), 64 * NW, lds, s>>>(p);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }
@@ -1374,6 +1376,12 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
       return which == 1 ? launch_tiled_one<F, true, 32, 256, 3, 4, 2>(p, t1, s)
                         : launch_tiled_one<F, false, 32, 128, 3, 4, 2>(p, t2, s);
     case 64:
+      if constexpr (F == F_BF16) {
+        if (a.pairs) {
+          if (which == 1) return launch_pair_one<true, 64>(p, t1, s);
+          if (a.H % 256 == 0) return launch_pair_one<false, 64>(p, t2 / 2, s);
+        }
+      }
       if (which == 1) return launch_tiled_one<F, true, 64, 256, (F == F_BF16 ? 4 : 3), NW>(p, t1, s);
       if constexpr (F == F_BF16)
         if (a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
@@ -1381,8 +1389,8 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
     case 128:
       if constexpr (F == F_BF16) {
         if (a.pairs) {
-          if (which == 1) return launch_pair_one<true>(p, t1, s);
-          if (a.H % 256 == 0) return launch_pair_one<false>(p, t2 / 2, s);
+          if (which == 1) return launch_pair_one<true, 128>(p, t1, s);
+          if (a.H % 256 == 0) return launch_pair_one<false, 128>(p, t2 / 2, s);
         }
       }
       if (which == 1) return launch_tiled_one<F, true, 128, 256, 3, NW>(p, t1, s);
@@ -1399,11 +1407,11 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
 #define MOE_PAIRED_TILES 1
 #endif
 bool ffn_paired(int wformat, int block_m) {
-  return MOE_PAIRED_TILES && wformat == MOE_W_BF16 && block_m == kPairBlock;
+  return MOE_PAIRED_TILES && wformat == MOE_W_BF16 && (block_m == 128 || block_m == 64);
 }
 
 moe_status launch_pair_table(const FfnArgs& a, hipStream_t s) {
-  pair_table_kernel<<<1, 1024, 0, s>>>(a.block_expert, a.num_post_padded, static_cast<int32_t*>(a.pairs));
+  pair_table_kernel<<<1, 1024, 0, s>>>(a.block_expert, a.num_post_padded, a.block_m, static_cast<int32_t*>(a.pairs));
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -103,14 +103,16 @@ CASES = [("bf16", 256, 256, bm, T) for bm, T in ((16, 5), (16, 300), (32, 300), 
                                                                        (64, 200), (128, 200))]
 
 
-# bf16 at BLOCK_M 128 runs the paired tiles (two blocks of one expert per
-# tile): experts with an even and an odd number of blocks (uniform ids: 375
+# bf16 at BLOCK_M 64 and 128 runs the paired tiles (two blocks of one
+# expert per tile): experts with an even and an odd number of blocks (uniform ids: 375
 # and 500 rows per expert), uneven counts from skewed ids, one expert with
 # one block (the hot expert set leaves the others empty), and a block table
 # longer than one 1024-block chunk of the pair table (checked on a sample).
 PAIRED = [("bf16", 256, 256, 128, 1500, "uniform", None), ("bf16", 512, 384, 128, 2000, "uniform", None),
           ("bf16", 256, 512, 128, 3000, "skewed", None), ("bf16", 256, 256, 128, 100, "hot", None),
-          ("bf16", 256, 128, 128, 70000, "uniform", 300)]
+          ("bf16", 256, 128, 128, 70000, "uniform", 300),
+          # 64-row blocks paired too: an odd count (175 rows per expert) and uneven ones
+          ("bf16", 512, 384, 64, 700, "uniform", None), ("bf16", 256, 256, 64, 1100, "skewed", None)]
 
 
 def _run_exact(fmt, H, F, bm, T, kind="uniform", sample=None):

@@ -118,7 +118,7 @@ def test_layer_swiglu_clamp(name, over, T, bm, limit):
     assert diff > 3 * LAYER_TOL[cfg.wformat]
 
 
-FULL = [("qwen3", 1), ("qwen3", 64), ("qwen3", 4096), ("glm", 1), ("glm", 8), ("glm", 512),
+FULL = [("qwen3", 1), ("qwen3", 64), ("qwen3", 1024), ("qwen3", 4096), ("glm", 1), ("glm", 8), ("glm", 512),
         ("dsv3", 1), ("dsv3", 256), ("dsv3", 2048), ("dsv4", 512), ("dsv4", 8192)]
 
 
