@@ -303,7 +303,7 @@ moe_status moe_layer(const void* x, const float* gate, const float* bias,
 size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared,
                                 int block_m, int wformat);
 /* The block size moe_layer uses for block_m = 0, from the mean rows per
- * expert m = T*k/E: 16 if m < 2, 32 if m <= 32, 64 if m <= 96, else 128. */
+ * expert m = T*k/E: 16 if m < 2, 32 if m <= 24, 64 if m <= 96, else 128. */
 int moe_layer_block_m(int T, int k, int E);
 
 /* ------------------------------------------------------------------------

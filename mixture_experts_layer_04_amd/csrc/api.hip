@@ -72,7 +72,7 @@ int read_grid(size_t bytes) {
 int layer_block_m(int T, int k, int E) {
   const double m = (double)T * k / E;  // rows per expert
   if (m < 2.0) return 16;
-  if (m <= 32.0) return 32;
+  if (m <= 24.0) return 32;
   if (m <= 96.0) return 64;
   return 128;
 }

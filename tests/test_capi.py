@@ -140,3 +140,5 @@ def test_block_m_choice(L):
     assert L.moe_layer_block_m(8, 8, 288) == 16
     assert L.moe_layer_block_m(4096, 8, 128) == 128
     assert L.moe_layer_block_m(2048, 8, 256) == 64
+    assert L.moe_layer_block_m(384, 8, 128) == 32   # m = 24
+    assert L.moe_layer_block_m(448, 8, 128) == 64   # m = 28
