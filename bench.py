@@ -250,7 +250,7 @@ def ep_share_sweep(moe, torch, timer):
         g = torch.Generator(device="cpu").manual_seed(T)
         w = torch.rand((T, cfg.k), generator=g)
         w = (w / w.sum(dim=1, keepdim=True)).to("cuda")
-        bm = moe.layer_block_m(T, cfg.k, cfg.E)
+        bm = moe.layer_block_m(T, cfg.k, cfg.E, cfg.F, cfg.wformat)
         y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
         fmt = 2
         ws = torch.zeros(max(moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, bm, fmt),
@@ -384,7 +384,7 @@ def main():
         del buf
     log(f"bench: {cfg.description}, T={T}")
     W, x = make_problem(cfg, T)
-    bm = moe.layer_block_m(T, cfg.k, cfg.E)
+    bm = moe.layer_block_m(T, cfg.k, cfg.E, cfg.F, cfg.wformat)
     step = Step(moe, torch, cfg, W, x, bm)
 
     for _ in range(args.warmup):

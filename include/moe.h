@@ -285,7 +285,8 @@ moe_status moe_expert_ffn_stages(const void* x, int wformat,
  *                 w2 and their scales then hold E + 1 experts, the shared
  *                 one last, and y adds its output with weight 1.
  *  block_m        0 lets the library choose from the tokens per expert
- *                 (moe_layer_block_m of T, k + n_shared, E + n_shared);
+ *                 (moe_layer_block_m of T, E + n_shared, F, k + n_shared
+ *                 and wformat);
  *                 otherwise 16, 32, 64 or 128.
  *  topk_ids_out, topk_weights_out   optional outputs (NULL allowed),
  *                 [T, k + n_shared].
@@ -303,8 +304,11 @@ moe_status moe_layer(const void* x, const float* gate, const float* bias,
 size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared,
                                 int block_m, int wformat);
 /* The block size moe_layer uses for block_m = 0, from the mean rows per
- * expert m = T*k/E: 16 if m < 2, 32 if m <= 24, 64 if m <= 96, else 128. */
-int moe_layer_block_m(int T, int k, int E);
+ * expert m = T*k/E: 32 if 2 <= m <= 24, 64 if m <= 96, else 128.  Below
+ * m = 2: 16 for MOE_W_FP8_BLOCK128; for bf16 and MXFP4, 32 once the
+ * expected number of 32-row GEMM1 tiles, E (1 - (1 - k/E)^T) * 2F / 256,
+ * reaches 400 (bf16) or 320 (MXFP4), else 16. */
+int moe_layer_block_m(int T, int E, int F, int k, int wformat);
 
 /* ------------------------------------------------------------------------
  * Diagnostics and measurement probes (not part of the layer).

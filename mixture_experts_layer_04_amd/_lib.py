@@ -40,7 +40,7 @@ SIGNATURES = {
     "moe_layer": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f,
                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
-    "moe_layer_block_m": (_i, [_i, _i, _i]),
+    "moe_layer_block_m": (_i, [_i, _i, _i, _i, _i]),
     "moe_debug_error": (_i32, [_vp, _vp]),
     "moe_probe_empty": (_i, [_vp]),
     "moe_probe_read": (_i, [_vp, _sz, _vp, _vp]),

@@ -1,6 +1,8 @@
 // moe_layer (route -> align -> expert FFN on one stream), status strings,
 // the test-only error read-back and the measurement probes.
 
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -64,14 +66,24 @@ int read_grid(size_t bytes) {
 
 }  // namespace
 
-// Block size for T tokens: with fewer than 2 rows per expert on average most
-// blocks hold a single row and the 16-row weight-stream kernel is fastest;
-// from 2 rows on, the tiled kernels' 128-column tiles (activation rows read
-// once per 256 weight rows) win, at the smallest block that the expected
-// rows per expert fill.
-int layer_block_m(int T, int k, int E) {
+// Block size for T tokens.  Below 2 rows per expert on average most blocks
+// hold one or two rows; the 16-row weight-stream kernel spreads the weights
+// of the few experts touched over every CU, while the 32-row tiled kernel
+// needs enough tiles to fill them: one per (expert touched, 256 GEMM1
+// weight rows), with E (1 - (1 - k/E)^T) experts touched.  Measured (cold
+// layers): bf16 turns to the tiled kernel at about 400 such tiles, MX (whose
+// 32-row kernel takes 256-wide K steps) at about 320, and fp8 keeps the
+// stream kernel up to 2 rows per expert.  From 2 rows on, the smallest
+// block that the expected rows per expert fill, with the cuts measured on
+// the tiled kernels.
+int layer_block_m(int T, int k, int E, int F, int wformat) {
   const double m = (double)T * k / E;  // rows per expert
-  if (m < 2.0) return 16;
+  if (m < 2.0) {
+    if (wformat == MOE_W_FP8_BLOCK128) return 16;
+    const double touched = E * (1.0 - std::pow(1.0 - (double)k / E, (double)T));
+    const double tiles = touched * (2.0 * F / 256.0);
+    return tiles >= (wformat == MOE_W_MXFP4 ? 320.0 : 400.0) ? 32 : 16;
+  }
   if (m <= 24.0) return 32;
   if (m <= 96.0) return 64;
   return 128;
@@ -90,15 +102,15 @@ extern "C" const char* moe_status_str(moe_status s) {
   return "unknown moe_status";
 }
 
-extern "C" int moe_layer_block_m(int T, int k, int E) {
-  if (T < 0 || k < 1 || E < 1) return 16;
-  return moe::layer_block_m(T, k, E);
+extern "C" int moe_layer_block_m(int T, int E, int F, int k, int wformat) {
+  if (T < 0 || k < 1 || E < 1 || F < 1) return 16;
+  return moe::layer_block_m(T, k, E, F, wformat);
 }
 
 extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared, int block_m,
                                            int wformat) {
   if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1 || n_shared < 0 || n_shared > 1) return 0;
-  if (block_m == 0) block_m = moe::layer_block_m(T, k + n_shared, E + n_shared);
+  if (block_m == 0) block_m = moe::layer_block_m(T, k + n_shared, E + n_shared, F, wformat);
   return moe::layer_layout(T, H, E, F, k, n_shared, block_m, wformat).total;
 }
 
@@ -111,7 +123,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   using namespace moe;
   if (n_shared != 0 && n_shared != 1) return MOE_E_INVAL;
   const int Ea = E + n_shared, ka = k + n_shared;  // the expert FFN sees the shared expert as expert E
-  if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1) ? layer_block_m(T, ka, Ea) : 16;
+  if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1 && F >= 1) ? layer_block_m(T, ka, Ea, F, wformat) : 16;
   // validate everything before enqueuing anything
   int32_t dummy_i = 0;
   float dummy_f = 0.f;

@@ -56,8 +56,8 @@ def align_max_blocks(T, k, E, block_m):
     return int(lib().moe_align_max_blocks(T, k, E, block_m))
 
 
-def layer_block_m(T, k, E):
-    return int(lib().moe_layer_block_m(T, k, E))
+def layer_block_m(T, k, E, F, wformat="bf16"):
+    return int(lib().moe_layer_block_m(T, E, F, k, WFORMAT[wformat]))
 
 
 def route(x, gate, bias, k, scoring="softmax", n_group=1, topk_group=1, renormalize=True,

@@ -134,11 +134,20 @@ def test_sizing_matches_oracle(L):
 def test_block_m_choice(L):
     # tile height follows the tokens per expert ([Kernels] "The fused expert
     # GEMM", last paragraph): small at decode, large at prefill
-    assert L.moe_layer_block_m(1, 8, 128) == 16
-    assert L.moe_layer_block_m(64, 8, 256) == 32
-    assert L.moe_layer_block_m(63, 8, 256) == 16
-    assert L.moe_layer_block_m(8, 8, 288) == 16
-    assert L.moe_layer_block_m(4096, 8, 128) == 128
-    assert L.moe_layer_block_m(2048, 8, 256) == 64
-    assert L.moe_layer_block_m(384, 8, 128) == 32   # m = 24
-    assert L.moe_layer_block_m(448, 8, 128) == 64   # m = 28
+    bf16, fp8, mx = 0, 1, 2
+    # (T, E, F, k, wformat): from 2 rows per expert on, by rows per expert
+    assert L.moe_layer_block_m(64, 256, 2048, 8, fp8) == 32
+    assert L.moe_layer_block_m(4096, 128, 768, 8, bf16) == 128
+    assert L.moe_layer_block_m(2048, 256, 2048, 8, fp8) == 64
+    assert L.moe_layer_block_m(384, 128, 768, 8, bf16) == 32   # m = 24
+    assert L.moe_layer_block_m(448, 128, 768, 8, bf16) == 64   # m = 28
+    # below 2: fp8 streams; bf16 / MX by the expected 32-row GEMM1 tiles
+    assert L.moe_layer_block_m(63, 256, 2048, 8, fp8) == 16
+    assert L.moe_layer_block_m(1, 128, 768, 8, bf16) == 16     # 8 experts x 6 tiles
+    assert L.moe_layer_block_m(8, 128, 768, 8, bf16) == 16     # ~51 x 6 = 308 tiles
+    assert L.moe_layer_block_m(16, 128, 768, 8, bf16) == 32    # ~81 x 6 = 486 tiles
+    assert L.moe_layer_block_m(8, 288, 2304, 8, bf16) == 32    # ~61 x 18 tiles
+    assert L.moe_layer_block_m(1, 288, 2304, 8, bf16) == 16
+    assert L.moe_layer_block_m(4, 256, 2048, 6, mx) == 32      # ~24 x 16 = 377 tiles
+    assert L.moe_layer_block_m(1, 32, 2048, 6, mx) == 16       # 6 x 16 tiles
+    assert L.moe_layer_block_m(4, 32, 2048, 6, mx) == 16       # ~18 x 16 = 290 tiles
