@@ -48,8 +48,13 @@ constexpr int KCH = 128;          // K chunk
 constexpr int CPG = 4;            // chunks per group
 constexpr int SMALL_T_MAX = 256;  // largest T routed with the decode layout
 constexpr int PROW = 104;         // LDS plane row (bf16): hi[32] mid[32] lo[32] pad[8]
-// the decode layout's election counters: one per 16-token tile
-static_assert(SMALL_T_MAX / 16 <= kMaxCounters, "router counters");
+// the decode layout's token tiles: 4 tokens (one per wave of the selecting
+// workgroup) up to T = 64 while the tiles read at most 24 MiB of gate in
+// all (each tile reads the whole gate), else 16; one election counter per
+// tile
+constexpr int SMALL_T_TILE4 = 64;
+constexpr double TILE4_GATE_BYTES = 24.0 * 1024 * 1024;
+static_assert(SMALL_T_TILE4 / 4 <= kMaxCounters && SMALL_T_MAX / 16 <= kMaxCounters, "router counters");
 
 struct RouteParams {
   const uint16_t* x;
@@ -72,6 +77,7 @@ struct RouteParams {
   void* xs;
   int qfmt;
   int NF, NC, NG;
+  int tt;  // decode layout: tokens per token tile (16 rows of the MFMA tile, the rest padding)
 };
 
 // g = hi + mid + lo exactly, each a bf16 (returned as the upper 16 bits).
@@ -353,7 +359,11 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
 
 // ---------------------------------------------------------------------------
 // Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token
-// tiles.  FUSE: the last token tile also aligns (dynamic LDS of
+// tiles of p.tt tokens: 4 at small T, so that each wave of the elected
+// workgroup selects one token (the selection is single-wave VALU code),
+// else 16 (more tiles multiply the gate reads; measured: 4-token tiles took
+// the Qwen3 router at T=16 from 16.0 to 8.7 us and DSV3's at T=8 from 23.2
+// to 18.7 us, but DSV3's at T=64 from 58 to 94 us).  FUSE: the last token tile also aligns (dynamic LDS of
 // (5 E + 1) ints, E counting the shared expert); with a single token tile,
 // from the ids it keeps in LDS (one wave for at most 64 assignments).
 template <int SLOTS, bool FUSE>
@@ -365,7 +375,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
   const int f = blockIdx.x % p.NF;
   const int j = blockIdx.x / p.NF;
   const int ttile = blockIdx.y;
-  const int t0 = ttile * 16;
+  const int t0 = ttile * p.tt;
   const int c = j * CPG + wave;
   __shared__ float red[CPG][16][17];
   __shared__ int s_last;
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
     const int e = min(f * 16 + r, p.E - 1);
     const float* grow = p.gate + (size_t)e * p.H + c * KCH + q * 8;
     const int t = t0 + r;
-    const bool tv = t < p.T;
+    const bool tv = r < p.tt && t < p.T;
     const uint16_t* xrow = p.x + (size_t)(tv ? t : 0) * p.H + c * KCH + q * 8;
     float4 g0[4], g1[4];
     bf16x8_t a[4];
@@ -413,7 +423,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
       // written through to memory (system scope): the election's release
       // then has fewer dirty L2 lines to write back (measured: the router
       // alone 0.3-1 us faster)
-      if (t < p.T && e < p.E)
+      if (tl < p.tt && t < p.T && e < p.E)
         __hip_atomic_store(p.part + ((size_t)j * p.T + t) * p.E + e, gsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every wave sees all group sums
-  for (int tl = wave; tl < 16; tl += 4) {
+  for (int tl = wave; tl < p.tt; tl += 4) {
     const int t = t0 + tl;
     if (t >= p.T) break;
     float bv[SLOTS];
@@ -614,7 +624,7 @@ moe_status launch_slots(const RouteParams& p, const AlignParams* ap, hipStream_t
     MOE_CHECK_LAUNCH();
     route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
   } else {
-    dim3 grid(p.NF * p.NG, ceil_div(p.T, 16));
+    dim3 grid(p.NF * p.NG, ceil_div(p.T, p.tt));
     if (ap)  // align_block's LDS: (4 waves + 1) x the alignment's experts (E + n_shared) + 1
       route_small<SLOTS, true><<<grid, 256, (5 * (size_t)ap->E + 1) * sizeof(int), stream>>>(p, *ap);
     else
@@ -662,6 +672,7 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.ids = ids;
   p.weights = weights;
   p.T = T; p.H = H; p.E = E; p.k = k;
+  p.tt = (T <= SMALL_T_TILE4 && (double)ceil_div(T, 4) * E * H * sizeof(float) <= TILE4_GATE_BYTES) ? 4 : 16;
   p.n_shared = n_shared; p.ks = k + n_shared;
   p.n_group = n_group; p.topk_group = topk_group;
   p.scoring = scoring; p.renorm = renormalize != 0;
