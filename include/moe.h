@@ -180,9 +180,11 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
  * then aligned with block_m.  With n_shared = 0 the outputs equal those of
  * moe_route followed by moe_align on the same stream, bit for bit.  For
  * T <= 256 the router's workgroups compute the gate product and each token
- * tile's last one selects its tokens; the last token tile to finish then
- * aligns all assignments in the same launch.  For T > 256 the router's two
- * launches run, then moe_align's.
+ * tile's last one selects its tokens (tiles of 4 tokens, or 16 where 4-token
+ * tiles would read more than 24 MiB of gate in all); when all tokens form
+ * one tile that workgroup also aligns them in the same launch, otherwise
+ * moe_align's launch follows.  For T > 256 the
+ * router's two launches run, then moe_align's.
  *  n_shared       0, or 1 for a shared expert as an always-selected slot
  *                 ([MoE] SGLang's fused shared expert: appended as expert
  *                 id E, top-k becomes top-(k+1); [MegaMoE] §3.8: its output

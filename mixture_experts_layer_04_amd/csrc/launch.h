@@ -14,13 +14,11 @@ namespace moe {
 // (zero after each call):
 //   [0, 4)            sticky alignment error bits
 //   [4, 8)            alignment counter (multi-workgroup path)
-//   [8, 12)           fused route + align counter (token tiles done)
 //   [16, 52)          grouped GEMM tile queues: one per XCD, then the
 //                     count of workgroups done
 //   [256, kCtrlBytes) one counter per router token tile
 constexpr size_t kCtrlBytes = 65536;
 constexpr size_t kAlignCounterOffset = 4;
-constexpr size_t kFusedCounterOffset = 8;
 constexpr size_t kTileQueueOffset = 16;
 constexpr size_t kCounterOffset = 256;
 constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);

@@ -63,7 +63,6 @@ struct RouteParams {
   float* part;        // decode layout: group sums [NG][T][E]
   float* logits_out;  // optional [T][E]
   unsigned* counters;
-  unsigned* fused_counter;  // route + align: token tiles done
   int32_t* ids;
   float* weights;
   int T, H, E, k, n_group, topk_group, scoring, renorm;
@@ -363,9 +362,10 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
 // workgroup selects one token (the selection is single-wave VALU code),
 // else 16 (more tiles multiply the gate reads; measured: 4-token tiles took
 // the Qwen3 router at T=16 from 16.0 to 8.7 us and DSV3's at T=8 from 23.2
-// to 18.7 us, but DSV3's at T=64 from 58 to 94 us).  FUSE: the last token tile also aligns (dynamic LDS of
-// (5 E + 1) ints, E counting the shared expert); with a single token tile,
-// from the ids it keeps in LDS (one wave for at most 64 assignments).
+// to 18.7 us, but DSV3's at T=64 from 58 to 94 us).  FUSE (one token tile
+// only): the selecting workgroup also aligns, from the ids it keeps in LDS
+// (one wave for at most 64 assignments, else dynamic LDS of (5 E + 1) ints,
+// E counting the shared expert).
 template <int SLOTS, bool FUSE>
 __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap) {
   const int wave = threadIdx.x >> 6;
@@ -449,29 +449,15 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
   }
   if constexpr (FUSE) {
     extern __shared__ int smem[];
-    if (gridDim.y == 1) {  // this workgroup selected every token
-      __syncthreads();
-      AlignParams lp = ap;
-      lp.ids = s_ids;
-      if (lp.A <= 64)
-        align_tiny<4>(lp);
-      else
-        align_block<4>(lp, smem);
-      return;
-    }
-    wait_wave_stores();  // every wave stored ids of this tile
+    // one token tile (the host fuses only then): this workgroup selected
+    // every token and aligns from the ids it keeps in LDS
     __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned prev =
-          __hip_atomic_fetch_add(p.fused_counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = prev == (unsigned)(gridDim.y - 1);
-      if (last) __hip_atomic_store(p.fused_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every tile's ids are visible
-    align_block<4>(ap, smem);
+    AlignParams lp = ap;
+    lp.ids = s_ids;
+    if (lp.A <= 64)
+      align_tiny<4>(lp);
+    else
+      align_block<4>(lp, smem);
   }
 }
 
@@ -655,6 +641,11 @@ moe_status route_validate(const void* x, const float* gate, int T, int H, int E,
 }
 
 namespace {
+// tokens per token tile of the decode layout (route_small)
+int decode_tile_tokens(int T, int E, int H) {
+  return (T <= SMALL_T_TILE4 && (double)ceil_div(T, 4) * E * H * sizeof(float) <= TILE4_GATE_BYTES) ? 4 : 16;
+}
+
 moe_status route_launch(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int n_shared, int32_t* ids, float* weights, float* logits_out, void* ws,
@@ -668,11 +659,10 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.part = reinterpret_cast<float*>(base + kCtrlBytes);
   p.logits_out = logits_out;
   p.counters = reinterpret_cast<unsigned*>(base + kCounterOffset);
-  p.fused_counter = reinterpret_cast<unsigned*>(base + kFusedCounterOffset);
   p.ids = ids;
   p.weights = weights;
   p.T = T; p.H = H; p.E = E; p.k = k;
-  p.tt = (T <= SMALL_T_TILE4 && (double)ceil_div(T, 4) * E * H * sizeof(float) <= TILE4_GATE_BYTES) ? 4 : 16;
+  p.tt = decode_tile_tokens(T, E, H);
   p.n_shared = n_shared; p.ks = k + n_shared;
   p.n_group = n_group; p.topk_group = topk_group;
   p.scoring = scoring; p.renorm = renormalize != 0;
@@ -721,10 +711,20 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
   // the alignment sees the shared expert as expert E and slot k
   const int Ea = E + n_shared, ka = k + n_shared;
   if (T == 0) return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
-  if (!use_large(T, E)) {
+  if (!use_large(T, E) && T <= decode_tile_tokens(T, E, H)) {
+    // one token tile: its selecting workgroup aligns in the same launch
     const AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
     return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                         n_shared, ids, weights, nullptr, ws, &ap, stream, xq, xs, qfmt);
+  }
+  if (!use_large(T, E)) {
+    // several token tiles: a launch of its own aligns (measured: faster than
+    // a second election among the tiles and an alignment by the last one's
+    // four waves, Qwen3 T=16 route + align 15.5 against about 13 us)
+    moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                                 routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream, xq, xs, qfmt);
+    if (st != MOE_OK) return st;
+    return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
   }
   moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
                                routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream);
