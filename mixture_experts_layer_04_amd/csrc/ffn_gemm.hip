@@ -1373,8 +1373,13 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   constexpr int NW = (F == F_MX) ? 4 : MOE_TILED_WAVES;
   switch (a.block_m) {
     case 32:  // MX: 256-wide K steps (measured: faster here; at 64 and 128 rows slower, one workgroup per CU)
-      return which == 1 ? launch_tiled_one<F, true, 32, 256, 3, 4, 2>(p, t1, s)
-                        : launch_tiled_one<F, false, 32, 128, 3, 4, 2>(p, t2, s);
+      if (which == 1) return launch_tiled_one<F, true, 32, 256, 3, 4, 2>(p, t1, s);
+      // MX GEMM2: 256 output columns once that still leaves >= 2048 tiles
+      // (measured: DSV4 T=512 layer 770 -> 753 us; with fewer tiles, as for
+      // bf16 GLM T=8, the CUs go short: 509 -> 529 us)
+      if constexpr (F == F_MX)
+        if (a.H % 256 == 0 && t2 / 2 >= 2048) return launch_tiled_one<F, false, 32, 256, 3, 4, 2>(p, t2 / 2, s);
+      return launch_tiled_one<F, false, 32, 128, 3, 4, 2>(p, t2, s);
     case 64:
       if constexpr (F == F_BF16) {
         if (a.pairs) {
