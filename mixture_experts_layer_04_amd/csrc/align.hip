@@ -49,6 +49,7 @@ struct Align2Params {
   unsigned* counter;  // control-block word, zero between calls
   int32_t* cnt;       // [E][G] counts, then first slots
   int32_t* start;     // [E + 1] scanned padded sizes
+  int32_t* pairs;     // optional pair table (write_pair_table), written by the last counting workgroup
   int A, E, bm, nbits, C, G, max_padded, max_blocks;
 };
 
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(NW * 64) void align_count_kernel(Align2Params p) {
   __syncthreads();
   for (int e = tid; e <= E; e += NT) p.start[e] = st[e];
   if (tid == 0) p.num_post_padded[0] = st[E];
+  if (p.pairs) write_pair_table(st, E, p.bm, p.pairs, M + EG);
   // first slot of each (expert, workgroup): exclusive scan over g, a
   // thread per expert
   for (int e = tid; e < E; e += NT) {
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(NW * 64) void align_place_kernel(Align2Params p) {
 
 int align_waves(int E) { return E <= 512 ? 16 : 8; }
 
-size_t align_lds_bytes(int E) { return ((size_t)align_waves(E) * E + E + 1) * sizeof(int); }
+// one workgroup: per-wave counts, first rows, and the pair table's scan
+size_t align_lds_bytes(int E) { return ((size_t)align_waves(E) * E + 2 * ((size_t)E + 1)) * sizeof(int); }
 
 // The multi-workgroup path: T*k of at least kAlignMultiMin assignments,
 // chunks of at least 2048 (a multiple of 512) and at most
@@ -236,12 +239,17 @@ AlignParams align_params(const int32_t* ids, int T, int k, int E, int block_m, i
   p.nbits = nbits;
   p.max_padded = (int)align_max_padded(T, k, E, block_m);
   p.max_blocks = (int)align_max_blocks(T, k, E, block_m);
+  p.pairs = nullptr;
   return p;
 }
 
 moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream) {
-  const AlignParams p = align_params(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws);
+                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
+                        int32_t* pairs, bool* pairs_written) {
+  AlignParams p = align_params(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws);
+  // the one-wave path (at most 64 assignments) leaves a pair table to its user
+  if (pairs_written) *pairs_written = pairs != nullptr && p.A > 64;
+  if (p.A > 64) p.pairs = pairs;
   const int nbits = p.nbits;
   if (align_multi(p.A)) {
     const AlignSplit sp = align_split(p.A, E);
@@ -254,10 +262,11 @@ moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, in
     q.counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + kAlignCounterOffset);
     q.cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kCtrlBytes);
     q.start = q.cnt + (size_t)sp.G * E;
+    q.pairs = p.pairs;
     q.A = p.A; q.E = E; q.bm = block_m; q.nbits = nbits; q.C = sp.C; q.G = sp.G;
     q.max_padded = p.max_padded; q.max_blocks = p.max_blocks;
     constexpr int NW = kAlignMultiWaves;
-    align_count_kernel<NW><<<sp.G, NW * 64, ((size_t)E * sp.G + 2 * (size_t)E + 1) * sizeof(int), stream>>>(q);
+    align_count_kernel<NW><<<sp.G, NW * 64, ((size_t)E * sp.G + 3 * (size_t)E + 2) * sizeof(int), stream>>>(q);
     MOE_CHECK_LAUNCH();
     align_place_kernel<NW><<<sp.G, NW * 64, ((size_t)NW * E + (size_t)E + 1) * sizeof(int), stream>>>(q);
     MOE_CHECK_LAUNCH();

@@ -28,11 +28,50 @@ struct AlignParams {
   int32_t* err;
   int A, E, bm, nbits;
   int max_padded, max_blocks;
+  int32_t* pairs;  // optional: the paired GEMM tiles' pair table (write_pair_table); null: none
 };
 
 // AlignParams of one call (the error word at the start of the workspace).
 AlignParams align_params(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
                          int32_t* block_expert, int32_t* num_post_padded, void* ws);
+
+// Pair table of the paired tiled GEMMs from the scanned first rows
+// start[0..E] (LDS, start[E] = padded length): tab[0] = number of pairs,
+// tab[1 + j] = first block of pair j with bit 30 set when the pair holds two
+// blocks; an expert's blocks pair up from the first block of its run, in
+// expert order (the layout pair_table_kernel writes from the block table).
+// Wave 0 scans the pair counts into pb[0..E] (LDS scratch); every thread
+// then writes the pairs of its experts.  Ends with a barrier.
+__device__ __forceinline__ void write_pair_table(const int* start, int E, int bm, int32_t* tab, int* pb) {
+  const int tid = threadIdx.x, lane = tid & 63, NT = blockDim.x;
+  if (tid < 64) {
+    const int per = (E + 63) / 64;
+    const int lo = min(E, lane * per);
+    const int hi = min(E, lo + per);
+    int run = 0;
+    for (int e = lo; e < hi; ++e) run += ((start[e + 1] - start[e]) / bm + 1) / 2;
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    int excl = incl - run;
+    for (int e = lo; e < hi; ++e) {
+      pb[e] = excl;
+      excl += ((start[e + 1] - start[e]) / bm + 1) / 2;
+    }
+    if (lane == 63) pb[E] = incl;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    const int nb = (start[e + 1] - start[e]) / bm;
+    const int b0 = start[e] / bm;
+    for (int j = 0; 2 * j < nb; ++j) tab[1 + pb[e] + j] = (b0 + 2 * j) | (2 * j + 1 < nb ? (1 << 30) : 0);
+  }
+  if (tid == 0) tab[0] = pb[E];
+  __syncthreads();
+}
 
 // expert owning padded row `row`: upper_bound of row in start[0..E], minus one
 __device__ __forceinline__ int expert_of_row(const int* start, int E, int row) {
@@ -199,7 +238,7 @@ __device__ __forceinline__ void align_tiny(const AlignParams& p) {
 }
 
 // The whole alignment in one workgroup of NW waves (threadIdx.x < NW * 64);
-// smem holds (NW * E + E + 1) ints.  Every slot first gets the sentinel
+// smem holds (NW * E + E + 1) ints, E + 1 more with a pair table.  Every slot first gets the sentinel
 // (coalesced stores); the placement overwrites the assignment slots after a
 // wait for those stores and a barrier.
 template <int NW>
@@ -260,6 +299,7 @@ __device__ __forceinline__ void align_block(const AlignParams& p, int* smem) {
 
   const int total = start[E];
   if (tid == 0) p.num_post_padded[0] = total;
+  if (p.pairs) write_pair_table(start, E, p.bm, p.pairs, start + E + 1);
   // first slot of each (wave, expert)
   for (int e = tid; e < E; e += NT) {
     int run = start[e];

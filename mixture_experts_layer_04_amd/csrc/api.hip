@@ -158,9 +158,14 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   // launch fewer)
   const int qfmt = wformat == MOE_W_FP8_BLOCK128 ? 1 : wformat == MOE_W_MXFP4 ? 2 : 0;
   a.x_ready = qfmt != 0 && route_quantizes_x(T, E);
+  // the alignment also writes the paired tiles' pair table where it can
+  // (one launch fewer); the FFN builds it otherwise
+  bool pairs_written = false;
   st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
-                          n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream, a.xq, a.xs, qfmt);
+                          n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream, a.xq, a.xs, qfmt,
+                          static_cast<int32_t*>(a.pairs), &pairs_written);
   if (st != MOE_OK) return st;
+  a.pairs_ready = pairs_written;
   return launch_ffn(a, stream);
 }
 

@@ -146,7 +146,7 @@ moe_status launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
   moe_status st = MOE_OK;
   if ((a.stages & MOE_STAGE_QUANT) && a.wformat != MOE_W_BF16 && !a.x_ready) st = launch_quant_x(a, s);
-  if (st == MOE_OK && a.pairs && (a.stages & MOE_STAGE_QUANT)) st = launch_pair_table(a, s);
+  if (st == MOE_OK && a.pairs && !a.pairs_ready && (a.stages & MOE_STAGE_QUANT)) st = launch_pair_table(a, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM1)) st = launch_gemm(a, 1, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_GEMM2)) st = launch_gemm(a, 2, s);
   if (st == MOE_OK && (a.stages & MOE_STAGE_COMBINE)) st = launch_finalize(a, s);
@@ -179,6 +179,7 @@ extern "C" moe_status moe_expert_ffn_stages(const void* x, int wformat, const vo
   a.swiglu_limit = swiglu_limit;
   a.stages = stages;
   a.x_ready = false;
+  a.pairs_ready = false;
   a.y = y;
   a.ctrl = workspace;
   ffn_carve(a, workspace);

@@ -41,7 +41,8 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
-                              void* xq, void* xs, int qfmt);
+                              void* xq, void* xs, int qfmt, int32_t* pairs = nullptr,
+                              bool* pairs_written = nullptr);
 bool route_quantizes_x(int T, int E);
 size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared);
 
@@ -50,8 +51,11 @@ moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, 
 size_t align_workspace_size(int T, int k, int E);
 int64_t align_max_padded(int T, int k, int E, int block_m);
 int64_t align_max_blocks(int T, int k, int E, int block_m);
+// pairs (optional): also write the paired GEMM tiles' pair table there
+// (*pairs_written says whether it did: not for at most 64 assignments)
 moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream);
+                        int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
+                        int32_t* pairs = nullptr, bool* pairs_written = nullptr);
 
 // Everything moe_expert_ffn needs, with the workspace already carved.
 struct FfnArgs {
@@ -70,6 +74,7 @@ struct FfnArgs {
   float swiglu_limit;  // +inf: no clamp
   int stages;      // bit mask of MOE_STAGE_* to run
   bool x_ready;    // xq / xs already hold the quantised x (the router wrote them)
+  bool pairs_ready;  // the pair table was written by the alignment (launch_align's pairs)
   void* y;
   // workspace regions
   void* xq;        // quantised x (fp8 formats)
