@@ -70,6 +70,13 @@ __device__ __forceinline__ float dpp_f32(float v) {
 __device__ __forceinline__ float readlane_f32(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
+// every lane gets the max of its 16-lane row (the DPP steps of wave_max_u)
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  return fmaxf(v, dpp_f32<0x140>(v));
+}
 __device__ __forceinline__ float wave_max_u(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
   v = fmaxf(v, dpp_f32<0x4E>(v));

@@ -169,24 +169,44 @@ __device__ __forceinline__ void select_token(const RouteParams& p, int t, const 
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) grp[s] = ok[s] ? (s * kWave + lane) / gsize : -1;
     float my_gs = NEG_INF;
-    for (int g = 0; g < p.n_group; ++g) {
-      float v = NEG_INF;
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s)
-        if (grp[s] == g) v = fmaxf(v, key[s]);
-      const float t1 = wave_max_u(v);
-      int drop = -1;  // lowest expert of the group holding t1
+    if (gsize == 32 && p.E == SLOTS * kWave) {
+      // every group is one half of one slot (DeepSeek-V3: 8 x 32): all
+      // groups at once, half-wave maxima of each slot; the same maxima, the
+      // same lowest-id drop and the same sums as the loop below
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
-        const uint64_t b = __ballot(grp[s] == g && key[s] == t1);
-        if (drop < 0 && b != 0) drop = s * kWave + __ffsll((unsigned long long)b) - 1;
+        const float r1 = row_max16(key[s]);
+        const float lo1 = fmaxf(readlane_f32(r1, 0), readlane_f32(r1, 16));
+        const float hi1 = fmaxf(readlane_f32(r1, 32), readlane_f32(r1, 48));
+        const uint64_t b = __ballot(key[s] == (lane < 32 ? lo1 : hi1));
+        const int dlo = __ffsll((unsigned long long)(b & 0xFFFFFFFFull)) - 1;
+        const int dhi = __ffsll((unsigned long long)(b >> 32)) + 31;
+        const float r2 = row_max16(lane == (lane < 32 ? dlo : dhi) ? NEG_INF : key[s]);
+        const float lo2 = fmaxf(readlane_f32(r2, 0), readlane_f32(r2, 16));
+        const float hi2 = fmaxf(readlane_f32(r2, 32), readlane_f32(r2, 48));
+        if (lane == 2 * s) my_gs = lo1 + lo2;
+        if (lane == 2 * s + 1) my_gs = hi1 + hi2;
       }
-      float v2 = NEG_INF;
+    } else {
+      for (int g = 0; g < p.n_group; ++g) {
+        float v = NEG_INF;
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s)
-        if (grp[s] == g && s * kWave + lane != drop) v2 = fmaxf(v2, key[s]);
-      const float t2 = wave_max_u(v2);
-      if (lane == g) my_gs = t1 + t2;
+        for (int s = 0; s < SLOTS; ++s)
+          if (grp[s] == g) v = fmaxf(v, key[s]);
+        const float t1 = wave_max_u(v);
+        int drop = -1;  // lowest expert of the group holding t1
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s) {
+          const uint64_t b = __ballot(grp[s] == g && key[s] == t1);
+          if (drop < 0 && b != 0) drop = s * kWave + __ffsll((unsigned long long)b) - 1;
+        }
+        float v2 = NEG_INF;
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+          if (grp[s] == g && s * kWave + lane != drop) v2 = fmaxf(v2, key[s]);
+        const float t2 = wave_max_u(v2);
+        if (lane == g) my_gs = t1 + t2;
+      }
     }
     // keep the topk_group best groups, lowest group id on ties
     uint64_t kept = 0;
