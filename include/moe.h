@@ -171,7 +171,7 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
 
 /* ------------------------------------------------------------------------
  * moe_route_align - moe_route followed by moe_align in one call, one
- * launch while T <= 256 ([Router] §6 and §6.1: one routing stage that
+ * launch while T <= 4 ([Router] §6 and §6.1: one routing stage that
  * scores, selects, counts and sorts; [Router] §8.1: the gate product stays
  * expert-parallel, the selection row-parallel).
  *
@@ -179,12 +179,13 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
  * layouts, ownership and results: topk_ids / topk_weights are written and
  * then aligned with block_m.  With n_shared = 0 the outputs equal those of
  * moe_route followed by moe_align on the same stream, bit for bit.  For
- * T <= 256 the router's workgroups compute the gate product and each token
- * tile's last one selects its tokens (tiles of 4 tokens, or 16 where 4-token
- * tiles would read more than 24 MiB of gate in all); when all tokens form
- * one tile that workgroup also aligns them in the same launch, otherwise
- * moe_align's launch follows.  For T > 256 the
- * router's two launches run, then moe_align's.
+ * T <= 4, and for T <= 64 while ceil(T / 4) * E * H * 4 bytes (the gate
+ * read once per 4-token tile) stay within 24 MiB, the router's workgroups
+ * compute the gate product and each 4-token tile's last one selects its
+ * tokens, one per wave; at T <= 4 that workgroup also aligns them in the
+ * same launch, otherwise moe_align's launch follows.  Elsewhere the
+ * router's two launches run (logits, then one wave per token), then
+ * moe_align's.
  *  n_shared       0, or 1 for a shared expert as an always-selected slot
  *                 ([MoE] SGLang's fused shared expert: appended as expert
  *                 id E, top-k becomes top-(k+1); [MegaMoE] §3.8: its output

@@ -157,7 +157,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   // at decode the router quantises x for the fp8 formats on the way (one
   // launch fewer)
   const int qfmt = wformat == MOE_W_FP8_BLOCK128 ? 1 : wformat == MOE_W_MXFP4 ? 2 : 0;
-  a.x_ready = qfmt != 0 && route_quantizes_x(T, E);
+  a.x_ready = qfmt != 0 && route_quantizes_x(T, E, H);
   // the alignment also writes the paired tiles' pair table where it can
   // (one launch fewer); the FFN builds it otherwise
   bool pairs_written = false;

@@ -30,7 +30,7 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream);
 
-// Route + align in one call: one launch while T <= 256 (the router's decode
+// Route + align in one call: one launch while T <= 4 (the router's decode
 // layout, whose last token tile aligns every assignment), else the router's
 // two launches and launch_align.
 // n_shared = 1: slot k of every token is the shared expert (id E, weight 1),
@@ -43,7 +43,7 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
                               void* xq, void* xs, int qfmt, int32_t* pairs = nullptr,
                               bool* pairs_written = nullptr);
-bool route_quantizes_x(int T, int E);
+bool route_quantizes_x(int T, int E, int H);
 size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared);
 
 moe_status align_validate(const int32_t* ids, int T, int k, int E, int block_m, const void* sorted_ids,

@@ -29,8 +29,8 @@
 //    With the alignment fused in (route + align in one launch), the last
 //    token tile to finish (a second agent-scope counter) then runs the
 //    one-workgroup block alignment over all T*k assignments.
-//  * large T (prefill, T > 256, where a second launch is cheap next to the
-//    layer): a tiled logits kernel (128 tokens x 64 experts per workgroup,
+//  * larger T or a larger gate (use_large: where the decode layout would
+//    need more than one token per selecting wave): a tiled logits kernel (128 tokens x 64 experts per workgroup,
 //    each gate value split once per 128 tokens into LDS planes) writes fp32
 //    logits, then a row-parallel kernel runs the same selection, one wave per
 //    token.
@@ -46,15 +46,18 @@ namespace {
 
 constexpr int KCH = 128;          // K chunk
 constexpr int CPG = 4;            // chunks per group
-constexpr int SMALL_T_MAX = 256;  // largest T routed with the decode layout
 constexpr int PROW = 104;         // LDS plane row (bf16): hi[32] mid[32] lo[32] pad[8]
-// the decode layout's token tiles: 4 tokens (one per wave of the selecting
-// workgroup) up to T = 64 while the tiles read at most 24 MiB of gate in
-// all (each tile reads the whole gate), else 16; one election counter per
-// tile
+// The decode layout takes tiles of 4 tokens (one per wave of the selecting
+// workgroup; each tile reads the whole gate) and serves T <= 4, and T <= 64
+// while those tiles read at most 24 MiB of gate in all; one election
+// counter per tile.  Measured (cold, router alone): where it needs more
+// tokens per wave (16-token tiles) the two-launch prefill layout is faster:
+// DSV3 T=256 128 -> 24 us, DSV4 T=256 74 -> 21 us, GLM T=256 83 -> 21 us,
+// Qwen3 T=256 26.5 -> 19.7 us, while with 4-token tiles the decode layout
+// wins (Qwen3 T=64 16.1 against 18.6, DSV3 T=8 19.4 against about 23).
 constexpr int SMALL_T_TILE4 = 64;
 constexpr double TILE4_GATE_BYTES = 24.0 * 1024 * 1024;
-static_assert(SMALL_T_TILE4 / 4 <= kMaxCounters && SMALL_T_MAX / 16 <= kMaxCounters, "router counters");
+static_assert(SMALL_T_TILE4 / 4 <= kMaxCounters, "router counters");
 
 struct RouteParams {
   const uint16_t* x;
@@ -378,11 +381,10 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
 
 // ---------------------------------------------------------------------------
 // Decode layout.  grid.x = NF * NG (expert fragment, group), grid.y = token
-// tiles of p.tt tokens: 4 at small T, so that each wave of the elected
-// workgroup selects one token (the selection is single-wave VALU code),
-// else 16 (more tiles multiply the gate reads; measured: 4-token tiles took
-// the Qwen3 router at T=16 from 16.0 to 8.7 us and DSV3's at T=8 from 23.2
-// to 18.7 us, but DSV3's at T=64 from 58 to 94 us).  FUSE (one token tile
+// tiles of p.tt = 4 tokens, so that each wave of the elected workgroup
+// selects one token (the selection is single-wave VALU code; measured:
+// 4-token against 16-token tiles took the Qwen3 router at T=16 from 16.0 to
+// 8.7 us and DSV3's at T=8 from 23.2 to 18.7 us).  FUSE (one token tile
 // only): the selecting workgroup also aligns, from the ids it keeps in LDS
 // (one wave for at most 64 assignments, else dynamic LDS of (5 E + 1) ints,
 // E counting the shared expert).
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
   const int c = j * CPG + wave;
   __shared__ float red[CPG][16][17];
   __shared__ int s_last;
-  __shared__ int s_ids[FUSE ? 16 * 17 : 1];  // FUSE: the tile's ids [16][k + n_shared]
+  __shared__ int s_ids[FUSE ? 16 * 17 : 1];  // FUSE: the tile's ids [tokens][k + n_shared]
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (c < p.NC) {
@@ -623,12 +625,14 @@ __global__ __launch_bounds__(256) void route_select(RouteParams p) {
   select_token<SLOTS>(p, t, l, bv);
 }
 
-bool use_large(int T, int E) { (void)E; return T > SMALL_T_MAX; }
+bool use_large(int T, int E, int H) {
+  return !(T <= 4 || (T <= SMALL_T_TILE4 && (double)ceil_div(T, 4) * E * H * sizeof(float) <= TILE4_GATE_BYTES));
+}
 
 // ap: the alignment to fuse into the decode layout, or nullptr
 template <int SLOTS>
 moe_status launch_slots(const RouteParams& p, const AlignParams* ap, hipStream_t stream) {
-  if (use_large(p.T, p.E)) {
+  if (use_large(p.T, p.E, p.H)) {
     route_logits_group<<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE), p.NG), 256, 0, stream>>>(p);
     MOE_CHECK_LAUNCH();
     route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
@@ -664,10 +668,6 @@ moe_status route_validate(const void* x, const float* gate, int T, int H, int E,
 }
 
 namespace {
-// tokens per token tile of the decode layout (route_small)
-int decode_tile_tokens(int T, int E, int H) {
-  return (T <= SMALL_T_TILE4 && (double)ceil_div(T, 4) * E * H * sizeof(float) <= TILE4_GATE_BYTES) ? 4 : 16;
-}
 
 moe_status route_launch(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
@@ -685,7 +685,7 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.ids = ids;
   p.weights = weights;
   p.T = T; p.H = H; p.E = E; p.k = k;
-  p.tt = decode_tile_tokens(T, E, H);
+  p.tt = 4;
   p.n_shared = n_shared; p.ks = k + n_shared;
   p.n_group = n_group; p.topk_group = topk_group;
   p.scoring = scoring; p.renorm = renormalize != 0;
@@ -693,7 +693,7 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.xq = nullptr;
   p.xs = nullptr;
   p.qfmt = 0;
-  if (!use_large(T, E) && qfmt != 0) {
+  if (!use_large(T, E, H) && qfmt != 0) {
     p.xq = static_cast<uint8_t*>(xq);
     p.xs = xs;
     p.qfmt = qfmt;
@@ -724,7 +724,7 @@ size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
   return r > a ? r : a;
 }
 
-bool route_quantizes_x(int T, int E) { return !use_large(T, E); }
+bool route_quantizes_x(int T, int E, int H) { return !use_large(T, E, H); }
 
 moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
@@ -735,13 +735,13 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
   const int Ea = E + n_shared, ka = k + n_shared;
   if (pairs_written) *pairs_written = false;
   if (T == 0) return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
-  if (!use_large(T, E) && T <= decode_tile_tokens(T, E, H)) {
+  if (!use_large(T, E, H) && T <= 4) {
     // one token tile: its selecting workgroup aligns in the same launch
     const AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
     return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                         n_shared, ids, weights, nullptr, ws, &ap, stream, xq, xs, qfmt);
   }
-  if (!use_large(T, E)) {
+  if (!use_large(T, E, H)) {
     // several token tiles: a launch of its own aligns (measured: faster than
     // a second election among the tiles and an alignment by the last one's
     // four waves, Qwen3 T=16 route + align 15.5 against about 13 us)

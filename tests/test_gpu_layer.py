@@ -139,9 +139,9 @@ MATCH = [("toy", dict(F=256), 200, 32), ("toy", dict(F=256), 300, 128),
 @pytest.mark.parametrize("name,over,T,bm", MATCH)
 def test_expert_ffn_matches_layer(name, over, T, bm):
     """moe_layer gives the bits of moe_align + moe_expert_ffn on its routing.
-    For the fp8 formats at T <= 256 the layer's router quantises x on the way
-    and the FFN skips its quantisation kernel; above that both quantise in
-    the FFN."""
+    For the fp8 formats, where the router takes its one-launch decode layout
+    (small T), it quantises x on the way and the FFN skips its quantisation
+    kernel; elsewhere both quantise in the FFN."""
     import mixture_experts_layer_04_amd as moe
     cfg = get_config(name, **over)
     x, W, y, ids, w, _ = check_layer(cfg, T, bm)

@@ -1,8 +1,8 @@
-"""GPU parity of moe_route_align (one launch for T <= 256): its ids and
+"""GPU parity of moe_route_align (one launch for T <= 4): its ids and
 weights equal moe_route's bit for bit, and its sorted_ids, block table and
 padded length equal moe_align's on those ids and the oracle alignment's,
 over one and several token tiles, group-limited routing, every BLOCK_M and
-the prefill path (T > 256)."""
+the prefill path (larger T)."""
 
 import pytest
 import torch
