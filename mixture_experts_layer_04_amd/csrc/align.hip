@@ -240,13 +240,15 @@ AlignParams align_params(const int32_t* ids, int T, int k, int E, int block_m, i
   p.max_padded = (int)align_max_padded(T, k, E, block_m);
   p.max_blocks = (int)align_max_blocks(T, k, E, block_m);
   p.pairs = nullptr;
+  p.fill_tail = true;
   return p;
 }
 
 moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
-                        int32_t* pairs, bool* pairs_written) {
+                        int32_t* pairs, bool* pairs_written, bool fill_tail) {
   AlignParams p = align_params(ids, T, k, E, block_m, sorted_ids, block_expert, num_post_padded, ws);
+  p.fill_tail = fill_tail;
   // the one-wave path (at most 64 assignments) leaves a pair table to its user
   if (pairs_written) *pairs_written = pairs != nullptr && p.A > 64;
   if (p.A > 64) p.pairs = pairs;

@@ -29,6 +29,10 @@ struct AlignParams {
   int A, E, bm, nbits;
   int max_padded, max_blocks;
   int32_t* pairs;  // optional: the paired GEMM tiles' pair table (write_pair_table); null: none
+  // false (moe_layer, whose kernels read only below the padded length): the
+  // one-wave path leaves the sentinel slots past the padded length and the
+  // block table's -1 tail unwritten
+  bool fill_tail;
 };
 
 // AlignParams of one call (the error word at the start of the workspace).
@@ -226,7 +230,8 @@ __device__ __forceinline__ void align_tiny(const AlignParams& p) {
     }
     return lo;
   };
-  for (int i = tid; i < p.max_padded; i += NT) {
+  const int fill_end = p.fill_tail ? p.max_padded : total;
+  for (int i = tid; i < fill_end; i += NT) {
     if (i < total) {
       const int d = owner(i);
       if (i - l_start[d] < l_count[d]) continue;  // an assignment's slot
@@ -234,7 +239,8 @@ __device__ __forceinline__ void align_tiny(const AlignParams& p) {
     p.sorted_ids[i] = A;
   }
   const int nb = total / p.bm;
-  for (int b = tid; b < p.max_blocks; b += NT) p.block_expert[b] = b < nb ? l_id[owner(b * p.bm)] : -1;
+  const int blk_end = p.fill_tail ? p.max_blocks : nb;
+  for (int b = tid; b < blk_end; b += NT) p.block_expert[b] = b < nb ? l_id[owner(b * p.bm)] : -1;
 }
 
 // The whole alignment in one workgroup of NW waves (threadIdx.x < NW * 64);

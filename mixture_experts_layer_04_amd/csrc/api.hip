@@ -163,7 +163,7 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   bool pairs_written = false;
   st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                           n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream, a.xq, a.xs, qfmt,
-                          static_cast<int32_t*>(a.pairs), &pairs_written);
+                          static_cast<int32_t*>(a.pairs), &pairs_written, /*fill_tail=*/false);
   if (st != MOE_OK) return st;
   a.pairs_ready = pairs_written;
   return launch_ffn(a, stream);

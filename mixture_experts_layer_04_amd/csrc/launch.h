@@ -42,7 +42,7 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
                               void* xq, void* xs, int qfmt, int32_t* pairs = nullptr,
-                              bool* pairs_written = nullptr);
+                              bool* pairs_written = nullptr, bool fill_tail = true);
 bool route_quantizes_x(int T, int E, int H);
 size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared);
 
@@ -55,7 +55,7 @@ int64_t align_max_blocks(int T, int k, int E, int block_m);
 // (*pairs_written says whether it did: not for at most 64 assignments)
 moe_status launch_align(const int32_t* ids, int T, int k, int E, int block_m, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
-                        int32_t* pairs = nullptr, bool* pairs_written = nullptr);
+                        int32_t* pairs = nullptr, bool* pairs_written = nullptr, bool fill_tail = true);
 
 // Everything moe_expert_ffn needs, with the workspace already carved.
 struct FfnArgs {

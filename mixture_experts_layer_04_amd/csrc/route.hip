@@ -730,14 +730,16 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
-                              void* xq, void* xs, int qfmt, int32_t* pairs, bool* pairs_written) {
+                              void* xq, void* xs, int qfmt, int32_t* pairs, bool* pairs_written,
+                              bool fill_tail) {
   // the alignment sees the shared expert as expert E and slot k
   const int Ea = E + n_shared, ka = k + n_shared;
   if (pairs_written) *pairs_written = false;
   if (T == 0) return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream);
   if (!use_large(T, E, H) && T <= 4) {
     // one token tile: its selecting workgroup aligns in the same launch
-    const AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
+    AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
+    ap.fill_tail = fill_tail;
     return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                         n_shared, ids, weights, nullptr, ws, &ap, stream, xq, xs, qfmt);
   }
@@ -749,13 +751,13 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
                                  routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream, xq, xs, qfmt);
     if (st != MOE_OK) return st;
     return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream, pairs,
-                        pairs_written);
+                        pairs_written, fill_tail);
   }
   moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
                                routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream);
   if (st != MOE_OK) return st;
   return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream, pairs,
-                      pairs_written);
+                      pairs_written, fill_tail);
 }
 
 }  // namespace moe
