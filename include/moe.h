@@ -306,6 +306,39 @@ moe_status moe_layer(const void* x, const float* gate, const float* bias,
                      hipStream_t stream);
 size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared,
                                 int block_m, int wformat);
+/* ------------------------------------------------------------------------
+ * moe_layer_noalloc - moe_layer without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, layouts, results and errors are those of moe_layer; the bits of
+ * y (and of the optional routing outputs) equal moe_layer's for the same
+ * arguments.  The workspace is a scratch array of MOE_NOALLOC_SCRATCH_BYTES
+ * (128 MiB) that the library holds on each GPU it runs on, from the first
+ * call on that GPU until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).
+ *  - A call whose moe_layer_workspace_size(T, H, E, F, k, n_shared, block_m,
+ *    wformat) exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_E_WORKSPACE and
+ *    enqueues nothing.  Every decode shape of the five layer configurations
+ *    (T <= 512) fits; the prefill shapes (e.g. 2048 tokens at H 7168) do not.
+ *  - The first call on a GPU looks up that GPU's scratch address (with the
+ *    stream's device made current for the lookup) and clears the scratch's
+ *    control block with one small kernel on `stream` before the layer.
+ *  - Every call on one GPU uses that GPU's one scratch array, which keeps the
+ *    last call's contents: calls that overlap in time on one GPU (two
+ *    streams, two threads) RACE and give undefined results.  Serialise them.
+ * ------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+moe_status moe_layer_noalloc(const void* x, const float* gate, const float* bias,
+                             int wformat, const void* w13, const void* w13_scale,
+                             const void* w2, const void* w2_scale,
+                             int T, int H, int E, int F, int k, int n_shared,
+                             int n_group, int topk_group, int scoring,
+                             int renormalize, float routed_scale, int block_m,
+                             float swiglu_limit,
+                             void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                             hipStream_t stream);
+
 /* The block size moe_layer uses for block_m = 0, from the mean rows per
  * expert m = T*k/E: 32 if 2 <= m <= 24, 64 if m <= 96, else 128.  Below
  * m = 2: 16 for MOE_W_FP8_BLOCK128; for bf16 and MXFP4, 32 once the

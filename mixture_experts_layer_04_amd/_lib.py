@@ -13,6 +13,7 @@ MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 SCORING = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
 WFORMAT = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 STAGE = {"quant": 1, "gemm1": 2, "gemm2": 4, "combine": 8, "all": 15}
+NOALLOC_SCRATCH_BYTES = 128 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -40,6 +41,8 @@ SIGNATURES = {
     "moe_layer": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f,
                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "moe_layer_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                               _i, _f, _vp, _vp, _vp, _vp]),
     "moe_layer_block_m": (_i, [_i, _i, _i, _i, _i]),
     "moe_debug_error": (_i32, [_vp, _vp]),
     "moe_probe_empty": (_i, [_vp]),

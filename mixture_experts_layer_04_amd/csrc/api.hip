@@ -107,32 +107,47 @@ extern "C" int moe_layer_block_m(int T, int E, int F, int k, int wformat) {
   return moe::layer_block_m(T, k, E, F, wformat);
 }
 
+namespace moe {
+size_t layer_workspace_bytes(int T, int H, int E, int F, int k, int n_shared, int block_m, int wformat) {
+  if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1 || n_shared < 0 || n_shared > 1) return 0;
+  if (block_m == 0) block_m = layer_block_m(T, k + n_shared, E + n_shared, F, wformat);
+  return layer_layout(T, H, E, F, k, n_shared, block_m, wformat).total;
+}
+}  // namespace moe
+
 extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared, int block_m,
                                            int wformat) {
-  if (T < 0 || H < 1 || E < 1 || F < 1 || k < 1 || n_shared < 0 || n_shared > 1) return 0;
-  if (block_m == 0) block_m = moe::layer_block_m(T, k + n_shared, E + n_shared, F, wformat);
-  return moe::layer_layout(T, H, E, F, k, n_shared, block_m, wformat).total;
+  return moe::layer_workspace_bytes(T, H, E, F, k, n_shared, block_m, wformat);
 }
 
-extern "C" moe_status moe_layer(const void* x, const float* gate, const float* bias, int wformat,
-                                const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
-                                int T, int H, int E, int F, int k, int n_shared, int n_group, int topk_group,
-                                int scoring, int renormalize, float routed_scale, int block_m, float swiglu_limit,
-                                void* y, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
-  using namespace moe;
+namespace moe {
+
+moe_status layer_validate(const void* x, const float* gate, int wformat, const void* w13, const void* w13_scale,
+                          const void* w2, const void* w2_scale, int T, int H, int E, int F, int k, int n_shared,
+                          int n_group, int topk_group, int scoring, int block_m, float swiglu_limit, const void* y) {
   if (n_shared != 0 && n_shared != 1) return MOE_E_INVAL;
-  const int Ea = E + n_shared, ka = k + n_shared;  // the expert FFN sees the shared expert as expert E
+  const int Ea = E + n_shared, ka = k + n_shared;
   if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1 && F >= 1) ? layer_block_m(T, ka, Ea, F, wformat) : 16;
-  // validate everything before enqueuing anything
   int32_t dummy_i = 0;
   float dummy_f = 0.f;
   moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, &dummy_i, &dummy_f);
   if (st != MOE_OK) return st;
-  st = ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, &dummy_i, &dummy_f, &dummy_i, &dummy_i, &dummy_i,
-                    T, H, Ea, F, ka, block_m, swiglu_limit, y);
+  return ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, &dummy_i, &dummy_f, &dummy_i, &dummy_i, &dummy_i,
+                      T, H, Ea, F, ka, block_m, swiglu_limit, y);
+}
+
+moe_status layer_enqueue(const void* x, const float* gate, const float* bias, int wformat, const void* w13,
+                         const void* w13_scale, const void* w2, const void* w2_scale, int T, int H, int E, int F,
+                         int k, int n_shared, int n_group, int topk_group, int scoring, int renormalize,
+                         float routed_scale, int block_m, float swiglu_limit, void* y, int32_t* topk_ids_out,
+                         float* topk_weights_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // validate everything before enqueuing anything
+  moe_status st = layer_validate(x, gate, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k, n_shared, n_group,
+                                 topk_group, scoring, block_m, swiglu_limit, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
+  const int Ea = E + n_shared, ka = k + n_shared;  // the expert FFN sees the shared expert as expert E
+  if (block_m == 0) block_m = layer_block_m(T, ka, Ea, F, wformat);
   if (!workspace) return MOE_E_INVAL;
   const LayerLayout L = layer_layout(T, H, E, F, k, n_shared, block_m, wformat);
   if (workspace_bytes < L.total) return MOE_E_WORKSPACE;
@@ -167,6 +182,19 @@ extern "C" moe_status moe_layer(const void* x, const float* gate, const float* b
   if (st != MOE_OK) return st;
   a.pairs_ready = pairs_written;
   return launch_ffn(a, stream);
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_layer(const void* x, const float* gate, const float* bias, int wformat,
+                                const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
+                                int T, int H, int E, int F, int k, int n_shared, int n_group, int topk_group,
+                                int scoring, int renormalize, float routed_scale, int block_m, float swiglu_limit,
+                                void* y, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return moe::layer_enqueue(x, gate, bias, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k, n_shared, n_group,
+                            topk_group, scoring, renormalize, routed_scale, block_m, swiglu_limit, y, topk_ids_out,
+                            topk_weights_out, workspace, workspace_bytes, stream);
 }
 
 extern "C" int32_t moe_debug_error(void* workspace, hipStream_t stream) {

@@ -111,6 +111,18 @@ moe_status launch_finalize(const FfnArgs& a, hipStream_t stream);
 // the 8 XCDs in contiguous runs (see xcd_tile()).
 int tile_grid(int64_t n_tiles, int max_wgs);
 
+// moe_layer's checks (scalars, formats, non-null pointers), and moe_layer on
+// a caller-chosen workspace (checks first, then route + align + expert FFN).
+size_t layer_workspace_bytes(int T, int H, int E, int F, int k, int n_shared, int block_m, int wformat);
+moe_status layer_validate(const void* x, const float* gate, int wformat, const void* w13, const void* w13_scale,
+                          const void* w2, const void* w2_scale, int T, int H, int E, int F, int k, int n_shared,
+                          int n_group, int topk_group, int scoring, int block_m, float swiglu_limit, const void* y);
+moe_status layer_enqueue(const void* x, const float* gate, const float* bias, int wformat, const void* w13,
+                         const void* w13_scale, const void* w2, const void* w2_scale, int T, int H, int E, int F,
+                         int k, int n_shared, int n_group, int topk_group, int scoring, int renormalize,
+                         float routed_scale, int block_m, float swiglu_limit, void* y, int32_t* topk_ids_out,
+                         float* topk_weights_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 }  // namespace moe
 
 #ifdef __HIPCC__

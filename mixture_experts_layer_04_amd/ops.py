@@ -178,6 +178,30 @@ def layer(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_group=1,
     return (y, ids, w) if return_routing else y
 
 
+def layer_noalloc(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_group=1, renormalize=True,
+                  routed_scale=1.0, wformat="bf16", w13_scale=None, w2_scale=None, block_m=0,
+                  return_routing=False, out=None, swiglu_limit=math.inf, n_shared=0):
+    """moe_layer_noalloc: moe_layer on the library's own scratch array (no
+    workspace; the outputs are still the caller's tensors, allocated here
+    unless ``out`` is given)."""
+    _check_cuda(x, gate, bias, w13, w2, w13_scale, w2_scale, out)
+    T, H, Ew, F = _dims(x, w13, w2, wformat)
+    E = gate.shape[0]
+    if Ew != E + n_shared:
+        raise ValueError(f"w13 holds {Ew} experts, the gate {E} and n_shared = {n_shared}")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if out is None else out
+    ids = w = None
+    if return_routing:
+        ids = torch.empty((T, k + n_shared), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, k + n_shared), dtype=torch.float32, device=x.device)
+    check(lib().moe_layer_noalloc(_ptr(x), _ptr(gate), _ptr(bias), WFORMAT[wformat], _ptr(w13), _ptr(w13_scale),
+                                  _ptr(w2), _ptr(w2_scale), T, H, E, F, k, n_shared, n_group, topk_group,
+                                  SCORING[scoring], int(bool(renormalize)), float(routed_scale), block_m,
+                                  float(swiglu_limit), _ptr(y), _ptr(ids), _ptr(w), _stream(x.device)),
+          "moe_layer_noalloc")
+    return (y, ids, w) if return_routing else y
+
+
 def debug_error(ws):
     """Synchronises and returns (and clears) the sticky alignment error bits."""
     return int(lib().moe_debug_error(_ptr(ws), _stream(ws.device)))
