@@ -101,6 +101,12 @@ typedef enum moe_wformat {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_str(moe_status s);
 
+/* Hash of the sources the library was built from (16 hex digits of a
+ * sha256 over the HIP sources, headers and build script; static string).
+ * The Python loader compares it with the sources beside the library and
+ * refuses a library built from other sources. */
+const char* moe_source_hash(void);
+
 /* ------------------------------------------------------------------------
  * moe_route - the router ([Router] §1.1 "Three Steps", §1.3, §5.3;
  * [MoE] fused_topk and grouped_topk listings; [Kernels] "Router: one fused

@@ -5,9 +5,32 @@ with an error that says how to build it.
 """
 
 import ctypes
+import glob
+import hashlib
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "moe.h")
+
+
+def source_files():
+    """Every file the library is built from: the HIP sources and headers, the
+    public header and the build script (its flags)."""
+    csrc = os.path.join(HERE, "csrc")
+    return sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))) + \
+        [HEADER, os.path.join(HERE, "build.py")]
+
+
+def source_hash():
+    """First 16 hex digits of a sha256 over the names and contents of
+    source_files(); build.py compiles it into the library."""
+    h = hashlib.sha256()
+    for f in source_files():
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = range(5)
 SCORING = {"softmax": 0, "sigmoid": 1, "sqrtsoftplus": 2}
@@ -24,6 +47,7 @@ _i32 = ctypes.c_int32
 
 SIGNATURES = {
     "moe_status_str": (ctypes.c_char_p, [_i]),
+    "moe_source_hash": (ctypes.c_char_p, []),
     "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_workspace_size": (_sz, [_i, _i, _i]),
     "moe_route_align": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp,
@@ -73,6 +97,11 @@ def lib():
             fn = getattr(L, name)
             fn.restype = res
             fn.argtypes = args
+        built, now = L.moe_source_hash().decode(), source_hash()
+        if built != now:
+            raise RuntimeError(
+                f"{LIB_PATH} was built from other sources (hash {built}, sources {now}); rebuild it with "
+                "`python -m mixture_experts_layer_04_amd.build`.")
         _lib = L
     return _lib
 

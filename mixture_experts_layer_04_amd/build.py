@@ -34,9 +34,18 @@ COMMON = [
 ]
 
 
-def _compile(src):
+def _source_hash():
+    sys.path.insert(0, os.path.dirname(HERE))
+    try:
+        from mixture_experts_layer_04_amd._lib import source_hash
+    finally:
+        sys.path.pop(0)
+    return source_hash()
+
+
+def _compile(src, defines=()):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -47,8 +56,11 @@ def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
+    # the library reports the hash of the sources it was built from
+    # (moe_source_hash); the loader refuses a library whose hash differs
+    defines = [f'-DMOE_SOURCE_HASH="{_source_hash()}"']
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, defines), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

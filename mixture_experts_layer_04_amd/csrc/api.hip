@@ -91,6 +91,11 @@ int layer_block_m(int T, int k, int E, int F, int wformat) {
 
 }  // namespace moe
 
+#ifndef MOE_SOURCE_HASH
+#define MOE_SOURCE_HASH "unknown"
+#endif
+extern "C" const char* moe_source_hash(void) { return MOE_SOURCE_HASH; }
+
 extern "C" const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";

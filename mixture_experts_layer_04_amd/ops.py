@@ -16,6 +16,10 @@ import torch
 from ._lib import SCORING, STAGE, WFORMAT, check, lib
 
 _WS = {}
+# Workspaces the cache has outgrown.  They are never freed: a HIP graph
+# captured with one keeps its address, and freeing it would let its replays
+# write router partials and tile-queue counters into another tensor's memory.
+_WS_RETIRED = []
 
 
 def _ptr(t):
@@ -29,11 +33,14 @@ def _stream(device):
 def workspace(device, nbytes):
     """A zero-filled workspace of at least ``nbytes`` on ``device`` (cached,
     grown on demand; the library leaves its counters at zero after each call,
-    so the cached buffer stays valid)."""
+    so the cached buffer stays valid; an outgrown one is kept alive, not
+    freed, since a captured graph may still use it)."""
     device = torch.device(device)
     key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _WS_RETIRED.append(ws)
         ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws

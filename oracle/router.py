@@ -103,8 +103,9 @@ def group_limit(keys, n_group, topk_group):
     """R4.  Group-limited routing: experts [g*E/n, (g+1)*E/n) form group g;
     a group's score is the sum of its two largest rank keys; the topk_group
     best groups stay (lowest group id on ties); the other experts are not
-    allowed.  ([MoE] grouped_topk listing and the DeepSeek-V3 trace, step 2:
-    "score the 8 groups by their top-2 sum, keep the best 4".)
+    allowed.  ([MoE] "Mixture of Experts", the grouped_topk listing and
+    the second step of the DeepSeek-V3 trace, where the eight groups are
+    ranked by the sum of their two best keys and four of them are kept.)
 
     Returns (allowed mask [T, E], group scores [T, n_group], kept groups
     [T, topk_group]).  Pinned by brute-force enumeration in the tests."""
@@ -153,7 +154,8 @@ def weights(sc, ids, renormalize=True, routed_scale=1.0):
     """R6.  The weight of a chosen expert is its (unbiased) score; with
     renormalisation it is divided by the sum over the k chosen plus 1e-20
     ([Router] §4, the naive router); then the routed scaling factor
-    multiplies ([MoE], DeepSeek-V3 trace step 2, "renormalise, scale")."""
+    multiplies ([MoE] "Mixture of Experts", second step of the DeepSeek-V3
+    trace: the weights are renormalised first and scaled after)."""
     sc = np.asarray(sc, dtype=np.float64)
     w = np.take_along_axis(sc, np.asarray(ids), axis=1)
     if renormalize:
