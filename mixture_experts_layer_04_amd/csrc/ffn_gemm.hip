@@ -158,19 +158,22 @@ __global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* x, uint8_t
     constexpr int GL = (F == F_FP8) ? 16 : 4;  // lanes per scale group
 #pragma unroll
     for (int off = 1; off < GL; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-    float inv;
+    float g[8];
     if (F == F_FP8) {
       const float s = fp8_group_scale(m);
-      inv = 1.f / s;
       if ((lane & 15) == 0) static_cast<float*>(xs)[(size_t)t * (H / 128) + h / 128] = s;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = fp8_scaled(f[i], s);
     } else {
       const uint32_t c = mx_group_code(m);
-      inv = e8m0_inv(c);
+      const float inv = e8m0_inv(c);
       if ((lane & 3) == 0) static_cast<uint8_t*>(xs)[(size_t)t * (H / 32) + h / 32] = (uint8_t)c;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) g[i] = clamp448(f[i] * inv);
     }
     uint2 q;
-    q.x = pack4_e4m3(clamp448(f[0] * inv), clamp448(f[1] * inv), clamp448(f[2] * inv), clamp448(f[3] * inv));
-    q.y = pack4_e4m3(clamp448(f[4] * inv), clamp448(f[5] * inv), clamp448(f[6] * inv), clamp448(f[7] * inv));
+    q.x = pack4_e4m3(g[0], g[1], g[2], g[3]);
+    q.y = pack4_e4m3(g[4], g[5], g[6], g[7]);
     *reinterpret_cast<uint2*>(xq + (size_t)t * H + h) = q;
   }
 }
@@ -605,11 +608,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 #pragma unroll
             for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, xch[w2 * BM + lr]);
             const float sc = fp8_group_scale(amax);
-            const float inv = 1.f / sc;
             if (wn == 0 && r == 0) act_s[(size_t)(blk * BM + lr) * (p.F / 128) + nt] = sc;
 #pragma unroll
             for (int fa = 0; fa < FA; ++fa)
-              lds[lr * BNA + lcol0 + fa * 16 + r] = (uint8_t)to_e4m3(clamp448(v[fm][fa][i] * inv));
+              lds[lr * BNA + lcol0 + fa * 16 + r] = (uint8_t)to_e4m3(fp8_scaled(v[fm][fa][i], sc));
           }
       } else {  // F_MX: groups of 32 columns = fragment pairs of this wave
         uint8_t* act_s = static_cast<uint8_t*>(p.act_s);
@@ -1232,19 +1234,22 @@ __global__ __launch_bounds__(256) void requant_act_kernel(GemmP p) {
       constexpr int GL = (F == F_FP8) ? 16 : 4;  // lanes per scale group
 #pragma unroll
       for (int off = 1; off < GL; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
-      float inv;
+      float g[8];
       if (F == F_FP8) {
         const float sc = fp8_group_scale(m);
-        inv = 1.f / sc;
         if ((lane & 15) == 0) static_cast<float*>(p.act_s)[(size_t)row * (p.F / 128) + c / 128] = sc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = fp8_scaled(f[i], sc);
       } else {
         const uint32_t code = mx_group_code(m);
-        inv = e8m0_inv(code);
+        const float inv = e8m0_inv(code);
         if ((lane & 3) == 0) static_cast<uint8_t*>(p.act_s)[(size_t)row * (p.F / 32) + c / 32] = (uint8_t)code;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[i] = clamp448(f[i] * inv);
       }
       uint2 q;
-      q.x = pack4_e4m3(clamp448(f[0] * inv), clamp448(f[1] * inv), clamp448(f[2] * inv), clamp448(f[3] * inv));
-      q.y = pack4_e4m3(clamp448(f[4] * inv), clamp448(f[5] * inv), clamp448(f[6] * inv), clamp448(f[7] * inv));
+      q.x = pack4_e4m3(g[0], g[1], g[2], g[3]);
+      q.y = pack4_e4m3(g[4], g[5], g[6], g[7]);
       *reinterpret_cast<uint2*>(p.act + (size_t)row * p.F + c) = q;
     }
   }

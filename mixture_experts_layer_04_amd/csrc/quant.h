@@ -33,9 +33,14 @@ __device__ __forceinline__ float e8m0_inv(uint32_t code) { return __uint_as_floa
 
 // Scale of one activation group from its amax: FP8 (128 values) an fp32
 // scale amax / 448 (1 for an all-zero group), MX (32 values) the e8m0 code
-// of pow2_at_least(amax / 448); the values are then multiplied by 1 / scale
-// (FP8) or e8m0_inv(code) (MX), clamped to +-448 and rounded to e4m3.
+// of pow2_at_least(amax / 448), both quotients in fp32.  A value then
+// becomes v / scale in fp32, clamped to +-448 and rounded to e4m3 (ties to
+// even).  FP8 divides (correctly rounded): multiplying by an fp32 1 / scale
+// instead moves values that sit exactly on an e4m3 rounding tie (frequent
+// for bf16 inputs) to one side of it.  MX multiplies by e8m0_inv(code), an
+// exact power of two, which is the same value.
 __device__ __forceinline__ float fp8_group_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
 __device__ __forceinline__ uint32_t mx_group_code(float amax) { return e8m0_at_least(amax / 448.f); }
+__device__ __forceinline__ float fp8_scaled(float v, float scale) { return clamp448(v / scale); }
 
 }  // namespace moe

@@ -339,12 +339,15 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
     }
   }
   uint8_t* xq = p.xq + (size_t)t * p.H + c * KCH + 8 * q;
-  auto store8 = [&](int s, float inv) {
+  // FP8 divides by the group's scale, MX multiplies by its exact inverse
+  // (the arithmetic of quant_x_kernel)
+  auto store8 = [&](int s, float sc, bool divide) {
+    float g[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = divide ? fp8_scaled(v[s][i], sc) : clamp448(v[s][i] * sc);
     uint2 w;
-    w.x = pack4_e4m3(clamp448(v[s][0] * inv), clamp448(v[s][1] * inv), clamp448(v[s][2] * inv),
-                     clamp448(v[s][3] * inv));
-    w.y = pack4_e4m3(clamp448(v[s][4] * inv), clamp448(v[s][5] * inv), clamp448(v[s][6] * inv),
-                     clamp448(v[s][7] * inv));
+    w.x = pack4_e4m3(g[0], g[1], g[2], g[3]);
+    w.y = pack4_e4m3(g[4], g[5], g[6], g[7]);
     *reinterpret_cast<uint2*>(xq + 32 * s) = w;
   };
   if (p.qfmt == 1) {
@@ -356,10 +359,9 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
     m = fmaxf(m, __shfl_xor(m, 16, kWave));  // the 4 lanes of a token row
     m = fmaxf(m, __shfl_xor(m, 32, kWave));
     const float sc = fp8_group_scale(m);
-    const float inv = 1.f / sc;
     if (tv) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) store8(s, inv);
+      for (int s = 0; s < 4; ++s) store8(s, sc, true);
       if (q == 0) static_cast<float*>(p.xs)[(size_t)t * (p.H / KCH) + c] = sc;
     }
   } else {
@@ -372,7 +374,7 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
       m = fmaxf(m, __shfl_xor(m, 32, kWave));
       const uint32_t code = mx_group_code(m);
       if (tv) {
-        store8(s, e8m0_inv(code));
+        store8(s, e8m0_inv(code), false);
         if (q == 0) static_cast<uint8_t*>(p.xs)[(size_t)t * (p.H / 32) + c * 4 + s] = (uint8_t)code;
       }
     }

@@ -29,13 +29,18 @@ Weight formats (dequantised exactly, never approximated):
 Activation modes:
 
 * ``dense`` (headline parity reference): activations are not quantised.
-* ``emulate`` (diagnostic): x and the SwiGLU output are quantised as the
-  quantised paths do: fp8 - e4m3 with a float scale amax/448 per 1 x 128
-  group; mxfp4 - e4m3 with a power-of-two scale pow2_at_least(amax/448) per
-  32 ([MegaMoE] §3.5 requantisation); an all-zero group gets scale 1.
-  The exact scale computation of the GPU (float32) is not reproduced, so
-  this mode is a diagnostic and carries no parity claim
-  ("parity unpinned" for the emulate mode).
+* ``emulate``: x and the SwiGLU output are quantised as the quantised
+  paths do: fp8 - e4m3 with a float scale amax/448 per 1 x 128 group;
+  mxfp4 - e4m3 with a power-of-two scale pow2_at_least(amax/448) per 32
+  ([MegaMoE] §3.5 requantisation); an all-zero group gets scale 1.  The
+  scale and the scaled value are formed in fp32 (``quantize_act``), so the
+  e4m3 codes of x are the kernels' own; the SwiGLU values the kernels
+  quantise are their fp32 sums, which differ from this float64 value by
+  rounding, so a value on a rounding tie may quantise one code apart.
+  Pinned by the quantiser tests (grid values with power-of-two group
+  scales come back unchanged; each group scales by its own amax; the MX
+  scale at and around its power-of-two boundaries; nearest rounding by
+  brute force).
 """
 
 import numpy as np
@@ -53,19 +58,26 @@ _E2M1_TABLE = e2m1_decode(np.arange(16))
 
 
 def dequant(fmt, data, scale=None):
-    """Exact float64 value of one stored [N, K] weight matrix."""
+    """Exact float64 value of one stored [N, K] weight matrix: each code's
+    value times the scale of the block (fp8: 128 x 128) or group (MX: 32
+    along K) that holds it."""
     if fmt == "bf16":
         return bf16_bits_to_f64(data)
     if fmt == "fp8":
         q = _E4M3_TABLE[np.asarray(data, dtype=np.uint8)]
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
         n, k = q.shape
+        if n % 128 == 0 and k % 128 == 0:  # every block whole: scale by broadcasting
+            return (q.reshape(n // 128, 128, k // 128, 128) * s[:, None, :, None]).reshape(n, k)
         rows = np.repeat(s, 128, axis=0)[:n]
         return q * np.repeat(rows, 128, axis=1)[:, :k]
     if fmt == "mxfp4":
         q = _E2M1_TABLE[unpack_fp4(data, axis=-1)]
         s = e8m0_decode(scale)
-        return q * np.repeat(s, 32, axis=1)[:, : q.shape[1]]
+        n, k = q.shape
+        if k % 32 == 0:
+            return (q.reshape(n, k // 32, 32) * s[:, :, None]).reshape(n, k)
+        return q * np.repeat(s, 32, axis=1)[:, :k]
     raise ValueError(f"unknown weight format {fmt!r}")
 
 
@@ -99,25 +111,37 @@ def silu(g):
 
 def quantize_act(v, fmt):
     """Emulate-mode activation quantisation of rows of ``v`` along its last
-    axis (see module docstring).  Returns dequantised float64 values."""
-    v = np.asarray(v, dtype=np.float64)
+    axis (see module docstring), returning dequantised float64 values.
+
+    Each group of 128 (fp8) or 32 (mxfp4) values of a row gets a scale s and
+    each value becomes s * e4m3_round(value / s).  The pages fix the group
+    sizes and the scale rule (amax / 448; for MX the smallest power of two at
+    least amax / 448) but not the precision in which the scale and the
+    scaled value are formed.  Reading: in fp32, the precision of the
+    formats' scales: the values are taken as fp32, s = fp32(amax / 448)
+    (MX: pow2_at_least of that fp32 quotient), value / s is an fp32
+    division (correctly rounded), then rounded to the nearest e4m3 value
+    with ties to even and saturation at 448.  An all-zero group gets s = 1.
+    So the e4m3 code, an integer decided by floating point, is decided in
+    the same precision on both sides."""
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
     if fmt == "bf16":
-        return v
+        return np.asarray(v, dtype=np.float64)
     group = 128 if fmt == "fp8" else 32
-    n, K = v.shape
-    out = np.empty_like(v)
-    for c0 in range(0, K, group):
-        blk = v[:, c0:c0 + group]
-        amax = np.abs(blk).max(axis=1)
-        for i in range(n):
-            if amax[i] == 0.0:
-                s = 1.0
-            elif fmt == "fp8":
-                s = amax[i] / E4M3_MAX
-            else:
-                s = pow2_at_least(amax[i] / E4M3_MAX)
-            out[i, c0:c0 + group] = e4m3_round(blk[i] / s) * s
-    return out
+    n, K = v32.shape
+    pad = -K % group  # a short last group: zeros change neither amax nor the values
+    g = np.pad(v32, ((0, 0), (0, pad))).reshape(n, (K + pad) // group, group)
+    amax = np.abs(g).max(axis=2, keepdims=True)
+    nz = amax > 0
+    q = np.where(nz, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    if fmt == "fp8":
+        s = q
+    else:
+        s = np.ones_like(q)
+        s[nz] = pow2_at_least(q[nz].astype(np.float64)).astype(np.float32)
+    scaled = (g / s).astype(np.float32)  # fp32 division, correctly rounded
+    out = e4m3_round(scaled.astype(np.float64)) * s.astype(np.float64)
+    return out.reshape(n, K + pad)[:, :K]
 
 
 def swiglu(g, u, limit=np.inf):
@@ -161,33 +185,55 @@ def layer_direct(x, ids, w, expert_fn):
     return combine_direct(outs, w), outs
 
 
-def layer_grouped(x, ids, w, expert_fn, E):
+def layer_grouped(x, ids, w, expert_fn, E, workers=1):
     """Loop over experts, run each on the rows routed to it, scatter the
     weighted results back (the grouped form of the [MoE] numpy check).
-    Also returns the per-assignment outputs [T, k, H]."""
+    Also returns the per-assignment outputs [T, k, H].
+
+    ``workers`` > 1 evaluates that many experts at a time on threads; each
+    expert's rows and result are its own, so the result does not depend on
+    it."""
     x = np.asarray(x, dtype=np.float64)
     ids = np.asarray(ids)
     w = np.asarray(w, dtype=np.float64)
     T, k = ids.shape
     outs = np.zeros((T, k, x.shape[1]))
+    work = []
     for e in range(E):
         toks, slots = np.nonzero(ids == e)
-        if len(toks) == 0:
-            continue
+        if len(toks):
+            work.append((e, toks, slots))
+
+    def run(item):
+        e, toks, slots = item
         outs[toks, slots] = expert_fn(e, x[toks])
+
+    if workers > 1 and len(work) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(run, work))
+    else:
+        for item in work:
+            run(item)
     return combine_direct(outs, w), outs
 
 
 def make_expert_fn(weights, mode="dense", limit=np.inf):
-    """expert_fn for ``layer_*`` from an ExpertWeights; caches each expert's
-    dequantised matrices for the lifetime of the returned function."""
-    cache = {}
+    """expert_fn for ``layer_*`` from an ExpertWeights.  An expert's
+    dequantised matrices are made when it is called and dropped after, except
+    that the last expert called is kept for a next call with the same id (the
+    direct form calls one expert per slot); host memory stays at a few
+    experts whatever E is."""
+    last = {}
     act_fmt = None if mode == "dense" else weights.fmt
 
     def fn(e, rows):
-        if e not in cache:
-            cache[e] = weights.expert(e)
-        W13, W2 = cache[e]
+        mats = last.get(e)
+        if mats is None:
+            mats = weights.expert(e)
+            last.clear()
+            last[e] = mats
+        W13, W2 = mats
         if act_fmt is not None:
             rows = quantize_act(rows, act_fmt)
         return expert_forward(rows, W13, W2, act_fmt, limit)
@@ -195,14 +241,25 @@ def make_expert_fn(weights, mode="dense", limit=np.inf):
     return fn
 
 
-def layer(x_bits, route_out, weights, E, mode="dense", tokens=None, limit=np.inf):
+def layer(x_bits, route_out, weights, E, mode="dense", tokens=None, limit=np.inf, workers=1):
     """The full layer for the tokens in ``tokens`` (all by default), given a
     router result (``oracle.router.route``).  Returns (y [n, H] float64,
-    per-assignment outputs [n, k, H])."""
+    per-assignment outputs [n, k, H]).  ``workers``: see layer_grouped."""
     x = bf16_bits_to_f64(x_bits)
     ids = route_out["ids"]
     w = route_out["weights"]
     if tokens is not None:
         x, ids, w = x[tokens], ids[tokens], w[tokens]
-    fn = make_expert_fn(weights, mode, limit)
-    return layer_grouped(x, ids, w, fn, E)
+    if workers > 1:
+        # one expert function per thread (its one-expert cache is its own)
+        fns = {}
+
+        def fn(e, rows):
+            import threading
+            key = threading.get_ident()
+            if key not in fns:
+                fns[key] = make_expert_fn(weights, mode, limit)
+            return fns[key](e, rows)
+    else:
+        fn = make_expert_fn(weights, mode, limit)
+    return layer_grouped(x, ids, w, fn, E, workers=workers)

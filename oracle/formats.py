@@ -118,9 +118,16 @@ def e4m3_round(values):
 
 
 def pow2_at_least(v):
-    """Smallest power of two >= v for v > 0 (float64, exact)."""
-    v = float(v)
-    if v <= 0.0:
-        raise ValueError("pow2_at_least needs a positive argument")
-    m, e = math.frexp(v)  # v = m * 2**e with 0.5 <= m < 1
-    return math.ldexp(1.0, e - 1) if m == 0.5 else math.ldexp(1.0, e)
+    """Smallest power of two >= v for v > 0 (float64, exact).  Takes a
+    number (returns a float) or an array (returns an array)."""
+    if np.ndim(v) == 0:
+        v = float(v)
+        if v <= 0.0:
+            raise ValueError("pow2_at_least needs a positive argument")
+        m, e = math.frexp(v)  # v = m * 2**e with 0.5 <= m < 1
+        return math.ldexp(1.0, e - 1) if m == 0.5 else math.ldexp(1.0, e)
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(v <= 0.0):
+        raise ValueError("pow2_at_least needs positive arguments")
+    m, e = np.frexp(v)
+    return np.ldexp(1.0, e - (m == 0.5))

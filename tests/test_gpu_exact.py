@@ -25,6 +25,14 @@ this pins the gather through sorted_ids, the gate / up row pairing, the
 SwiGLU column, the GEMM2 scatter to the assignment slot and the slot-order
 combine: a transposed operand, a wrong row or a shifted column changes the
 exact result.
+
+The power-of-two variant keeps these exact values but makes every scale a
+different power of two: fp8 weight blocks 2^((block + e) mod 5 - 2), MX
+e8m0 exponents that change from 32-group to 32-group, activation groups
+whose amax is 448 * 2^j for j varying by group and token (x) or by SwiGLU
+column group (the requantised act).  A scale applied to the wrong block,
+group, row or token then changes the result.  The tile-queue cases are large
+enough that the tiled kernels hand tiles out through their per-XCD queues.
 """
 
 import numpy as np
@@ -41,11 +49,15 @@ pytestmark = pytest.mark.gpu
 _E2M1_CODE = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
 
 
+_E2M1_GRID = np.array(sorted(_E2M1_CODE))  # magnitudes in code order
+
+
 def _encode_e2m1(w):
     """float32 [N, K] on the e2m1 grid -> packed uint8 [N, K/2] (element 2j in
     the low nibble of byte j)."""
     a = np.abs(w)
-    codes = np.vectorize(lambda v: _E2M1_CODE[float(v)])(a).astype(np.uint8)
+    codes = np.searchsorted(_E2M1_GRID, a).astype(np.uint8)
+    assert np.array_equal(_E2M1_GRID[codes], a), "a value is not on the e2m1 grid"
     codes |= ((w < 0) & (a > 0)).astype(np.uint8) << 3
     return codes[:, 0::2] | (codes[:, 1::2] << 4)
 
@@ -77,7 +89,85 @@ def build(E, H, F, T, k, seed, kind="uniform"):
     return x, w13, w2, ids, w
 
 
-def to_device(fmt, x, w13, w2):
+def pow2_variant(x, w13, w2):
+    """The same exact values with activation groups of different power-of-two
+    amax: x[t, 32 i] = 448 * 2^j, j = (t + i) mod 5 - 2 (those columns meet
+    no nonzero weight), and the up row of every 32nd SwiGLU column scaled by
+    2^jf, jf = (f / 32 + e) mod 3, so that column's act is 448 * 2^jf, the
+    largest of its group (the other act values are 32 u, |u| <= 12).  The
+    fp8 scales of x (per 1 x 128: amax / 448) and of act, and the MX scales
+    (per 32: the smallest power of two at least amax / 448), are then exact
+    powers of two that differ from group to group and token to token; every
+    quantised value stays exact and y is unchanged."""
+    x, w13 = x.copy(), w13.copy()
+    T, H = x.shape
+    E, N13, _ = w13.shape
+    F = N13 // 2
+    j = (np.arange(T)[:, None] + np.arange(H // 32)[None, :]) % 5 - 2
+    x[:, ::32] = 448.0 * np.exp2(j)
+    for e in range(E):
+        for f in range(0, F, 32):
+            jf = (f // 32 + e) % 3
+            w13[e, F + f, 1] = 1.5 * 2.0 ** jf
+            w13[e, F + f, 2] = 2.0 ** jf
+    return x, w13, w2
+
+
+def _fp8_block_exponents(E, N, K):
+    """2^s per 128 x 128 block, s = (block index + e) mod 5 - 2."""
+    b = np.arange((N // 128) * (K // 128)).reshape(N // 128, K // 128)
+    return np.stack([(b + e) % 5 - 2 for e in range(E)])
+
+
+def _mx_group_exponents(w):
+    """One e8m0 exponent per (expert, row, 32-group) for weights w [E, N, K]
+    whose values are fixed: each group takes one of the exponents s in -3..4
+    for which every value / 2^s is an e2m1 value (any s for an all-zero
+    group), a different one from group to group."""
+    E, N, K = w.shape
+    g = np.abs(w).reshape(E, N, K // 32, 1, 32)
+    cand = np.arange(-3, 5)
+    scaled = g / np.exp2(cand.astype(np.float64))[:, None]
+    ok = np.all((g == 0) | np.isin(scaled, _E2M1_GRID), axis=-1)  # [E, N, G, 8]
+    count = ok.sum(axis=-1)
+    assert np.all(count > 0)
+    e_, n_, i_ = np.meshgrid(np.arange(E), np.arange(N), np.arange(K // 32), indexing="ij")
+    pick = (7 * n_ + 3 * i_ + e_) % count  # index among the allowed exponents
+    rank = np.cumsum(ok, axis=-1) - 1
+    sel = ok & (rank == pick[..., None])
+    return cand[np.argmax(sel, axis=-1)]
+
+
+def to_device(fmt, x, w13, w2, pow2=False):
+    """Stored tensors of each format: unit scales, or (``pow2``) scales that
+    are distinct powers of two per fp8 128 x 128 block / MX 32-group, with the
+    codes chosen so that code x scale is the same exact weight."""
+    if pow2 and fmt == "fp8":
+        E, N13, H = w13.shape
+        F = w2.shape[2]
+        s13 = np.exp2(_fp8_block_exponents(E, N13, H)).astype(np.float32)
+        s2 = np.exp2(_fp8_block_exponents(E, H, F)).astype(np.float32)
+        c13 = w13 / np.repeat(np.repeat(s13, 128, axis=1), 128, axis=2)
+        c2 = w2 / np.repeat(np.repeat(s2, 128, axis=1), 128, axis=2)
+        as_codes = lambda c: torch.from_numpy(c.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+        k13, k2 = as_codes(c13), as_codes(c2)
+        # every code is exact: decoding gives back the value it encodes
+        assert np.array_equal(fm.e4m3_decode(k13.numpy()), c13) and np.array_equal(fm.e4m3_decode(k2.numpy()), c2)
+        xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+        return xd, k13.cuda(), torch.from_numpy(s13).cuda(), k2.cuda(), torch.from_numpy(s2).cuda()
+    if pow2 and fmt == "mxfp4":
+        e13, e2 = _mx_group_exponents(w13), _mx_group_exponents(w2)
+        c13 = w13 / np.repeat(np.exp2(e13.astype(np.float64)), 32, axis=2)
+        c2 = w2 / np.repeat(np.exp2(e2.astype(np.float64)), 32, axis=2)
+        p13 = np.stack([_encode_e2m1(c13[e]) for e in range(c13.shape[0])])
+        p2 = np.stack([_encode_e2m1(c2[e]) for e in range(c2.shape[0])])
+        xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
+        sc = lambda ex: torch.from_numpy((ex + 127).astype(np.uint8)).cuda()
+        return xd, torch.from_numpy(p13).cuda(), sc(e13), torch.from_numpy(p2).cuda(), sc(e2)
+    return _to_device_unit(fmt, x, w13, w2)
+
+
+def _to_device_unit(fmt, x, w13, w2):
     """Stored tensors of each format (unit scales)."""
     xd = torch.from_numpy(x).to(torch.bfloat16).cuda()
     E, N13, H = w13.shape
@@ -107,20 +197,24 @@ CASES = [("bf16", 256, 256, bm, T) for bm, T in ((16, 5), (16, 300), (32, 300), 
 # expert per tile): experts with an even and an odd number of blocks (uniform ids: 375
 # and 500 rows per expert), uneven counts from skewed ids, one expert with
 # one block (the hot expert set leaves the others empty), and a block table
-# longer than one 1024-block chunk of the pair table (checked on a sample).
+# longer than one 1024-block chunk of the pair table, whose tiles the per-XCD
+# queues hand out (every token compared).
 PAIRED = [("bf16", 256, 256, 128, 1500, "uniform", None), ("bf16", 512, 384, 128, 2000, "uniform", None),
           ("bf16", 256, 512, 128, 3000, "skewed", None), ("bf16", 256, 256, 128, 100, "hot", None),
-          ("bf16", 256, 128, 128, 70000, "uniform", 300),
+          ("bf16", 256, 128, 128, 70000, "uniform", None),
           # 64-row blocks paired too: an odd count (175 rows per expert) and uneven ones
           ("bf16", 512, 384, 64, 700, "uniform", None), ("bf16", 256, 256, 64, 1100, "skewed", None)]
 
 
-def _run_exact(fmt, H, F, bm, T, kind="uniform", sample=None):
+def _run_exact(fmt, H, F, bm, T, kind="uniform", sample=None, pow2=False):
     import mixture_experts_layer_04_amd as moe
     E, k = 8, 2
-    say(f"exact probe {fmt} H={H} F={F} E={E} k={k} T={T} block_m={bm} ids={kind}")
+    say(f"exact probe {fmt} H={H} F={F} E={E} k={k} T={T} block_m={bm} ids={kind}"
+        + (" power-of-two scales" if pow2 else ""))
     x, w13, w2, ids, w = build(E, H, F, T, k, seed=T + bm, kind=kind)
-    xd, c13, s13, c2, s2 = to_device(fmt, x, w13, w2)
+    if pow2:
+        x, w13, w2 = pow2_variant(x, w13, w2)
+    xd, c13, s13, c2, s2 = to_device(fmt, x, w13, w2, pow2)
     ids_d = ids.cuda()
     w_d = torch.from_numpy(w).cuda()
     s, b, n = moe.align(ids_d, E, bm)
@@ -153,3 +247,28 @@ def test_expert_ffn_exact(fmt, H, F, bm, T):
 @pytest.mark.parametrize("fmt,H,F,bm,T,kind,sample", PAIRED)
 def test_expert_ffn_exact_paired_tiles(fmt, H, F, bm, T, kind, sample):
     _run_exact(fmt, H, F, bm, T, kind, sample)
+
+
+# Every scale a power of two that differs from block to block (fp8 weights),
+# from 32-group to 32-group (MX weights) and from activation group to group
+# and token to token: a scale read from the wrong block, group, row or token
+# changes the exact result.  Stream (16) and tiled (32 / 64 / 128) kernels.
+POW2 = [(f, 512, 512, bm, T) for f in ("fp8", "mxfp4") for bm, T in ((16, 3), (16, 200), (32, 200), (64, 200),
+                                                                     (128, 200))] + \
+       [("fp8", 1024, 512, 128, 600), ("mxfp4", 512, 1024, 64, 600)]
+
+
+@pytest.mark.parametrize("fmt,H,F,bm,T", POW2)
+def test_expert_ffn_exact_pow2_scales(fmt, H, F, bm, T):
+    _run_exact(fmt, H, F, bm, T, pow2=True)
+
+
+# Large enough that every XCD has more tiles than workgroups, so the tiled
+# kernels take tiles from their per-XCD queues: every token compared.
+QUEUE = [("fp8", 512, 512, 128, 40000), ("mxfp4", 512, 512, 128, 40000), ("mxfp4", 512, 512, 32, 12000),
+         ("fp8", 512, 512, 64, 20000)]
+
+
+@pytest.mark.parametrize("fmt,H,F,bm,T", QUEUE)
+def test_expert_ffn_exact_tile_queue(fmt, H, F, bm, T):
+    _run_exact(fmt, H, F, bm, T, pow2=True)

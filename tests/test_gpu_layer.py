@@ -1,15 +1,17 @@
-"""GPU parity of moe_layer / moe_expert_ffn against the float64 oracle
-(relative Frobenius error within the benchmark spec's tolerance), at small sizes
-on every token (several tiles, ragged tails, every BLOCK_M) and at the full
-layer shapes on sampled tokens in the launch configuration the benchmark
-uses; plus HIP-graph capture and determinism."""
+"""GPU parity of moe_layer / moe_expert_ffn against the float64 oracle, on
+every token: relative Frobenius error within the benchmark spec's tolerance and
+every token's own error within three times it, at small sizes (several
+tiles, ragged tails, every BLOCK_M) and at the full layer shapes in the
+launch configuration the benchmark uses; for fp8 / MXFP4 also against the
+oracle that quantises activations as the kernels do; plus HIP-graph capture
+and determinism."""
 
 import numpy as np
 import pytest
 import torch
 
-from helpers import (LAYER_TOL, bf16_to_f64, check_routing, oracle_layer, oracle_route, rel_fro,
-                     routing_for_layer, say)
+from helpers import (EMULATE_TOL, LAYER_TOL, bf16_to_f64, check_output, check_routing, oracle_layer, oracle_route,
+                     rel_fro, routing_for_layer, say)
 from synth import get_config, make_weights, make_x
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +36,10 @@ def run_layer(cfg, W, x, block_m=0, limit=np.inf):
                      swiglu_limit=limit)
 
 
-def check_layer(cfg, T, block_m=0, sample=None, seed=0, limit=np.inf):
+def check_layer(cfg, T, block_m=0, limit=np.inf, dense=True):
+    """moe_layer against the oracle on every token.  ``dense``: against the
+    dense-equivalent oracle (the headline tolerance); the quantised formats
+    are also checked against the emulate-mode oracle."""
     say(f"layer {cfg.name} {cfg.wformat} E={cfg.E} H={cfg.H} F={cfg.F} k={cfg.k} T={T} block_m={block_m}"
         + (f" SwiGLU limit {limit}" if np.isfinite(limit) else ""))
     W = weights_for(cfg)
@@ -44,23 +49,15 @@ def check_layer(cfg, T, block_m=0, sample=None, seed=0, limit=np.inf):
     r = oracle_route(cfg, x, W["gate"], W["bias"])
     check_routing(cfg, r, ids.cpu().numpy(), w.cpu().numpy())
     routing = routing_for_layer(cfg, r, ids.cpu().numpy())
-    tokens = None
-    if sample is not None and sample < T:
-        rng = np.random.default_rng(seed)
-        tokens = np.unique(np.concatenate([rng.choice(T, sample - 1, replace=False), [T - 1]]))
-    y_ref = oracle_layer(cfg, x, routing, W, tokens=tokens, limit=limit)
     got = bf16_to_f64(y)
-    if tokens is not None:
-        got = got[tokens]
-    err = rel_fro(got, y_ref)
-    say(f"  rel. Frobenius error {err:.3e} (tolerance {LAYER_TOL[cfg.wformat]:.0e})")
-    if cfg.wformat != "bf16" and (tokens is None or len(tokens) <= 8):
-        # diagnostic: against the oracle that quantises activations as the
-        # kernels do (scales in float64, so rare e4m3 rounding flips differ)
-        y_em = oracle_layer(cfg, x, routing, W, tokens=tokens, mode="emulate", limit=limit)
-        say(f"  vs emulate-mode oracle: {rel_fro(got, y_em):.3e}")
-    assert np.all(np.isfinite(got))
-    assert err <= LAYER_TOL[cfg.wformat]
+    err = None
+    if dense:
+        y_ref = oracle_layer(cfg, x, routing, W, limit=limit)
+        err, _, _ = check_output(got, y_ref, LAYER_TOL[cfg.wformat], "dense-equivalent oracle")
+    if cfg.wformat != "bf16":
+        y_em = oracle_layer(cfg, x, routing, W, mode="emulate", limit=limit)
+        e_em, _, _ = check_output(got, y_em, EMULATE_TOL, "emulate-mode oracle")
+        err = e_em if err is None else err
     return x, W, y, ids, w, err
 
 
@@ -96,20 +93,25 @@ def test_layer_small_all_tokens(name, over, T, bm):
     check_layer(cfg, T, bm)
 
 
-CLAMPED = [("toy", dict(F=256), 100, 16, 0.25), ("toy", dict(F=256), 300, 64, 0.25),
-           ("toy", dict(F=256), 300, 128, 0.25),
-           ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 300, 32, 0.5),
-           ("dsv4", dict(E=16, H=512, F=512, k=4), 37, 16, 0.5), ("dsv4", dict(E=8, H=512, F=1024, k=2), 700, 128, 0.5)]
+CLAMPED = [("toy", dict(F=256), 100, 16, 0.25, True), ("toy", dict(F=256), 300, 64, 0.25, True),
+           ("toy", dict(F=256), 300, 128, 0.25, True),
+           # quantised formats at the same limit: judged against the oracle
+           # that quantises the activations as the kernels do (a limit this
+           # low leaves most SwiGLU values at a few levels, where one e4m3
+           # rounding is a larger share of the dense-equivalent result)
+           ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 300, 32, 0.25, False),
+           ("dsv3", dict(E=16, H=512, F=512, k=4, n_group=4, topk_group=2), 37, 16, 0.25, False),
+           ("dsv4", dict(E=16, H=512, F=512, k=4), 37, 16, 0.25, False),
+           ("dsv4", dict(E=8, H=512, F=1024, k=2), 700, 128, 0.25, False),
+           ("dsv4", dict(E=16, H=512, F=512, k=4), 300, 32, 0.5, True)]
 
 
-@pytest.mark.parametrize("name,over,T,bm,limit", CLAMPED)
-def test_layer_swiglu_clamp(name, over, T, bm, limit):
+@pytest.mark.parametrize("name,over,T,bm,limit,dense", CLAMPED)
+def test_layer_swiglu_clamp(name, over, T, bm, limit, dense):
     """The DeepSeek-V4 SwiGLU clamp ([MegaMoE] §3.5) with a limit that a
-    large share of the gate and up values exceed (they are ~N(0, 0.3); the
-    quantised formats take 0.5, where the fp8 activation error of the
-    concentrated clamped values stays inside their tolerance)."""
+    large share of the gate and up values exceed (they are ~N(0, 0.3))."""
     cfg = get_config(name, **over)
-    x, W, y, ids, w, err = check_layer(cfg, T, bm, limit=limit)
+    x, W, y, ids, w, err = check_layer(cfg, T, bm, limit=limit, dense=dense)
     # the clamp changes the layer by far more than the tolerance
     r = oracle_route(cfg, x, W["gate"], W["bias"])
     routing = routing_for_layer(cfg, r, ids.cpu().numpy())
@@ -123,9 +125,25 @@ FULL = [("qwen3", 1), ("qwen3", 64), ("qwen3", 1024), ("qwen3", 4096), ("glm", 1
 
 
 @pytest.mark.parametrize("name,T", FULL)
-def test_layer_full_size_sampled(name, T):
+def test_layer_full_size_all_tokens(name, T):
+    """The configurations' own shapes, in the launch configuration bench.py
+    times (block_m chosen by the library), every token compared."""
     cfg = get_config(name)
-    check_layer(cfg, T, 0, sample=4 if cfg.wformat != "bf16" else 6)
+    check_layer(cfg, T, 0)
+
+
+RENORM_OFF = [("toy", dict(F=256), 100, 16), ("qwen3", {}, 64, 0)]
+
+
+@pytest.mark.parametrize("name,over,T,bm", RENORM_OFF)
+def test_layer_softmax_without_renormalisation(name, over, T, bm):
+    """Softmax top-k without renormalisation ([MoE] fused_topk listing, the
+    renormalize flag): the weights are the chosen experts' softmax
+    probabilities, which sum to less than one."""
+    cfg = get_config(name, **dict(over, renormalize=False))
+    x, W, y, ids, w, err = check_layer(cfg, T, bm)
+    s = w.sum(dim=1).cpu().numpy()
+    assert np.all(s < 1.0) and np.all(s > 0.0)
 
 
 MATCH = [("toy", dict(F=256), 200, 32), ("toy", dict(F=256), 300, 128),
@@ -222,8 +240,8 @@ SHARED = [("toy", {}, 16, 0), ("toy", dict(F=256), 100, 16), ("toy", dict(F=256)
 def test_layer_shared_expert(name, over, T, bm):
     """The shared expert as an always-selected slot (id E, weight 1): the
     router writes slot k, the alignment and the grouped GEMMs treat it as
-    expert E, and y adds its output (full DSV3 / DSV4 shapes on sampled
-    tokens)."""
+    expert E, and y adds its output (full DSV3 / DSV4 shapes included),
+    every token compared."""
     import mixture_experts_layer_04_amd as moe
     cfg = get_config(name, **over)
     say(f"layer + shared expert {cfg.name} {cfg.wformat} E={cfg.E}+1 k={cfg.k}+1 T={T} block_m={bm}")
@@ -243,12 +261,5 @@ def test_layer_shared_expert(name, over, T, bm):
     check_routing(cfg, r, ids[:, :cfg.k], w[:, :cfg.k])
     from oracle import router as orouter
     routing = orouter.with_shared_expert(routing_for_layer(cfg, r, ids[:, :cfg.k]), cfg.E)
-    tokens = None
-    if T > 64:
-        rng = np.random.default_rng(1)
-        tokens = np.unique(np.concatenate([rng.choice(T, 5, replace=False), [T - 1]]))
-    y_ref = oracle_layer(get_config(name, **dict(over, E=cfg.E + 1)), x, routing, W, tokens=tokens)
-    got = bf16_to_f64(y) if tokens is None else bf16_to_f64(y)[tokens]
-    err = rel_fro(got, y_ref)
-    say(f"  rel. Frobenius error {err:.3e} (tolerance {LAYER_TOL[cfg.wformat]:.0e})")
-    assert np.all(np.isfinite(got)) and err <= LAYER_TOL[cfg.wformat]
+    y_ref = oracle_layer(get_config(name, **dict(over, E=cfg.E + 1)), x, routing, W)
+    check_output(bf16_to_f64(y), y_ref, LAYER_TOL[cfg.wformat], "dense-equivalent oracle")

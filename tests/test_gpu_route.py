@@ -62,6 +62,27 @@ def test_route_parity_sqrt_softplus(name, over, T):
     say(f"  clear tokens {int(clear.sum())}/{T}, near-tie tokens with other ids: {differ}")
 
 
+RENORM_OFF = [("qwen3", 1), ("qwen3", 64), ("qwen3", 4096), ("toy", 300)]
+
+
+@pytest.mark.parametrize("name,T", RENORM_OFF)
+def test_route_parity_softmax_without_renormalisation(name, T):
+    """Softmax top-k with renormalize = 0 ([MoE] fused_topk listing): the
+    weights are the chosen experts' probabilities under the softmax over all
+    E experts (they sum to less than one)."""
+    cfg = get_config(name, renormalize=False)
+    say(f"route parity softmax without renormalisation {name} T={T}")
+    gate, bias = make_router_weights(cfg, "cuda")
+    x = make_x(cfg, T, "cuda")
+    ids, w = _route(cfg, x, gate, bias)
+    torch.cuda.synchronize()
+    r = oracle_route(cfg, x, gate, bias)
+    clear, differ = check_routing(cfg, r, ids.cpu().numpy(), w.cpu().numpy())
+    s = w.sum(dim=1).cpu().numpy()
+    assert np.all(s < 1.0) and np.all(s > 0.0)
+    say(f"  clear tokens {int(clear.sum())}/{T}, near-tie tokens with other ids: {differ}")
+
+
 def test_route_toy_worked_example(golden):
     """[Router] §1.1 / §1.3 / §2.1 toy example on the GPU."""
     g = golden("router_toy.json")

@@ -100,7 +100,7 @@ def test_mxfp4_generator_roundtrip_is_nearest():
 @pytest.mark.parametrize("fmt,group", [("fp8", 128), ("mxfp4", 32)])
 def test_activation_quantiser_error_bound(fmt, group):
     rng = np.random.default_rng(9)
-    v = rng.normal(0, 1, size=(6, 256))
+    v = rng.normal(0, 1, size=(6, 256)).astype(np.float32).astype(np.float64)  # fp32 values, as the kernels hold
     v[2, :group] = 0.0  # an all-zero group
     q = offn.quantize_act(v, fmt)
     assert np.all(q[2, :group] == 0.0)
@@ -111,8 +111,85 @@ def test_activation_quantiser_error_bound(fmt, group):
         # range, plus a subnormal floor of half of 2^-9 times the scale
         s = np.where(amax > 0, amax / 448.0, 1.0) if fmt == "fp8" else \
             np.array([[fm.pow2_at_least(a / 448.0) if a > 0 else 1.0] for a in amax[:, 0]])
-        assert np.all(np.abs(qb - blk) <= 2.0 ** -4 * np.abs(blk) + 2.0 ** -10 * s + 1e-15)
-        assert np.all(np.abs(qb) <= 448.0 * s * (1 + 1e-15))
+        assert np.all(np.abs(qb - blk) <= 2.0 ** -4 * np.abs(blk) + 2.0 ** -10 * s + 1e-6 * np.abs(blk))
+        assert np.all(np.abs(qb) <= 448.0 * s * (1 + 1e-6))
+
+
+_E4M3_GRID = fm.e4m3_decode(np.arange(256, dtype=np.uint8))
+_E4M3_GRID = _E4M3_GRID[np.isfinite(_E4M3_GRID)]
+
+
+@pytest.mark.parametrize("fmt,group", [("fp8", 128), ("mxfp4", 32)])
+def test_activation_quantiser_keeps_grid_values_with_pow2_group_scales(fmt, group):
+    """Each group is e4m3 values times its own power of two, with one element
+    at +-448 times it: the group's scale is exactly that power of two (amax /
+    448, and the smallest power of two at least amax / 448, agree), so the
+    quantiser returns every value unchanged.  A wrong group size, a scale
+    from another group or a wrong scale rule changes some of them."""
+    rng = np.random.default_rng(3)
+    n, K = 5, 4 * group
+    codes = rng.choice(_E4M3_GRID[np.abs(_E4M3_GRID) <= 256], size=(n, K))
+    j = rng.integers(-6, 7, size=(n, K // group))
+    codes[:, ::group] = np.where(rng.random((n, K // group)) < 0.5, -448.0, 448.0)
+    v = codes * np.repeat(np.exp2(j.astype(np.float64)), group, axis=1)
+    assert np.array_equal(offn.quantize_act(v, fmt), v)
+
+
+@pytest.mark.parametrize("fmt,group", [("fp8", 128), ("mxfp4", 32)])
+def test_activation_quantiser_scales_each_group_by_its_own_amax(fmt, group):
+    """Neighbouring groups whose magnitudes differ by 10^6 (and an all-zero
+    group): every group keeps its largest element to rounding (fp8: it maps to
+    448 exactly; MX: to the e4m3 value nearest amax / s with s = the smallest
+    power of two at least amax / 448) and the zero group stays zero.  A scale
+    taken from the neighbouring group would flush the small group to zero or
+    saturate the large one."""
+    rng = np.random.default_rng(4)
+    n, G = 4, 6
+    v = rng.normal(0, 1, size=(n, G * group))
+    mag = np.where(np.arange(G) % 2 == 0, 1e3, 1e-3)
+    v = (v * np.repeat(mag, group)[None, :]).astype(np.float32)  # fp32 values, as the kernels hold
+    v[1, 2 * group:3 * group] = 0.0
+    q = offn.quantize_act(v, fmt)
+    assert np.all(q[1, 2 * group:3 * group] == 0.0)
+    for i in range(n):
+        for g in range(G):
+            blk, qb = v[i, g * group:(g + 1) * group], q[i, g * group:(g + 1) * group]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                continue
+            m = np.argmax(np.abs(blk))
+            # the scale and the scaled values in fp32
+            q32 = amax / np.float32(448.0)
+            s = float(q32) if fmt == "fp8" else fm.pow2_at_least(float(q32))
+            scaled = (blk / np.float32(s)).astype(np.float64)
+            assert 224.0 < scaled[m] * np.sign(blk[m]) <= 448.0 * (1 + 1e-6)
+            # the group's largest element lands on (or next to) 448 x s
+            assert abs(qb[m]) == pytest.approx(s * fm.e4m3_round(abs(scaled[m])), rel=1e-15)
+            # every element is s times its nearest e4m3 value (brute force
+            # over all 254 finite codes; ties have measure zero here)
+            near = _E4M3_GRID[np.argmin(np.abs(_E4M3_GRID[None, :] - np.minimum(np.abs(scaled), 448.0)[:, None]),
+                                        axis=1)] * np.sign(scaled)
+            assert np.allclose(qb, s * near, rtol=1e-15, atol=0)
+
+
+def test_mx_activation_scale_is_the_smallest_power_of_two_at_least_amax_over_448():
+    """The MX activation scale ([MegaMoE] §3.5: a power of two at least
+    amax / 448, the smallest one): amax exactly 448 * 2^j takes 2^j (the
+    element maps to 448); a hair above takes 2^(j+1) (the element maps to
+    224, the rest of the group halves its resolution); a hair below keeps
+    2^j."""
+    for j in (-3, 0, 5):
+        for amax, scale in ((448.0 * 2.0 ** j, 2.0 ** j), (448.0 * 2.0 ** j * (1 + 2.0 ** -20), 2.0 ** (j + 1)),
+                            (448.0 * 2.0 ** j * (1 - 2.0 ** -20), 2.0 ** j)):
+            v = np.zeros((1, 32))
+            v[0, 7] = amax
+            v[0, 8] = 3.0 * 2.0 ** j  # 3 * 2^j / scale is on the e4m3 grid for both scales
+            q = offn.quantize_act(v, "mxfp4")
+            assert q[0, 7] == scale * fm.e4m3_round(amax / scale)
+            assert q[0, 8] == 3.0 * 2.0 ** j
+            assert fm.pow2_at_least(amax / 448.0) == scale
+    assert np.array_equal(fm.pow2_at_least(np.array([0.75, 1.0, 1.5, 2.0 ** -130])),
+                          np.array([1.0, 1.0, 2.0, 2.0 ** -130]))
 
 
 def test_swiglu_clamp_worked_values_and_bounds():
