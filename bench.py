@@ -3,24 +3,35 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input
 resident in HBM: one moe_layer call (route -> align -> expert FFN: GEMM1 +
-SwiGLU, GEMM2, slot-order combine).  The dominant kernel's launch time (the
-grouped GEMM1, for the roofline) comes from a second loop of as many steps
-driven through moe_route, moe_align and moe_expert_ffn_stages, so that HIP
-events on the kernels' stream bracket GEMM1.
+SwiGLU, GEMM2, slot-order combine), replayed from a HIP graph captured once.
+The K timed steps run back to back, bracketed by synchronisation.
 
-Default workload: the Qwen3-30B-A3B-shaped layer (H 2048, E 128, k 8, F 768,
-softmax top-8, bf16 experts) at T = 4096 tokens.  Printed as one JSON line
-on stdout; diagnostics go to stderr.
+Default workload: the DeepSeek-V4-Flash-shaped layer (H 4096, E 256, k 6,
+F 2048, sigmoid + bias top-6, MXFP4 expert weights x e4m3 activations with
+per-32 power-of-two scales) at T = 8192 tokens, the largest configuration of
+the headline metric.  Printed as one JSON line on stdout; diagnostics go to
+stderr.
 
 Also reported in the same line:
-  roofline      - the GEMM1 kernel against MI355X's published peaks
-  cpu_baseline  - the float64 oracle timed on a bounded token sample
-  decode        - cold-cache moe_layer at decode sizes (Qwen3 T = 1, 64;
-                  GLM T = 1, 8; DeepSeek-V3 T = 1; DeepSeek-V4 T = 512):
-                  us/layer and achieved HBM bandwidth on the weights of the
-                  experts actually touched
-  router        - moe_route alone next to the launch floor (empty kernel)
-                  and the bare gate-read kernel, cold
+  span          - cold replays of the same graph (each after a 1 GiB read
+                  that evicts the L2s and the last-level cache): median,
+                  p10 and p90 of the event-pair time around one replay
+  roofline      - the dominant kernel (grouped GEMM1 + SwiGLU) against the
+                  published peak of the matrix-core instruction it issues
+                  and against HBM; its launch time from HIP events on its
+                  own stream in a staged loop with a fixed warm-up
+  decode        - cold graph replays at every decode size of the five
+                  configurations: us/layer (median, p10, p90) and the HBM
+                  rate on the weights of the experts actually touched
+  prefill       - the other prefill configurations: warm back-to-back
+                  replays and cold replays, MFMA and HBM fractions
+  router        - moe_route alone at T = 1 for every configuration (and GLM
+                  at 8 and 512 rows) next to the bare read of its gate
+                  weight and an empty kernel, cold
+  ep_share      - one GPU's share of DeepSeek-V4 expert parallelism (32
+                  MXFP4 experts), cold
+  cpu_baseline  - the float64 oracle timed on a token sample of the
+                  headline workload, and the routing near-tie report
 """
 
 import argparse
@@ -34,21 +45,29 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK = 8.0e12          # B/s, MI355X published
-MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp4": 10.1e15}  # dense FLOP/s
+HBM_PEAK = 8.0e12  # B/s, MI355X published
+# Published dense matrix-core peaks (FLOP/s) by the operand types of the
+# instruction each weight format issues: bf16 x bf16; e4m3 x e4m3; e4m3
+# activations x e2m1 weights, which issues at the fp8 rate (measured:
+# profiles/mfma_rates.txt).
+MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp4": 5.0e15}
+MFMA_ISSUED = {"bf16": "bf16 x bf16 (v_mfma_f32_16x16x32_bf16)",
+               "fp8": "e4m3 x e4m3 (v_mfma_scale_f32_16x16x128_f8f6f4)",
+               "mxfp4": "e4m3 x e2m1 with e8m0 scales (v_mfma_scale_f32_16x16x128_f8f6f4)"}
+DTYPE = {"bf16": "bf16", "fp8": "fp8 (e4m3)", "mxfp4": "fp8 x fp4 (e4m3 x e2m1)"}
 METRIC = "MoE layer µs & tokens/s; HBM TB/s % (T≤256), MFMA % (T≥4k); router µs"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm1_qwen3_T4096_traffic.txt")
+GEMM1_WARMUP = 30  # staged steps before the GEMM1 events, whatever --warmup says
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def traffic_file(cfg, T):
+    return os.path.join(ROOT, "profiles", f"gemm1_{cfg.name}_T{T}_traffic.txt")
+
+
 # ---------------------------------------------------------------- accounting
-def expert_bytes(cfg):
-    return cfg.expert_bytes()
-
-
 def w13_bytes(cfg):
     """Bytes of one expert's w13 [2F, H] with its scales."""
     H, F = cfg.H, cfg.F
@@ -60,24 +79,20 @@ def w13_bytes(cfg):
 
 
 def gemm1_work(cfg, T, touched):
-    """Algorithmic work of one grouped GEMM1 launch: w13 bytes of the experts
-    touched + the activation rows read once + the SwiGLU output written once
-    (activations in bf16, or e4m3 for the fp8 formats; scales not counted);
-    FLOPs 2 * T * k * 2F * H (padding rows not counted)."""
-    ab = 2 if cfg.wformat == "bf16" else 1
-    nbytes = touched * w13_bytes(cfg) + T * cfg.H * ab + T * cfg.k * cfg.F * ab
-    flops = 2 * T * cfg.k * 2 * cfg.F * cfg.H
-    return nbytes, flops
+    """Algorithmic work of one grouped GEMM1 launch: the w13 bytes of the
+    experts touched (scales included) and the FLOPs 2 * T * k * 2F * H
+    (padding rows not counted)."""
+    return touched * w13_bytes(cfg), 2 * T * cfg.k * 2 * cfg.F * cfg.H
 
 
 def layer_flops(cfg, T):
     return 6 * T * cfg.k * cfg.H * cfg.F
 
 
-def touched_experts(cfg, T):
-    """Expected distinct experts touched by T tokens under uniform routing,
-    E (1 - (1 - k/E)^T) ([MoE] "How many experts does a batch touch?")."""
-    return cfg.E * (1 - (1 - cfg.k / cfg.E) ** T)
+def touched_experts(moe, torch, cfg, W, x):
+    ids, _ = moe.route(x, W["gate"], W["bias"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
+                       cfg.renormalize, cfg.routed_scale)
+    return int(torch.unique(ids).numel())
 
 
 def kernel_source_hash():
@@ -88,13 +103,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(cfg, T):
     """HBM bytes per GEMM1 launch from the committed rocprofv3 counter
     summary, or None if absent or taken on another version of the kernel."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(cfg, T)
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -107,98 +123,192 @@ def measured_traffic():
         return None
 
 
+def pct(ts, q):
+    s = sorted(ts)
+    i = min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))
+    return s[i]
+
+
+def summary(ts):
+    return {"median": round(statistics.median(ts), 2), "p10": round(pct(ts, 0.1), 2),
+            "p90": round(pct(ts, 0.9), 2), "n": len(ts)}
+
+
 # ---------------------------------------------------------------- GPU parts
-def make_problem(cfg, T, device="cuda"):
-    from synth import make_weights, make_x
-    W = make_weights(cfg, device)
-    x = make_x(cfg, T, device)
-    return W, x
+class Flush:
+    """A read of 1 GiB: evicts the L2s and the 256 MB last-level cache
+    without leaving dirty lines (a write would, and their write-back would
+    overlap the timed work)."""
+
+    def __init__(self, moe, torch):
+        self.moe = moe
+        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        self.sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(1 << 30)), dtype=torch.float32,
+                                device="cuda")
+
+    def __call__(self):
+        self.moe.probe_read(self.buf, self.sink)
 
 
-class Step:
-    """The hot path as its constituent calls, with preallocated buffers."""
+def cold_times(torch, flush, fn, reps):
+    """Event-pair time (us) around fn() on the current stream, each after a
+    flush; the events also hold the launch of the first kernel and the
+    completion of the last (about 2-4 us more than the kernel span)."""
+    fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        flush()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) * 1000.0)
+    return out
+
+
+class LayerGraph:
+    """moe_layer on preallocated buffers, captured once in a HIP graph."""
+
+    def __init__(self, moe, torch, cfg, W, x, block_m=0):
+        self.moe, self.torch, self.cfg, self.W, self.x = moe, torch, cfg, W, x
+        T = x.shape[0]
+        self.bm = block_m or moe.layer_block_m(T, cfg.k, cfg.E, cfg.F, cfg.wformat)
+        self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=x.device)
+        self.ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, self.bm, cfg.wformat, 0),
+                              dtype=torch.uint8, device=x.device)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.eager()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.eager()
+        torch.cuda.synchronize()
+
+    def eager(self):
+        c, W = self.cfg, self.W
+        self.moe.layer(self.x, W["gate"], W["bias"], W["w13"], W["w2"], c.k, c.scoring, c.n_group, c.topk_group,
+                       c.renormalize, c.routed_scale, wformat=c.wformat, w13_scale=W["w13_scale"],
+                       w2_scale=W["w2_scale"], block_m=self.bm, ws=self.ws, out=self.y)
+
+    def replay(self):
+        self.graph.replay()
+
+    def warm_ms(self, warmup, steps):
+        """Mean time of `steps` back-to-back replays after `warmup` more."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+
+class Staged:
+    """The hot path through moe_route, moe_align and moe_expert_ffn_stages,
+    so that HIP events on the launch stream bracket GEMM1 alone."""
 
     def __init__(self, moe, torch, cfg, W, x, block_m):
         self.moe, self.torch, self.cfg, self.W, self.x, self.bm = moe, torch, cfg, W, x, block_m
         T = x.shape[0]
-        dev = x.device
-        self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=x.device)
+        fmt = {"bf16": 0, "fp8": 1, "mxfp4": 2}[cfg.wformat]
         need = max(moe.lib().moe_route_workspace_size(T, cfg.H, cfg.E),
                    moe.lib().moe_align_workspace_size(T, cfg.k, cfg.E),
-                   moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, block_m,
-                                                           {"bf16": 0, "fp8": 1, "mxfp4": 2}[cfg.wformat]))
-        self.ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-
-    def route_align(self):
-        c, W = self.cfg, self.W
-        self.ids, self.w = self.moe.route(self.x, W["gate"], W["bias"], c.k, c.scoring, c.n_group, c.topk_group,
-                                          c.renormalize, c.routed_scale, ws=self.ws)
-        self.sid, self.bexp, self.npp = self.moe.align(self.ids, c.E, self.bm, ws=self.ws)
-
-    def ffn(self, stages):
-        W = self.W
-        self.moe.expert_ffn(self.x, W["w13"], W["w2"], self.ids, self.w, self.sid, self.bexp, self.npp, self.bm,
-                            wformat=self.cfg.wformat, w13_scale=W["w13_scale"], w2_scale=W["w2_scale"],
-                            ws=self.ws, stages=stages, out=self.y)
+                   moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, block_m, fmt))
+        self.ws = torch.zeros(need, dtype=torch.uint8, device=x.device)
 
     def __call__(self, ev=None):
-        self.route_align()
-        self.ffn(("quant",))
+        c, W, moe = self.cfg, self.W, self.moe
+        ids, w = moe.route(self.x, W["gate"], W["bias"], c.k, c.scoring, c.n_group, c.topk_group, c.renormalize,
+                           c.routed_scale, ws=self.ws)
+        sid, bexp, npp = moe.align(ids, c.E, self.bm, ws=self.ws)
+        kw = dict(wformat=c.wformat, w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], ws=self.ws, out=self.y)
+        args = (self.x, W["w13"], W["w2"], ids, w, sid, bexp, npp, self.bm)
+        moe.expert_ffn(*args, stages=("quant",), **kw)
         if ev is not None:
             ev[0].record()
-        self.ffn(("gemm1",))
+        moe.expert_ffn(*args, stages=("gemm1",), **kw)
         if ev is not None:
             ev[1].record()
-        self.ffn(("gemm2", "combine"))
+        moe.expert_ffn(*args, stages=("gemm2", "combine"), **kw)
 
-
-class ColdTimer:
-    """GPU time of fn() with cold caches: each sample is preceded by a read of
-    1 GiB (it evicts the L2s and the 256 MB last-level cache; a write would
-    leave dirty lines whose write-back then overlaps the timed work), and is
-    the event-pair time around fn() minus the median event-pair time around
-    nothing measured the same way (the event overhead, about 4 us)."""
-
-    def __init__(self, moe, torch):
-        self.moe, self.torch = moe, torch
-        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-        self.sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(1 << 30)), dtype=torch.float32,
-                                device="cuda")
-        self.base = None
-
-    def raw(self, fn, reps):
+    def gemm1_us(self, steps):
         torch = self.torch
-        ts = []
-        for _ in range(reps):
-            self.moe.probe_read(self.buf, self.sink)
-            s = torch.cuda.Event(enable_timing=True)
-            e = torch.cuda.Event(enable_timing=True)
-            s.record()
-            fn()
-            e.record()
-            torch.cuda.synchronize()
-            ts.append(s.elapsed_time(e) * 1000.0)
-        return statistics.median(ts)
-
-    def __call__(self, fn, reps=20):
-        if self.base is None:
-            self.base = self.raw(lambda: None, 30)
-        fn()
-        self.torch.cuda.synchronize()
-        return max(self.raw(fn, reps) - self.base, 0.01)
+        for _ in range(GEMM1_WARMUP):
+            self()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self(evs[i])
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) * 1000.0 for s, e in evs]
 
 
-DECODE_CASES = (("qwen3", 1), ("qwen3", 64), ("glm", 1), ("glm", 8), ("dsv3", 1), ("dsv4", 512))
+def roofline_entry(cfg, T, touched, us, traffic=None):
+    nbytes, flops = gemm1_work(cfg, T, touched)
+    peak_f = MFMA_PEAK[cfg.wformat]
+    t_hbm, t_mfma = nbytes / HBM_PEAK, flops / peak_f
+    sec = us * 1e-6
+    if t_hbm >= t_mfma:
+        bound, achieved, peak, unit = "hbm", nbytes / sec / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / sec / 1e12, peak_f / 1e12, "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": "grouped GEMM1 + SwiGLU", "kernel_us": round(us, 2), "mfma_issued": MFMA_ISSUED[cfg.wformat],
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "mfma_frac": round(flops / sec / peak_f, 4), "hbm_frac": round(nbytes / sec / HBM_PEAK, 4)}
 
 
-def decode_sweep(moe, torch, timer, qwen3_weights):
-    """Cold moe_layer at decode sizes: us per layer and the HBM rate on the
-    weights of the experts actually touched (distinct experts x expert bytes,
-    scales included)."""
+def headline(moe, torch, cfg, T, args, flush):
+    from synth import make_weights, make_x
+    W = make_weights(cfg, "cuda")
+    x = make_x(cfg, T, "cuda")
+    touched = touched_experts(moe, torch, cfg, W, x)
+    bm = moe.layer_block_m(T, cfg.k, cfg.E, cfg.F, cfg.wformat)
+
+    # GEMM1's launch time: a staged loop after a fixed warm-up of its own
+    st = Staged(moe, torch, cfg, W, x, bm)
+    g1 = st.gemm1_us(20)
+    g1_us = statistics.mean(g1)
+    del st
+
+    # the timed region: W untimed replays, then exactly K, back to back
+    lg = LayerGraph(moe, torch, cfg, W, x, bm)
+    ms = lg.warm_ms(args.warmup, args.steps)
+    span = cold_times(torch, flush, lg.replay, args.reps)
+    roof = roofline_entry(cfg, T, touched, g1_us, measured_traffic(cfg, T))
+    log(f"headline {cfg.name} T={T}: {ms:.3f} ms per step (warm replays), cold median {statistics.median(span):.1f} us, "
+        f"GEMM1 {g1_us:.1f} us ({roof['frac']:.3f} of {roof['bound']} peak)")
+    sec = ms * 1e-3
+    wbytes = touched * cfg.expert_bytes()
+    res = {"ms_per_step": ms, "span": summary(span), "touched": touched, "block_m": bm, "roofline": roof,
+           "gemm1_us": summary(g1),
+           "layer_mfma_frac": round(layer_flops(cfg, T) / sec / MFMA_PEAK[cfg.wformat], 4),
+           "layer_hbm_frac": round(wbytes / sec / HBM_PEAK, 4), "weight_bytes": wbytes}
+    return res, W, x, lg
+
+
+DECODE = (("toy", 16), ("qwen3", 1), ("qwen3", 64), ("glm", 1), ("glm", 8), ("dsv3", 1), ("dsv3", 256),
+          ("dsv4", 512))
+PREFILL = (("qwen3", 4096), ("glm", 512), ("dsv3", 2048))
+
+
+def layer_sweep(moe, torch, flush, cases, reps, warm, keep=None):
+    """Cold (and for prefill warm) graph replays of moe_layer per case."""
     from synth import get_config, make_weights, make_x
     out = {}
-    cache = {"qwen3": qwen3_weights} if qwen3_weights is not None else {}
-    for name, T in DECODE_CASES:
+    cache = dict(keep or {})
+    for name, T in cases:
         cfg = get_config(name)
         if name not in cache:
             cache.clear()
@@ -206,29 +316,59 @@ def decode_sweep(moe, torch, timer, qwen3_weights):
             cache[name] = make_weights(cfg, "cuda")
         W = cache[name]
         x = make_x(cfg, T, "cuda")
-        y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
-        ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, 0, cfg.wformat, 0),
-                         dtype=torch.uint8, device="cuda")
-        def call():
-            moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group,
-                      cfg.topk_group, cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat,
-                      w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], ws=ws, out=y)
-
-        us = timer(call)
-        r_ids, _ = moe.route(x, W["gate"], W["bias"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
-                             cfg.renormalize, cfg.routed_scale)
-        touched = int(torch.unique(r_ids).numel())
-        nbytes = touched * expert_bytes(cfg)
+        lg = LayerGraph(moe, torch, cfg, W, x)
+        ts = cold_times(torch, flush, lg.replay, reps)
+        touched = touched_experts(moe, torch, cfg, W, x)
+        wbytes = touched * cfg.expert_bytes()
+        us = statistics.median(ts)
+        r = {"us_per_layer": summary(ts), "tokens_per_s": round(T / (us * 1e-6), 1), "block_m": lg.bm,
+             "experts_touched": touched, "weight_bytes": wbytes, "weights": cfg.wformat,
+             "hbm_TBps": round(wbytes / (us * 1e-6) / 1e12, 3), "hbm_frac": round(wbytes / (us * 1e-6) / HBM_PEAK, 4)}
+        if warm:
+            ms = lg.warm_ms(10, 20)
+            r["warm_us_per_layer"] = round(ms * 1e3, 2)
+            r["warm_tokens_per_s"] = round(T / (ms * 1e-3), 1)
+            r["mfma_frac_warm"] = round(layer_flops(cfg, T) / (ms * 1e-3) / MFMA_PEAK[cfg.wformat], 4)
+            r["hbm_frac_warm"] = round(wbytes / (ms * 1e-3) / HBM_PEAK, 4)
+            r["mfma_issued"] = MFMA_ISSUED[cfg.wformat]
         key = f"{name}_T{T}"
-        out[key] = {"us_per_layer": round(us, 2), "experts_touched": touched, "weight_bytes": nbytes,
-                    "weights": cfg.wformat, "hbm_TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
-                    "hbm_frac": round(nbytes / (us * 1e-6) / HBM_PEAK, 4),
-                    "tokens_per_s": round(T / (us * 1e-6), 1)}
-        log(f"decode {key}: {us:.1f} us/layer, {touched} experts, {out[key]['hbm_TBps']} TB/s "
-            f"({out[key]['hbm_frac']:.3f} of peak)")
+        out[key] = r
+        log(f"{key}: cold {r['us_per_layer']} us, {touched} experts, {r['hbm_TBps']} TB/s ({r['hbm_frac']:.3f} of HBM)"
+            + (f"; warm {r['warm_us_per_layer']} us, MFMA {r['mfma_frac_warm']:.3f}" if warm else ""))
+        del lg
     cache.clear()
     torch.cuda.empty_cache()
     return out
+
+
+ROUTER = (("toy", 1), ("qwen3", 1), ("glm", 1), ("glm", 8), ("glm", 512), ("dsv3", 1), ("dsv4", 1))
+
+
+def router_probe(moe, torch, flush, reps):
+    """moe_route alone next to the bare read of its gate weight
+    (moe_probe_read, the same bytes) and an empty kernel, all cold; raw
+    event-pair times (each holds the same few us of event overhead)."""
+    from synth import get_config, make_router_weights, make_x
+    empty = cold_times(torch, flush, lambda: moe.probe_empty(), reps)
+    res = {"empty_kernel_us": summary(empty)}
+    for name, T in ROUTER:
+        cfg = get_config(name)
+        gate, bias = make_router_weights(cfg, "cuda")
+        x = make_x(cfg, T, "cuda")
+        ids = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(moe.lib().moe_route_workspace_size(T, cfg.H, cfg.E), dtype=torch.uint8, device="cuda")
+        sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(gate.numel() * 4)), dtype=torch.float32,
+                           device="cuda")
+        r = cold_times(torch, flush, lambda: moe.route(x, gate, bias, cfg.k, cfg.scoring, cfg.n_group,
+                                                        cfg.topk_group, cfg.renormalize, cfg.routed_scale, ws=ws),
+                       reps)
+        b = cold_times(torch, flush, lambda: moe.probe_read(gate, sink), reps)
+        rm, bm_ = statistics.median(r), statistics.median(b)
+        res[f"{name}_T{T}"] = {"route_us": summary(r), "bare_gate_read_us": summary(b), "gate_bytes": gate.numel() * 4,
+                               "ratio": round(rm / bm_, 3)}
+        log(f"router {name} T={T}: {rm:.2f} us vs bare read {bm_:.2f} us (x{rm / bm_:.2f})")
+        del ids
+    return res
 
 
 # One GPU's share of DeepSeek-V4 expert parallelism over 8 GPUs: 32 local
@@ -238,7 +378,7 @@ EP_SHARE_T = (1, 4, 16, 64, 512)
 EP_SHARE_PAGE_US = {1: 40.0, 4: 68.0, 16: 95.0, 64: 99.0, 512: 112.0}  # B300, the page's figures
 
 
-def ep_share_sweep(moe, torch, timer):
+def ep_share_sweep(moe, torch, flush, reps):
     """Cold alignment + expert FFN (fp8 quantisation, both grouped GEMMs and
     the combine) for 32 MXFP4 experts, k = 6, at the page's token counts."""
     from synth import get_config, make_topk_ids, make_weights, make_x
@@ -253,87 +393,81 @@ def ep_share_sweep(moe, torch, timer):
         w = (w / w.sum(dim=1, keepdim=True)).to("cuda")
         bm = moe.layer_block_m(T, cfg.k, cfg.E, cfg.F, cfg.wformat)
         y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device="cuda")
-        fmt = 2
-        ws = torch.zeros(max(moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, bm, fmt),
+        ws = torch.zeros(max(moe.lib().moe_expert_ffn_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, bm, 2),
                              moe.lib().moe_align_workspace_size(T, cfg.k, cfg.E)), dtype=torch.uint8, device="cuda")
         holder = {}
 
-        def align():
-            holder["a"] = moe.align(ids, cfg.E, bm, ws=ws)
-
-        def ffn():
-            s_, b_, n_ = holder["a"]
+        def both():
+            holder["a"] = s_, b_, n_ = moe.align(ids, cfg.E, bm, ws=ws)
             moe.expert_ffn(x, W["w13"], W["w2"], ids, w, s_, b_, n_, bm, wformat=cfg.wformat,
                            w13_scale=W["w13_scale"], w2_scale=W["w2_scale"], ws=ws, out=y)
 
-        def both():
-            align()
-            ffn()
-
-        us = timer(both)
-        align()
-        us_ffn = timer(ffn)
+        ts = cold_times(torch, flush, both, reps)
+        us = statistics.median(ts)
         touched = int(torch.unique(ids).numel())
-        nbytes = touched * expert_bytes(cfg)
-        out[f"T{T}"] = {"us_align_ffn": round(us, 2), "us_ffn": round(us_ffn, 2), "block_m": bm,
-                        "experts_touched": touched, "weight_bytes": nbytes,
-                        "hbm_TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
+        nbytes = touched * cfg.expert_bytes()
+        out[f"T{T}"] = {"us_align_ffn": summary(ts), "block_m": bm, "experts_touched": touched,
+                        "weight_bytes": nbytes, "hbm_TBps": round(nbytes / (us * 1e-6) / 1e12, 3),
                         "page_b300_us": EP_SHARE_PAGE_US[T]}
-        log(f"EP share (32 MXFP4 experts, k=6) T={T}: {us:.1f} us (FFN alone {us_ffn:.1f}), {touched} experts, "
+        log(f"EP share (32 MXFP4 experts, k=6) T={T}: {us:.1f} us, {touched} experts, "
             f"{out[f'T{T}']['hbm_TBps']} TB/s; the page's B300 figure {EP_SHARE_PAGE_US[T]:.0f} us")
     del W
     torch.cuda.empty_cache()
     return out
 
 
-def router_probe(moe, torch, timer):
-    """moe_route alone at T = 1 next to the bare read of its gate weight
-    (moe_probe_read, the same bytes) and an empty kernel, all cold."""
-    from synth import get_config, make_router_weights, make_x
-    res = {"empty_kernel_us": round(timer(lambda: moe.probe_empty()), 2)}
-    for name in ("glm", "qwen3", "dsv3"):
-        cfg = get_config(name)
-        gate, bias = make_router_weights(cfg, "cuda")
-        x = make_x(cfg, 1, "cuda")
-        ws = torch.zeros(moe.lib().moe_route_workspace_size(1, cfg.H, cfg.E), dtype=torch.uint8, device="cuda")
-        sink = torch.empty(int(moe.lib().moe_probe_read_sink_len(gate.numel() * 4)), dtype=torch.float32,
-                           device="cuda")
-        r_us = timer(lambda: moe.route(x, gate, bias, cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
-                                       cfg.renormalize, cfg.routed_scale, ws=ws))
-        b_us = timer(lambda: moe.probe_read(gate, sink))
-        res[name] = {"route_us_T1": round(r_us, 2), "bare_gate_read_us": round(b_us, 2),
-                     "gate_bytes": gate.numel() * 4, "ratio": round(r_us / b_us, 3)}
-        log(f"router {name}: {r_us:.2f} us vs bare read {b_us:.2f} us")
-    return res
-
-
 # ---------------------------------------------------------------- CPU oracle
-def cpu_baseline(cfg, W, x, n_sample):
+def cpu_baseline(moe, torch, cfg, W, x, n_sample):
     """The oracle as it stands on a bounded sample of the same workload:
-    route + dense-equivalent layer for the first n_sample tokens."""
+    route + dense-equivalent layer for the first n_sample tokens, with its
+    expert loop on the host's threads.  Also, on all T tokens, the routing
+    near-tie report: tokens whose oracle margin at the cut (or between kept
+    and dropped groups) is at most 1e-5, and how many of them the GPU routes
+    to other experts."""
     import numpy as np
     from oracle import ffn as offn
     from oracle import router as orouter
     from synth import to_numpy
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, threads))
     xs = to_numpy(x[:n_sample])
     gate, bias = to_numpy(W["gate"]), to_numpy(W["bias"])
-    Wn = offn.ExpertWeights(cfg.wformat, to_numpy(W["w13"]), to_numpy(W["w2"]),
-                            to_numpy(W["w13_scale"]), to_numpy(W["w2_scale"]))
+
+    class Lazy:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            return to_numpy(self.t[e])
+
+    Wn = offn.ExpertWeights(cfg.wformat, Lazy(W["w13"]), Lazy(W["w2"]),
+                            None if W["w13_scale"] is None else Lazy(W["w13_scale"]),
+                            None if W["w2_scale"] is None else Lazy(W["w2_scale"]))
     t0 = time.perf_counter()
     r = orouter.route(xs, gate, bias, cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group, cfg.renormalize,
                       cfg.routed_scale)
-    y, _ = offn.layer(xs, r, Wn, cfg.E)
+    y, _ = offn.layer(xs, r, Wn, cfg.E, workers=workers)
     dt = time.perf_counter() - t0
     assert np.all(np.isfinite(y))
-    return {"value": round(n_sample / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"first {n_sample} of the {x.shape[0]} tokens" if n_sample < x.shape[0] else
-                       f"all {n_sample} tokens") + f" (router + float64 dense-equivalent layer), {dt:.1f} s",
+    T = x.shape[0]
+    base = {"value": round(n_sample / dt, 3), "unit": "tokens/s", "cores": int(workers), "kind": "oracle",
+            "sample": (f"first {n_sample} of the {T} tokens" if n_sample < T else f"all {T} tokens")
+            + f" (router + float64 dense-equivalent layer, expert loop on {workers} threads), {dt:.1f} s",
             "seconds": round(dt, 2)}
+    # near ties on every token
+    ids, _ = moe.route(x, W["gate"], W["bias"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group, cfg.renormalize,
+                       cfg.routed_scale)
+    torch.cuda.synchronize()
+    rf = orouter.route(to_numpy(x), gate, bias, cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group, cfg.renormalize,
+                       cfg.routed_scale)
+    near = ~((rf["margin"] > 1e-5) & (rf["group_margin"] > 1e-5))
+    gi = ids.cpu().numpy()
+    differ = int(np.sum(np.any(gi[near] != rf["ids"][near], axis=1)))
+    clear_differ = int(np.sum(np.any(gi[~near] != rf["ids"][~near], axis=1)))
+    ties = {"tokens": T, "near_tie_tokens": int(near.sum()), "near_tie_tokens_routed_differently": differ,
+            "near_tie_mismatch_rate": round(differ / max(1, int(near.sum())), 4),
+            "clear_tokens_routed_differently": clear_differ, "margin": 1e-5}
+    return base, ties
 
 
 # ---------------------------------------------------------------- main
@@ -341,127 +475,77 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--T", type=int, default=4096)
-    ap.add_argument("--config", default="qwen3")
-    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: all T)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--reps", type=int, default=30, help="cold replays per case")
+    ap.add_argument("--T", type=int, default=8192)
+    ap.add_argument("--config", default="dsv4")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: T / 4)")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the decode sweep and router probes")
-    ap.add_argument("--decode-only", action="store_true",
-                    help="diagnostic: only the cold decode cases (for kernel traces), no benchmark line")
-    ap.add_argument("--ep-share-only", action="store_true",
-                    help="diagnostic: only the 32-expert DeepSeek-V4 share cases, no benchmark line")
+    ap.add_argument("--no-extras", action="store_true", help="skip the decode, prefill, router and EP-share rows")
+    ap.add_argument("--only", choices=("decode", "prefill", "router", "ep"),
+                    help="diagnostic: only these rows (for kernel traces), no benchmark line")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first write MIB MiB with a fill kernel and read them once with moe_probe_read "
                          "(kernels of known traffic that calibrate rocprofv3 WRITE_SIZE / FETCH_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every expert is local to the "
-              "one GPU). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the layer keeps every expert on the one GPU and has no multi-GPU path. "
+              "Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
     import mixture_experts_layer_04_amd as moe
     from synth import get_config
 
-    cfg = get_config(args.config)
-    T = args.T
-    if args.decode_only:
-        timer = ColdTimer(moe, torch)
-        for key, v in decode_sweep(moe, torch, timer, None).items():
-            log(f"{key}: {v}")
-        return 0
-    if args.ep_share_only:
-        timer = ColdTimer(moe, torch)
-        for key, v in ep_share_sweep(moe, torch, timer).items():
+    flush = Flush(moe, torch)
+    if args.only:
+        rows = {"decode": lambda: layer_sweep(moe, torch, flush, DECODE, args.reps, False),
+                "prefill": lambda: layer_sweep(moe, torch, flush, PREFILL, args.reps, True),
+                "router": lambda: router_probe(moe, torch, flush, args.reps),
+                "ep": lambda: ep_share_sweep(moe, torch, flush, args.reps)}[args.only]()
+        for key, v in rows.items():
             log(f"{key}: {v}")
         return 0
     if args.copy_probe:
-        # kernels of known traffic for the counter calibration: a fill that
-        # writes MIB MiB and moe_probe_read reading them once
         buf = torch.zeros(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
         moe.probe_read(buf)
         torch.cuda.synchronize()
         del buf
+
+    cfg = get_config(args.config)
+    T = args.T
     log(f"bench: {cfg.description}, T={T}")
-    W, x = make_problem(cfg, T)
-    bm = moe.layer_block_m(T, cfg.k, cfg.E, cfg.F, cfg.wformat)
-    step = Step(moe, torch, cfg, W, x, bm)
-    y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=x.device)
-    ws = torch.zeros(moe.layer_workspace_size(T, cfg.H, cfg.E, cfg.F, cfg.k, bm, cfg.wformat, 0),
-                     dtype=torch.uint8, device=x.device)
-
-    def layer_step():
-        moe.layer(x, W["gate"], W["bias"], W["w13"], W["w2"], cfg.k, cfg.scoring, cfg.n_group, cfg.topk_group,
-                  cfg.renormalize, cfg.routed_scale, wformat=cfg.wformat, w13_scale=W["w13_scale"],
-                  w2_scale=W["w2_scale"], block_m=bm, ws=ws, out=y)
-
-    # GEMM1's launch time first: K steps through the stage entry points
-    # (after W of them), HIP events around GEMM1 on the launch stream.  The
-    # first ~25 steps after setup run about 15 % slower (measured), so this
-    # loop also brings the GPU to its steady state before the timed region.
-    for _ in range(args.warmup):
-        step()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    s0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    staged_ms = (time.perf_counter() - s0) / args.steps * 1e3
-    g1_us = statistics.mean(s.elapsed_time(e) for s, e in evs) * 1000.0
-
-    # the timed region: W untimed moe_layer steps, then exactly K
-    for _ in range(args.warmup):
-        layer_step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        layer_step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) / args.steps * 1e3
-
-    touched = int(torch.unique(step.ids).numel())
-    g1_bytes, g1_flops = gemm1_work(cfg, T, touched)
-    t_hbm, t_mfma = g1_bytes / HBM_PEAK, g1_flops / MFMA_PEAK[cfg.wformat]
-    bound = "hbm" if t_hbm >= t_mfma else "mfma"
-    if bound == "hbm":
-        achieved, peak, unit = g1_bytes / (g1_us * 1e-6) / 1e9, HBM_PEAK / 1e9, "GB/s"
-    else:
-        achieved, peak, unit = g1_flops / (g1_us * 1e-6) / 1e12, MFMA_PEAK[cfg.wformat] / 1e12, "TFLOP/s"
-    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
-            "kernel": "grouped GEMM1 + SwiGLU (" + ("gemm_stream" if bm == 16 else "gemm_pair_bf16"
-                                                   if bm == 128 and cfg.wformat == "bf16" else "gemm_tiled") + ")",
-            "kernel_us": round(g1_us, 2), "algorithmic_bytes": g1_bytes, "algorithmic_flops": g1_flops,
-            "mfma_frac": round(g1_flops / (g1_us * 1e-6) / MFMA_PEAK[cfg.wformat], 4),
-            "hbm_frac": round(g1_bytes / (g1_us * 1e-6) / HBM_PEAK, 4)}
-    log(f"step {ms:.3f} ms (staged calls {staged_ms:.3f} ms), GEMM1 {g1_us:.1f} us ({roof['frac']:.3f} of {bound} peak)")
-
+    h, W, x, lg = headline(moe, torch, cfg, T, args, flush)
+    ms = h["ms_per_step"]
     result = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{cfg.description}, T={T}", "T": T, "H": cfg.H,
-                   "E": cfg.E, "k": cfg.k, "F": cfg.F, "block_m": bm, "weights": cfg.wformat,
-                   "experts_touched": touched},
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[cfg.wformat], "data": "synthetic",
+        "config": {"workload": f"{cfg.description}, T={T}", "T": T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "F": cfg.F, "block_m": h["block_m"], "weights": cfg.wformat, "experts_touched": h["touched"],
+                   "step": "one HIP-graph replay of moe_layer (router, alignment, GEMM1 + SwiGLU, GEMM2, combine)"},
         "us_per_layer": round(ms * 1e3, 2),
-        "staged_ms_per_step": round(staged_ms, 4),
-        "layer_mfma_frac": round(layer_flops(cfg, T) / (ms * 1e-3) / MFMA_PEAK[cfg.wformat], 4),
-        "roofline": roof,
+        "span_cold_us": h["span"],
+        "layer_mfma_frac": h["layer_mfma_frac"], "layer_hbm_frac": h["layer_hbm_frac"],
+        "mfma_issued": MFMA_ISSUED[cfg.wformat],
+        "roofline": h["roofline"],
+        "gemm1_event_us": h["gemm1_us"],
     }
-    if not args.no_extras:
-        timer = ColdTimer(moe, torch)
-        result["router"] = router_probe(moe, torch, timer)
-        result["decode"] = decode_sweep(moe, torch, timer, W if cfg.name == "qwen3" else None)
-        result["ep_share_dsv4_32_experts"] = ep_share_sweep(moe, torch, timer)
-        result["cold_timing"] = ("median event-pair time after a 1 GiB read, minus the empty event-pair "
-                                 f"time ({timer.base:.2f} us)")
-        del timer
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(cfg, W, x, args.cpu_sample if args.cpu_sample > 0 else T)
-        log(f"cpu oracle: {result['cpu_baseline']['value']} tokens/s on {result['cpu_baseline']['cores']} threads")
+        n = args.cpu_sample if args.cpu_sample > 0 else max(1, T // 4)
+        base, ties = cpu_baseline(moe, torch, cfg, W, x, n)
+        result["cpu_baseline"] = base
+        result["routing_near_ties"] = ties
+        log(f"cpu oracle: {base['value']} tokens/s on {base['cores']} threads; near ties {ties}")
+    del lg, W, x
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        result["decode"] = layer_sweep(moe, torch, flush, DECODE, args.reps, False)
+        result["prefill"] = layer_sweep(moe, torch, flush, PREFILL, max(10, args.reps // 3), True)
+        result["router"] = router_probe(moe, torch, flush, args.reps)
+        result["ep_share_dsv4_32_experts"] = ep_share_sweep(moe, torch, flush, args.reps)
+        result["cold_timing"] = ("each replay after a 1 GiB read; raw event-pair time around it (median, p10, p90), "
+                                 "which includes the first kernel's launch and the last one's completion")
     print(json.dumps(result), flush=True)
     return 0
 

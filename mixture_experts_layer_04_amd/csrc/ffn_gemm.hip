@@ -996,6 +996,258 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
 }
 
 // ---------------------------------------------------------------------------
+// Paired tiled kernel for MXFP4 weights (BLOCK_M = 64 or 128, prefill): the
+// tile of gemm_pair_bf16 (up to two consecutive blocks of one expert x 256
+// weight rows; 8 waves as 2 x 4, each one block's rows x 64 weight rows) on
+// e4m3 activations x e2m1 weights.  Each weight tile is copied once for
+// both blocks, and a K step moves 2.98 bytes per kFLOP instead of the 3.99
+// of a BLOCK_M x 256 tile.  A K step is one 128-wide MFMA step: 128 bytes of
+// each A row, 64 bytes of each weight row and one 4-byte word of e8m0
+// scales (four 32-wide K groups) per row of either.  One ring of three
+// slots, two steps ahead; a slot holds a step's A rows, weight rows and
+// scale words (50 KiB at BB = 128).  GEMM1's epilogue requantises each row's
+// 32 SwiGLU columns of a wave (one MX group) with the power-of-two scale
+// pow2_at_least(amax / 448) ([MegaMoE] §3.5).
+template <bool G1, int BB>  // BB: rows per block (64 or 128)
+__global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
+  constexpr int NW = 8, NT = 64 * NW, WN = NW / 2;
+  constexpr int BMT = 2 * BB;          // rows per tile
+  constexpr int BNW = 256;             // weight rows per tile
+  constexpr int ARB = 128, BRB = 64;   // A / B bytes per row and step
+  constexpr int ASZ = BMT * ARB;
+  constexpr int BSZ = BNW * BRB;
+  constexpr int SCSZ = NT * 4;         // one scale word per thread: A rows, then B rows
+  constexpr int SSZ = ASZ + BSZ + SCSZ;
+  constexpr int NS = 3, D = NS - 1;
+  constexpr int FM = BB / 16;          // 16-row fragments per wave (one block's rows)
+  constexpr int FN = BNW / WN / 16;    // 16-column fragments per wave
+  constexpr int RW = BMT / NW;         // A rows each wave copies
+  constexpr int RWB = BNW / NW;        // weight rows each wave copies
+  constexpr int LA = RW / 8;           // 1 KiB copies per wave per step: 8 A rows of 128 bytes
+  constexpr int LB = RWB / 16;         //                                16 weight rows of 64 bytes
+  constexpr int LS = LA + LB + 1;      // + the scale word
+  static_assert(BMT + BNW <= NT && NS * SSZ <= 163840 && LA >= 1 && LB >= 1 && FN % 2 == 0 &&
+                LS * (D - 1) <= 63, "tile, ring, scale words and vmcnt");
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave / WN;  // rows [BB wm, +BB): the tile's first or second block
+  const int wn = wave % WN;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int K = G1 ? p.H : p.F;
+  const int N = G1 ? p.F : p.H;
+  const int BNO = G1 ? BNW / 2 : BNW;  // output columns per tile
+  const int ntn = N / BNO;
+  const int nblk = *p.npp / BB;
+  // a pair table left by another shape holds more pairs than blocks exist:
+  // at most one pair per block, and tiles past the blocks are skipped
+  const int npairs = min(p.pairs[0], nblk);
+  const int64_t n_valid = (int64_t)npairs * ntn;
+  const int64_t per = (n_valid + 7) >> 3;
+  const int nk = K / 128;
+  const int rowbytes_a = K;       // e4m3
+  const int rowbytes_b = K / 2;   // packed e2m1
+  const int kgroups = K / 32;     // e8m0 scale bytes per row
+  const uint8_t* asrc = G1 ? p.x : p.act;
+  const uint8_t* wsrc = G1 ? p.w13 : p.w2;
+  const uint8_t* ascale = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s);
+  const uint8_t* wscale = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s);
+  const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
+  const rsrc_t ra = make_rsrc(asrc, (uint64_t)(G1 ? p.A / p.k : nblk * BB) * rowbytes_a);
+  const rsrc_t rnone = make_rsrc(asrc, 0);  // every read returns zero
+
+  // LDS chunk slots: A rows of 128 bytes, chunk c at c ^ (rr / 2 % 8);
+  // weight rows of 64 bytes, chunk c at c ^ (rr / 2 % 4) (a fragment read of
+  // 16 rows then hits no bank twice)
+  auto a_off = [](int rr, int c) { return rr * ARB + 16 * (c ^ ((rr >> 1) & 7)); };
+  auto b_off = [](int rr, int c) { return rr * BRB + 16 * (c ^ ((rr >> 1) & 3)); };
+  // GEMM1: the first FN / 2 fragments are gate rows, the rest the matching up rows
+  auto frag_lrow = [&](int fn) {
+    return G1 ? (fn < FN / 2 ? wn * (BNW / (2 * WN)) + fn * 16 : BNW / 2 + wn * (BNW / (2 * WN)) + (fn - FN / 2) * 16)
+              : wn * (BNW / WN) + fn * 16;
+  };
+  auto weight_row = [&](int nt, int lrow) {
+    if (G1) return lrow < BNW / 2 ? nt * (BNW / 2) + lrow : p.F + nt * (BNW / 2) + (lrow - BNW / 2);
+    return nt * BNW + lrow;
+  };
+
+  // Tiles as gemm_pair_bf16: XCD x owns the contiguous run [x per, +per) of
+  // logical (pair-major) tiles, first tiles by index, then per-XCD queues.
+  const int xcd = blockIdx.x & 7;
+  const int wpx = (int)(gridDim.x >> 3);
+  const bool dyn = per > wpx;
+  int j = (int)(blockIdx.x >> 3);
+  for (;; ) {
+    const int64_t L = (int64_t)xcd * per + j;
+    if (j >= per || L >= n_valid) break;
+    const int pe = __builtin_amdgcn_readfirstlane(p.pairs[1 + (int)(L / ntn)]);
+    const int nt = (int)(L % ntn);
+    const int blk = pe & 0x3FFFFFFF;  // first block of the tile
+    const bool two = (pe >> 30) & 1;
+    if (blk + (two ? 1 : 0) < nblk) {
+      const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
+      const bool mine = wm == 0 || two;  // this wave's block exists
+
+      // A copies: wave w fills tile rows [RW w, +RW), 8 per instruction;
+      // rows of a missing second block come from the empty range
+      const bool copy_rows = wave < NW / 2 || two;
+      const rsrc_t rA = copy_rows ? ra : rnone;
+      uint32_t ag[LA];
+#pragma unroll
+      for (int i = 0; i < LA; ++i) {
+        const int rr = wave * RW + 8 * i + lane / 8;
+        const int c = (lane % 8) ^ ((rr >> 1) & 7);
+        bool v;
+        const int src = copy_rows ? a_row_index<G1>(p, blk, BB, rr, v) : 0;  // padding rows read row 0
+        ag[i] = (uint32_t)src * rowbytes_a + 16 * c;
+      }
+      const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes_b, (uint64_t)erows * rowbytes_b);
+      uint32_t bg[LB];
+#pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        const int rr = wave * RWB + 16 * i + lane / 4;
+        const int c = (lane % 4) ^ ((rr >> 1) & 3);
+        bg[i] = (uint32_t)weight_row(nt, rr) * rowbytes_b + 16 * c;
+      }
+      // scale word of thread q: A row q (q < BMT), weight row q - BMT;
+      // rows of a missing block read the tile's first row
+      const uint8_t* scg;
+      {
+        const int q = tid < BMT + BNW ? tid : 0;
+        if (q < BMT) {
+          bool v;
+          const int row = (q < BB || two) ? q : 0;
+          const int src = a_row_index<G1>(p, blk, BB, row, v);
+          scg = ascale + (size_t)src * kgroups;
+        } else {
+          scg = wscale + ((size_t)e * erows + weight_row(nt, q - BMT)) * kgroups;
+        }
+      }
+      auto issue = [&](int s) {
+        uint8_t* st = lds + (s % NS) * SSZ;
+        s = s < nk ? s : nk - 1;  // past the end: the last step again, into a slot no later step reads
+#pragma unroll
+        for (int i = 0; i < LA; ++i) buf2lds16(rA, ag[i], s * ARB, st + (wave * RW + 8 * i) * ARB);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * BRB, st + ASZ + (wave * RWB + 16 * i) * BRB);
+        g2lds4(scg + 4 * s, st + ASZ + BSZ + wave * 256);
+      };
+
+      f32x4_t acc[FM][FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      issue(0);
+      issue(1);
+      for (int s = 0; s < nk; ++s) {
+        // this wave's reads of the slot about to be refilled are done, its
+        // copies of step s have landed (only step s + 1's may remain), then
+        // the barrier and the copies of step s + 2
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
+        wait_vm<LS * (D - 1)>();
+        barrier_no_fence();
+        issue(s + D);
+        if (mine) {
+          const uint8_t* st = lds + (s % NS) * SSZ;
+          const uint8_t* Ss = st + ASZ + BSZ;
+          i32x8_t bfr[FN];
+          int sb[FN];
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int rr = frag_lrow(fn) + r;
+            const i32x4_t v = *reinterpret_cast<const i32x4_t*>(st + ASZ + b_off(rr, g));
+            bfr[fn] = i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+            sb[fn] = (int)Ss[(BMT + rr) * 4 + g];
+          }
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            const int rr = wm * BB + fm * 16 + r;
+            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + a_off(rr, g));
+            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + a_off(rr, 4 + g));
+            const i32x8_t af = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const int sa = (int)Ss[rr * 4 + g];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_mx(af, bfr[fn], acc[fm][fn], sa, sb[fn]);
+          }
+        }
+      }
+      wait_vm<0>();     // the copies past the last step have landed too
+      __syncthreads();  // every wave is done reading the ring
+
+      // ---------------------------------------------------------------- epilogue
+      const int nrows = two ? BMT : BB;
+      if (G1) {
+        constexpr int BNA = BNW / 2;  // SwiGLU columns per tile
+        uint8_t* acts = static_cast<uint8_t*>(p.act_s);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int lr = wm * BB + fm * 16 + 4 * g + i;
+            const float v0 = swiglu(acc[fm][0][i], acc[fm][FN / 2][i], p.lim);
+            const float v1 = swiglu(acc[fm][1][i], acc[fm][FN / 2 + 1][i], p.lim);
+            // the wave's 32 columns of row lr are one MX group: its amax over
+            // the 16 lanes that hold the row
+            float m = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+            const uint32_t code = mx_group_code(m);
+            const float inv = e8m0_inv(code);
+            if (mine && r == 0) acts[(size_t)(blk * BB + lr) * (p.F / 32) + nt * (BNA / 32) + wn] = (uint8_t)code;
+            lds[lr * BNA + wn * 32 + r] = (uint8_t)to_e4m3(clamp448(v0 * inv));
+            lds[lr * BNA + wn * 32 + 16 + r] = (uint8_t)to_e4m3(clamp448(v1 * inv));
+          }
+        __syncthreads();
+        constexpr int CH = BNA / 16;  // 16-byte chunks per tile row
+        for (int idx = tid; idx < nrows * CH; idx += NT) {
+          const int lr = idx / CH;
+          const int c = idx % CH;
+          const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNA + c * 16);
+          *reinterpret_cast<uint4*>(p.act + (size_t)(blk * BB + lr) * p.F + nt * BNA + c * 16) = val;
+        }
+      } else {
+        uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
+                  (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
+        __syncthreads();
+        constexpr int CH = BNW * 2 / 16;
+        for (int idx = tid; idx < nrows * CH; idx += NT) {
+          const int lr = idx / CH;
+          const int c = idx % CH;
+          const int sid = p.sorted_ids[blk * BB + lr];
+          if (sid >= p.A) continue;
+          const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNW * 2 + c * 16);
+          *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
+        }
+      }
+    }
+    if (!dyn) break;
+    __syncthreads();  // this tile (and the last index read) is done with LDS
+    if (tid == 0) *reinterpret_cast<volatile int*>(lds) = wpx + atomicAdd(p.queue + xcd, 1);
+    __syncthreads();
+    j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(lds));
+    __syncthreads();  // every wave has the index before the copies overwrite it
+  }
+  // the last workgroup to finish leaves the counters at zero for the next
+  // launch (every workgroup has made its last take before it counts itself)
+  if (dyn && tid == 0 && atomicAdd(p.queue + 8, 1) == (int)gridDim.x - 1) {
+#pragma unroll
+    for (int x = 0; x < 9; ++x) p.queue[x] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Stream kernel (BLOCK_M = 16, decode).  A weight element is used by at most
 // the 16 rows of one block, so the kernel is a weight stream: what decides
 // its speed is that every CU gets an even share of the weight bytes and keeps
@@ -1329,6 +1581,16 @@ moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
   return MOE_OK;
 }
 
+template <bool G1, int BB>
+moe_status launch_pair_mx_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
+  constexpr size_t lds = (size_t)3 * ((size_t)2 * BB * 128 + 256 * 64 + 512 * 4);  // 3 slots: A, B, scale words
+  static std::atomic<int> cache[64];
+  const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_mx<G1, BB>), 512, lds, cache);
+  gemm_pair_mx<G1, BB><<<tile_grid(max_tiles, wgs), 512, lds, s>>>(p);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 template <int F>
 moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   GemmP p;
@@ -1392,6 +1654,12 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
           if (a.H % 256 == 0) return launch_pair_one<false, 64>(p, t2 / 2, s);
         }
       }
+      if constexpr (F == F_MX) {
+        if (a.pairs) {
+          if (which == 1) return launch_pair_mx_one<true, 64>(p, t1, s);
+          if (a.H % 256 == 0) return launch_pair_mx_one<false, 64>(p, t2 / 2, s);
+        }
+      }
       if (which == 1) return launch_tiled_one<F, true, 64, 256, (F == F_BF16 ? 4 : 3), NW>(p, t1, s);
       if constexpr (F == F_BF16)
         if (a.H % 256 == 0) return launch_tiled_one<F, false, 64, 256, 3, NW>(p, t2 / 2, s);
@@ -1401,6 +1669,12 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
         if (a.pairs) {
           if (which == 1) return launch_pair_one<true, 128>(p, t1, s);
           if (a.H % 256 == 0) return launch_pair_one<false, 128>(p, t2 / 2, s);
+        }
+      }
+      if constexpr (F == F_MX) {
+        if (a.pairs) {
+          if (which == 1) return launch_pair_mx_one<true, 128>(p, t1, s);
+          if (a.H % 256 == 0) return launch_pair_mx_one<false, 128>(p, t2 / 2, s);
         }
       }
       if (which == 1) return launch_tiled_one<F, true, 128, 256, 3, NW>(p, t1, s);
@@ -1417,7 +1691,7 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
 #define MOE_PAIRED_TILES 1
 #endif
 bool ffn_paired(int wformat, int block_m) {
-  return MOE_PAIRED_TILES && wformat == MOE_W_BF16 && (block_m == 128 || block_m == 64);
+  return MOE_PAIRED_TILES && (wformat == MOE_W_BF16 || wformat == MOE_W_MXFP4) && (block_m == 128 || block_m == 64);
 }
 
 moe_status launch_pair_table(const FfnArgs& a, hipStream_t s) {
