@@ -133,12 +133,44 @@ struct SOp<F_MX> {
   static constexpr int S = 4;
 };
 
-// silu(min(g, lim)) * clamp(u, -lim, lim) ([MegaMoE] §3.5); lim = +inf: no clamp
+// silu(min(g, lim)) * clamp(u, -lim, lim) ([MegaMoE] §3.5); lim = +inf: no
+// clamp.  silu(g) = g / (1 + e^-g) on the hardware exp2 and reciprocal
+// (about 1 ulp each; e^-g overflows to +inf for g < -88, giving -0 * u)
 __device__ __forceinline__ float swiglu(float g, float u, float lim) {
   g = fminf(g, lim);
   u = fminf(fmaxf(u, -lim), lim);
-  return g / (1.f + expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
 }
+
+// Rows of a staged GEMM2 output tile (bf16, CH 16-byte chunks per row, LDS
+// row stride CH * 16) to their assignment slots in out [T*k, H]: thread t
+// stores chunk t % CH of rows t / CH + (NT / CH) i.  load_slots fetches the
+// slots of the thread's rows all at once (one memory latency instead of one
+// per row); call it before staging the tile so that the latency overlaps.
+template <int NT, int CH, int ROWS>
+struct RowScatter {
+  static constexpr int RP = NT / CH;      // rows per pass
+  static constexpr int NP = ROWS / RP;    // passes over ROWS rows
+  static_assert(NT % CH == 0 && ROWS % RP == 0, "whole passes");
+  int sid[NP];
+  __device__ __forceinline__ void load_slots(const GemmP& p, int row0, int nrows, int tid) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int lr = tid / CH + RP * i;
+      sid[i] = lr < nrows ? p.sorted_ids[row0 + lr] : p.A;
+    }
+  }
+  __device__ __forceinline__ void store(const GemmP& p, const uint8_t* st, int col0, int tid) const {
+    const int c = tid % CH;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (sid[i] >= p.A) continue;  // padding, or past the tile's rows
+      const int lr = tid / CH + RP * i;
+      const uint4 val = *reinterpret_cast<const uint4*>(st + lr * CH * 16 + c * 16);
+      *reinterpret_cast<uint4*>(p.out + (size_t)sid[i] * p.H + col0 + c * 8) = val;
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Activation quantisation of x (FP8: per 128, fp32 scale amax/448;
@@ -593,8 +625,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
             float mm = 0.f;
 #pragma unroll
             for (int fa = 0; fa < FA; ++fa) mm = fmaxf(mm, fabsf(v[fm][fa][i]));
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
+            mm = row_max16(mm);  // the 16 lanes (one DPP row) of the row
             if (r == 0) xch[wn * BM + wm * (BM / 2) + fm * 16 + 4 * g + i] = mm;
           }
         __syncthreads();
@@ -622,9 +653,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
             const int lr = wm * (BM / 2) + fm * 16 + 4 * g + i;
 #pragma unroll
             for (int gp = 0; gp < FA / 2; ++gp) {
-              float mm = fmaxf(fabsf(v[fm][2 * gp][i]), fabsf(v[fm][2 * gp + 1][i]));
-#pragma unroll
-              for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, kWave));
+              const float mm = row_max16(fmaxf(fabsf(v[fm][2 * gp][i]), fabsf(v[fm][2 * gp + 1][i])));
               const uint32_t c = mx_group_code(mm);
               const float inv = e8m0_inv(c);
               const int lc = lcol0 + gp * 32;
@@ -645,6 +674,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
         *reinterpret_cast<uint4*>(p.act + ((size_t)(blk * BM + lr) * p.F + nt * BNA) * T::AB + c * 16) = val;
       }
     } else {
+      RowScatter<NT, BNW * 2 / 16, BM> rows;
+      rows.load_slots(p, blk * BM, BM, tid);
       uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BM][BNW]
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -655,15 +686,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
             st[(wm * (BM / 2) + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
                 (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
       __syncthreads();
-      constexpr int CH = BNW * 2 / 16;
-      for (int idx = tid; idx < BM * CH; idx += NT) {
-        const int lr = idx / CH;
-        const int c = idx % CH;
-        const int sid = p.sorted_ids[blk * BM + lr];
-        if (sid >= p.A) continue;
-        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNW * 2 + c * 16);
-        *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
-      }
+      rows.store(p, lds, nt * BNW, tid);
     }
     if (!dyn) break;
     __syncthreads();  // this tile (and the last index read) is done with LDS
@@ -960,6 +983,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
         *reinterpret_cast<uint4*>(p.act + ((size_t)(blk * BB + lr) * p.F + nt * BNA) * 2 + c * 16) = val;
       }
     } else {
+      RowScatter<NT, BNW * 2 / 16, BMT> rows;
+      rows.load_slots(p, blk * BB, nrows, tid);
       uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
@@ -970,15 +995,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
             st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
                 (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
       __syncthreads();
-      constexpr int CH = BNW * 2 / 16;
-      for (int idx = tid; idx < nrows * CH; idx += NT) {
-        const int lr = idx / CH;
-        const int c = idx % CH;
-        const int sid = p.sorted_ids[blk * BB + lr];
-        if (sid >= p.A) continue;
-        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNW * 2 + c * 16);
-        *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
-      }
+      rows.store(p, lds, nt * BNW, tid);
     }
     if (!dyn) break;
     __syncthreads();  // this tile (and the last index read) is done with LDS
@@ -1000,38 +1017,52 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
 // tile of gemm_pair_bf16 (up to two consecutive blocks of one expert x 256
 // weight rows; 8 waves as 2 x 4, each one block's rows x 64 weight rows) on
 // e4m3 activations x e2m1 weights.  Each weight tile is copied once for
-// both blocks, and a K step moves 2.98 bytes per kFLOP instead of the 3.99
-// of a BLOCK_M x 256 tile.  A K step is one 128-wide MFMA step: 128 bytes of
-// each A row, 64 bytes of each weight row and one 4-byte word of e8m0
-// scales (four 32-wide K groups) per row of either.  One ring of three
-// slots, two steps ahead; a slot holds a step's A rows, weight rows and
-// scale words (50 KiB at BB = 128).  GEMM1's epilogue requantises each row's
-// 32 SwiGLU columns of a wave (one MX group) with the power-of-two scale
-// pow2_at_least(amax / 448) ([MegaMoE] §3.5).
+// both blocks.  A K step is one 128-wide MFMA step: 128 bytes of each A row
+// and 64 bytes of each weight row.
+//
+// Copies.  Waves 0-3 copy the A rows (one step ahead: they come from the L2,
+// where the rows of a pair serve all its N tiles) and waves 4-7 the weight
+// rows (four steps ahead: they come from HBM).  A wave's copies complete in
+// issue order, so a wave that copied both would have to wait for its
+// younger weight copies whenever it waits for an A step; split, each half
+// waits for its own stream only.  LDS: two A slots, five weight slots and
+// two slots of e8m0 scales, 160 KiB at BB = 128.  The scales (one byte per
+// row and 32-wide K group) are copied 16 bytes per row at a time, four
+// steps' worth (a CU keeps a fixed number of copy requests in flight).
+//
+// Multiply.  Per step a wave reads its weight fragments, then its A
+// fragments one at a time, each read issued before the MFMAs of the
+// previous one so that LDS latency overlaps the matrix cores.  GEMM1's
+// epilogue requantises each row's 32 SwiGLU columns of a wave (one MX group)
+// with the power-of-two scale pow2_at_least(amax / 448) ([MegaMoE] §3.5).
 template <bool G1, int BB>  // BB: rows per block (64 or 128)
 __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   constexpr int NW = 8, NT = 64 * NW, WN = NW / 2;
   constexpr int BMT = 2 * BB;          // rows per tile
   constexpr int BNW = 256;             // weight rows per tile
   constexpr int ARB = 128, BRB = 64;   // A / B bytes per row and step
-  constexpr int ASZ = BMT * ARB;
-  constexpr int BSZ = BNW * BRB;
-  constexpr int SCSZ = NT * 4;         // one scale word per thread: A rows, then B rows
-  constexpr int SSZ = ASZ + BSZ + SCSZ;
-  constexpr int NS = 3, D = NS - 1;
+  constexpr int ASZ = BMT * ARB;       // one A slot
+  constexpr int BSZ = BNW * BRB;       // one weight slot
+  constexpr int NA = 2, NB = 5;        // slots: A one step ahead, weights four
+  constexpr int DA = NA - 1, DB = NB - 1;
+  constexpr int SCG = 4;               // steps per scale group
+  constexpr int SCSZ = NT * 16;        // a scale group: 16 bytes per row, A rows then weight rows
   constexpr int FM = BB / 16;          // 16-row fragments per wave (one block's rows)
   constexpr int FN = BNW / WN / 16;    // 16-column fragments per wave
-  constexpr int RW = BMT / NW;         // A rows each wave copies
-  constexpr int RWB = BNW / NW;        // weight rows each wave copies
-  constexpr int LA = RW / 8;           // 1 KiB copies per wave per step: 8 A rows of 128 bytes
-  constexpr int LB = RWB / 16;         //                                16 weight rows of 64 bytes
-  constexpr int LS = LA + LB + 1;      // + the scale word
-  static_assert(BMT + BNW <= NT && NS * SSZ <= 163840 && LA >= 1 && LB >= 1 && FN % 2 == 0 &&
-                LS * (D - 1) <= 63, "tile, ring, scale words and vmcnt");
+  constexpr int CW = NW / 2;           // waves per copy stream
+  constexpr int RA = BMT / CW;         // A rows each A wave copies
+  constexpr int RB = BNW / CW;         // weight rows each weight wave copies
+  constexpr int LA = RA / 8;           // 1 KiB copies per step: 8 A rows of 128 bytes
+  constexpr int LB = RB / 16;          //                        16 weight rows of 64 bytes
+  constexpr int ABASE = 0, BBASE = NA * ASZ, SBASE = NA * ASZ + NB * BSZ;
+  static_assert(BMT <= CW * 64 && BNW == CW * 64 && SBASE + 2 * SCSZ <= 163840 && LA >= 1 && LB >= 1 &&
+                FN % 2 == 0 && LB * (DB - 1) + 1 <= 63 && FM % 2 == 0, "tile, LDS, copies and vmcnt");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool bwave = wave >= CW;  // copies weight rows (else A rows)
+  const int cw = wave % CW;       // index among the waves of its copy stream
   const int lane = tid & 63;
   const int wm = wave / WN;  // rows [BB wm, +BB): the tile's first or second block
   const int wn = wave % WN;
@@ -1047,7 +1078,8 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   const int npairs = min(p.pairs[0], nblk);
   const int64_t n_valid = (int64_t)npairs * ntn;
   const int64_t per = (n_valid + 7) >> 3;
-  const int nk = K / 128;
+  const int nk = K / 128;              // a multiple of SCG (K is a multiple of 512)
+  const int ng = nk / SCG;
   const int rowbytes_a = K;       // e4m3
   const int rowbytes_b = K / 2;   // packed e2m1
   const int kgroups = K / 32;     // e8m0 scale bytes per row
@@ -1056,8 +1088,10 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   const uint8_t* ascale = static_cast<const uint8_t*>(G1 ? p.xs : p.act_s);
   const uint8_t* wscale = static_cast<const uint8_t*>(G1 ? p.w13_s : p.w2_s);
   const size_t erows = G1 ? (size_t)2 * p.F : (size_t)p.H;
-  const rsrc_t ra = make_rsrc(asrc, (uint64_t)(G1 ? p.A / p.k : nblk * BB) * rowbytes_a);
+  const uint32_t arows = G1 ? (uint32_t)(p.A / p.k) : (uint32_t)nblk * BB;
+  const rsrc_t ra = make_rsrc(asrc, (uint64_t)arows * rowbytes_a);
   const rsrc_t rnone = make_rsrc(asrc, 0);  // every read returns zero
+  const rsrc_t ras = make_rsrc(ascale, (uint64_t)arows * kgroups);
 
   // LDS chunk slots: A rows of 128 bytes, chunk c at c ^ (rr / 2 % 8);
   // weight rows of 64 bytes, chunk c at c ^ (rr / 2 % 4) (a fragment read of
@@ -1091,49 +1125,61 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
       const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
       const bool mine = wm == 0 || two;  // this wave's block exists
 
-      // A copies: wave w fills tile rows [RW w, +RW), 8 per instruction;
-      // rows of a missing second block come from the empty range
-      const bool copy_rows = wave < NW / 2 || two;
-      const rsrc_t rA = copy_rows ? ra : rnone;
-      uint32_t ag[LA];
-#pragma unroll
-      for (int i = 0; i < LA; ++i) {
-        const int rr = wave * RW + 8 * i + lane / 8;
-        const int c = (lane % 8) ^ ((rr >> 1) & 7);
-        bool v;
-        const int src = copy_rows ? a_row_index<G1>(p, blk, BB, rr, v) : 0;  // padding rows read row 0
-        ag[i] = (uint32_t)src * rowbytes_a + 16 * c;
-      }
+      // This wave's copy stream.  A waves: tile rows [RA cw, +RA), 8 per
+      // instruction (rows of a missing second block from the empty range).
+      // Weight waves: weight rows [RB cw, +RB), 16 per instruction.
+      const bool copy_rows = (cw * RA < BB) || two;
       const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes_b, (uint64_t)erows * rowbytes_b);
-      uint32_t bg[LB];
+      const rsrc_t rc = bwave ? rb : (copy_rows ? ra : rnone);
+      constexpr int LC = LA > LB ? LA : LB;
+      uint32_t cg[LC];
 #pragma unroll
-      for (int i = 0; i < LB; ++i) {
-        const int rr = wave * RWB + 16 * i + lane / 4;
-        const int c = (lane % 4) ^ ((rr >> 1) & 3);
-        bg[i] = (uint32_t)weight_row(nt, rr) * rowbytes_b + 16 * c;
-      }
-      // scale word of thread q: A row q (q < BMT), weight row q - BMT;
-      // rows of a missing block read the tile's first row
-      const uint8_t* scg;
-      {
-        const int q = tid < BMT + BNW ? tid : 0;
-        if (q < BMT) {
-          bool v;
-          const int row = (q < BB || two) ? q : 0;
-          const int src = a_row_index<G1>(p, blk, BB, row, v);
-          scg = ascale + (size_t)src * kgroups;
+      for (int i = 0; i < LC; ++i) {
+        if (bwave) {
+          const int rr = cw * RB + 16 * i + lane / 4;
+          const int c = (lane % 4) ^ ((rr >> 1) & 3);
+          cg[i] = i < LB ? (uint32_t)weight_row(nt, rr) * rowbytes_b + 16 * c : 0u;
         } else {
-          scg = wscale + ((size_t)e * erows + weight_row(nt, q - BMT)) * kgroups;
+          const int rr = cw * RA + 8 * i + lane / 8;
+          const int c = (lane % 8) ^ ((rr >> 1) & 7);
+          bool v;
+          const int src = (i < LA && copy_rows) ? a_row_index<G1>(p, blk, BB, rr, v) : 0;  // padding: row 0
+          cg[i] = (uint32_t)src * rowbytes_a + 16 * c;
         }
       }
+      // scale groups: 16 bytes of A row q (A waves, q = tid < BMT; the rest
+      // and rows of a missing block read the tile's first row) or of weight
+      // row q = tid - 256 (weight waves); the descriptor is wave-uniform
+      rsrc_t rs;
+      uint32_t sg;
+      if (bwave) {
+        rs = make_rsrc(wscale + (size_t)e * erows * kgroups, (uint64_t)erows * kgroups);
+        sg = (uint32_t)weight_row(nt, tid - CW * 64) * kgroups;
+      } else {
+        const int q = tid < BMT ? tid : 0;
+        bool v;
+        rs = ras;
+        sg = (uint32_t)a_row_index<G1>(p, blk, BB, (q < BB || two) ? q : 0, v) * kgroups;
+      }
+      // step s's copies of this wave's stream (past the end: the last step
+      // again, into a slot no later step reads)
       auto issue = [&](int s) {
-        uint8_t* st = lds + (s % NS) * SSZ;
-        s = s < nk ? s : nk - 1;  // past the end: the last step again, into a slot no later step reads
+        if (bwave) {
+          uint8_t* st = lds + BBASE + (s % NB) * BSZ + cw * RB * BRB;
+          s = s < nk ? s : nk - 1;
 #pragma unroll
-        for (int i = 0; i < LA; ++i) buf2lds16(rA, ag[i], s * ARB, st + (wave * RW + 8 * i) * ARB);
+          for (int i = 0; i < LB; ++i) buf2lds16(rc, cg[i], s * BRB, st + 16 * i * BRB);
+        } else {
+          uint8_t* st = lds + ABASE + (s % NA) * ASZ + cw * RA * ARB;
+          s = s < nk ? s : nk - 1;
 #pragma unroll
-        for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * BRB, st + ASZ + (wave * RWB + 16 * i) * BRB);
-        g2lds4(scg + 4 * s, st + ASZ + BSZ + wave * 256);
+          for (int i = 0; i < LA; ++i) buf2lds16(rc, cg[i], s * ARB, st + 8 * i * ARB);
+        }
+      };
+      auto issue_sc = [&](int G) {
+        uint8_t* st = lds + SBASE + (G & 1) * SCSZ + wave * 1024;
+        G = G < ng ? G : ng - 1;
+        buf2lds16(rs, sg, G * 16, st);
       };
 
       f32x4_t acc[FM][FN];
@@ -1142,67 +1188,110 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-      issue(0);
-      issue(1);
+      issue_sc(0);
+      if (bwave) {
+#pragma unroll
+        for (int s = 0; s < DB; ++s) issue(s);
+      } else {
+        issue(0);
+      }
       for (int s = 0; s < nk; ++s) {
-        // this wave's reads of the slot about to be refilled are done, its
-        // copies of step s have landed (only step s + 1's may remain), then
-        // the barrier and the copies of step s + 2
+        // Every wave has read the slots about to be refilled (lgkmcnt(0)) and
+        // this wave's copies of step s have landed: A waves wait for all of
+        // theirs but the scale group issued at step s - 1 (if any); weight
+        // waves leave the copies of steps s + 1 .. s + 3 in flight (and the
+        // scale group one of those steps issued).  Then the barrier, and the
+        // copies of steps s + 1 (A) / s + 4 (weights) and of the next scale
+        // group.
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
-        wait_vm<LS * (D - 1)>();
+        if (bwave) {
+          if (s % SCG == 0) wait_vm<LB * (DB - 1)>();
+          else wait_vm<LB * (DB - 1) + 1>();
+        } else {
+          if (s % SCG == 1) wait_vm<1>();
+          else wait_vm<0>();
+        }
         barrier_no_fence();
-        issue(s + D);
+        issue(s + (bwave ? DB : DA));
+        if (s % SCG == 0) issue_sc(s / SCG + 1);
         if (mine) {
-          const uint8_t* st = lds + (s % NS) * SSZ;
-          const uint8_t* Ss = st + ASZ + BSZ;
-          i32x8_t bfr[FN];
+          const uint8_t* As = lds + ABASE + (s % NA) * ASZ;
+          const uint8_t* Bs = lds + BBASE + (s % NB) * BSZ;
+          // row q's byte for K group g of step s: 16 q + 4 (s % 4) + g
+          const uint8_t* Ss = lds + SBASE + ((s / SCG) & 1) * SCSZ + 4 * (s % SCG);
+          i32x4_t bfr[FN];
           int sb[FN];
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
             const int rr = frag_lrow(fn) + r;
-            const i32x4_t v = *reinterpret_cast<const i32x4_t*>(st + ASZ + b_off(rr, g));
-            bfr[fn] = i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-            sb[fn] = (int)Ss[(BMT + rr) * 4 + g];
+            bfr[fn] = *reinterpret_cast<const i32x4_t*>(Bs + b_off(rr, g));
+            sb[fn] = (int)Ss[(CW * 64 + rr) * 16 + g];
           }
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
+          auto read_a = [&](int fm, i32x4_t& lo, i32x4_t& hi, int& sa) {
             const int rr = wm * BB + fm * 16 + r;
-            const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + a_off(rr, g));
-            const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + a_off(rr, 4 + g));
+            lo = *reinterpret_cast<const i32x4_t*>(As + a_off(rr, g));
+            hi = *reinterpret_cast<const i32x4_t*>(As + a_off(rr, 4 + g));
+            sa = (int)Ss[rr * 16 + g];
+          };
+          auto mult = [&](int fm, const i32x4_t& lo, const i32x4_t& hi, int sa) {
             const i32x8_t af = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const int sa = (int)Ss[rr * 4 + g];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_mx(af, bfr[fn], acc[fm][fn], sa, sb[fn]);
+            for (int fn = 0; fn < FN; ++fn) {
+              const i32x4_t v = bfr[fn];
+              acc[fm][fn] = mfma_mx(af, i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0}, acc[fm][fn], sa, sb[fn]);
+            }
+          };
+          // A fragments in two register sets: the reads of fragment fm + 1
+          // go out before the MFMAs of fragment fm
+          i32x4_t lo0, hi0, lo1, hi1;
+          int sa0, sa1;
+          read_a(0, lo0, hi0, sa0);
+#pragma unroll
+          for (int fm = 0; fm < FM; fm += 2) {
+            read_a(fm + 1, lo1, hi1, sa1);
+            __builtin_amdgcn_sched_barrier(0);
+            mult(fm, lo0, hi0, sa0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (fm + 2 < FM) read_a(fm + 2, lo0, hi0, sa0);
+            __builtin_amdgcn_sched_barrier(0);
+            mult(fm + 1, lo1, hi1, sa1);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
       wait_vm<0>();     // the copies past the last step have landed too
-      __syncthreads();  // every wave is done reading the ring
+      __syncthreads();  // every wave is done reading the rings
+
 
       // ---------------------------------------------------------------- epilogue
       const int nrows = two ? BMT : BB;
       if (G1) {
         constexpr int BNA = BNW / 2;  // SwiGLU columns per tile
         uint8_t* acts = static_cast<uint8_t*>(p.act_s);
+        // this lane's first row (fm = 0, i = 0) in the byte tile and in the
+        // code table; the others are compile-time offsets from it
+        uint8_t* const rowp = lds + (wm * BB + 4 * g) * BNA + wn * 32 + r;
+        uint8_t* const codep = lds + BMT * BNA + (wm * BB + 4 * g) * (BNA / 32) + wn;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int lr = wm * BB + fm * 16 + 4 * g + i;
             const float v0 = swiglu(acc[fm][0][i], acc[fm][FN / 2][i], p.lim);
             const float v1 = swiglu(acc[fm][1][i], acc[fm][FN / 2 + 1][i], p.lim);
             // the wave's 32 columns of row lr are one MX group: its amax over
-            // the 16 lanes that hold the row
-            float m = fmaxf(fabsf(v0), fabsf(v1));
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+            // the 16 lanes (one DPP row) that hold the row
+            const float m = row_max16(fmaxf(fabsf(v0), fabsf(v1)));
             const uint32_t code = mx_group_code(m);
             const float inv = e8m0_inv(code);
-            if (mine && r == 0) acts[(size_t)(blk * BB + lr) * (p.F / 32) + nt * (BNA / 32) + wn] = (uint8_t)code;
-            lds[lr * BNA + wn * 32 + r] = (uint8_t)to_e4m3(clamp448(v0 * inv));
-            lds[lr * BNA + wn * 32 + 16 + r] = (uint8_t)to_e4m3(clamp448(v1 * inv));
+            if (r == 0) codep[(fm * 16 + i) * (BNA / 32)] = (uint8_t)code;
+            rowp[(fm * 16 + i) * BNA] = (uint8_t)to_e4m3(clamp448(v0 * inv));
+            rowp[(fm * 16 + i) * BNA + 16] = (uint8_t)to_e4m3(clamp448(v1 * inv));
           }
         __syncthreads();
+        // the tile's BNA / 32 codes of a row are one 4-byte word of act_s
+        if (tid < nrows)
+          *reinterpret_cast<uint32_t*>(acts + (size_t)(blk * BB + tid) * (p.F / 32) + nt * (BNA / 32)) =
+              *reinterpret_cast<const uint32_t*>(lds + BMT * BNA + tid * (BNA / 32));
         constexpr int CH = BNA / 16;  // 16-byte chunks per tile row
         for (int idx = tid; idx < nrows * CH; idx += NT) {
           const int lr = idx / CH;
@@ -1211,6 +1300,8 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
           *reinterpret_cast<uint4*>(p.act + (size_t)(blk * BB + lr) * p.F + nt * BNA + c * 16) = val;
         }
       } else {
+        RowScatter<NT, BNW * 2 / 16, BMT> rows;
+        rows.load_slots(p, blk * BB, nrows, tid);
         uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
@@ -1221,15 +1312,7 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
               st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
                   (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
         __syncthreads();
-        constexpr int CH = BNW * 2 / 16;
-        for (int idx = tid; idx < nrows * CH; idx += NT) {
-          const int lr = idx / CH;
-          const int c = idx % CH;
-          const int sid = p.sorted_ids[blk * BB + lr];
-          if (sid >= p.A) continue;
-          const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNW * 2 + c * 16);
-          *reinterpret_cast<uint4*>(p.out + (size_t)sid * p.H + nt * BNW + c * 8) = val;
-        }
+        rows.store(p, lds, nt * BNW, tid);
       }
     }
     if (!dyn) break;
@@ -1583,7 +1666,7 @@ moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
 
 template <bool G1, int BB>
 moe_status launch_pair_mx_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
-  constexpr size_t lds = (size_t)3 * ((size_t)2 * BB * 128 + 256 * 64 + 512 * 4);  // 3 slots: A, B, scale words
+  constexpr size_t lds = (size_t)2 * (2 * BB * 128) + 5 * 256 * 64 + 2 * 512 * 16;  // A: 2 slots, B: 5, scales: 2
   static std::atomic<int> cache[64];
   const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_mx<G1, BB>), 512, lds, cache);
   gemm_pair_mx<G1, BB><<<tile_grid(max_tiles, wgs), 512, lds, s>>>(p);
