@@ -20,9 +20,10 @@ Also reported in the same line:
                   published peak of the matrix-core instruction it issues
                   and against HBM; its launch time from HIP events on its
                   own stream in a staged loop with a fixed warm-up
-  decode        - cold graph replays at every decode size of the five
-                  configurations: us/layer (median, p10, p90) and the HBM
-                  rate on the weights of the experts actually touched
+  decode        - cold moe_layer calls (eager, and replays of the captured
+                  graph) at every decode size of the five configurations:
+                  us/layer (median, p10, p90) and the HBM rate on the
+                  weights of the experts actually touched
   prefill       - the other prefill configurations: warm back-to-back
                   replays and cold replays, MFMA and HBM fractions
   router        - moe_route alone at T = 1 for every configuration (and GLM
@@ -317,11 +318,15 @@ def layer_sweep(moe, torch, flush, cases, reps, warm, keep=None):
         W = cache[name]
         x = make_x(cfg, T, "cuda")
         lg = LayerGraph(moe, torch, cfg, W, x)
-        ts = cold_times(torch, flush, lg.replay, reps)
+        # eager moe_layer calls and replays of the captured graph (the graph
+        # launch costs a few us more here)
+        ts = cold_times(torch, flush, lg.eager, reps)
+        tg = cold_times(torch, flush, lg.replay, reps)
         touched = touched_experts(moe, torch, cfg, W, x)
         wbytes = touched * cfg.expert_bytes()
         us = statistics.median(ts)
-        r = {"us_per_layer": summary(ts), "tokens_per_s": round(T / (us * 1e-6), 1), "block_m": lg.bm,
+        r = {"us_per_layer": summary(ts), "graph_replay_us": summary(tg),
+             "tokens_per_s": round(T / (us * 1e-6), 1), "block_m": lg.bm,
              "experts_touched": touched, "weight_bytes": wbytes, "weights": cfg.wformat,
              "hbm_TBps": round(wbytes / (us * 1e-6) / 1e12, 3), "hbm_frac": round(wbytes / (us * 1e-6) / HBM_PEAK, 4)}
         if warm:
@@ -333,7 +338,7 @@ def layer_sweep(moe, torch, flush, cases, reps, warm, keep=None):
             r["mfma_issued"] = MFMA_ISSUED[cfg.wformat]
         key = f"{name}_T{T}"
         out[key] = r
-        log(f"{key}: cold {r['us_per_layer']} us, {touched} experts, {r['hbm_TBps']} TB/s ({r['hbm_frac']:.3f} of HBM)"
+        log(f"{key}: cold {r['us_per_layer']} us (graph replay {r['graph_replay_us']['median']}), {touched} experts, {r['hbm_TBps']} TB/s ({r['hbm_frac']:.3f} of HBM)"
             + (f"; warm {r['warm_us_per_layer']} us, MFMA {r['mfma_frac_warm']:.3f}" if warm else ""))
         del lg
     cache.clear()
@@ -479,7 +484,7 @@ def main():
     ap.add_argument("--reps", type=int, default=30, help="cold replays per case")
     ap.add_argument("--T", type=int, default=8192)
     ap.add_argument("--config", default="dsv4")
-    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: T / 4)")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: T / 16)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode, prefill, router and EP-share rows")
     ap.add_argument("--only", choices=("decode", "prefill", "router", "ep"),
@@ -532,7 +537,7 @@ def main():
         "gemm1_event_us": h["gemm1_us"],
     }
     if not args.no_cpu:
-        n = args.cpu_sample if args.cpu_sample > 0 else max(1, T // 4)
+        n = args.cpu_sample if args.cpu_sample > 0 else max(1, T // 16)
         base, ties = cpu_baseline(moe, torch, cfg, W, x, n)
         result["cpu_baseline"] = base
         result["routing_near_ties"] = ties
@@ -544,8 +549,9 @@ def main():
         result["prefill"] = layer_sweep(moe, torch, flush, PREFILL, max(10, args.reps // 3), True)
         result["router"] = router_probe(moe, torch, flush, args.reps)
         result["ep_share_dsv4_32_experts"] = ep_share_sweep(moe, torch, flush, args.reps)
-        result["cold_timing"] = ("each replay after a 1 GiB read; raw event-pair time around it (median, p10, p90), "
-                                 "which includes the first kernel's launch and the last one's completion")
+        result["cold_timing"] = ("each call (eager moe_layer, or a replay of its captured graph) after a 1 GiB read; "
+                                 "raw event-pair time around it (median, p10, p90), which includes the first "
+                                 "kernel's launch and the last one's completion")
     print(json.dumps(result), flush=True)
     return 0
 

@@ -265,8 +265,8 @@ size_t moe_expert_ffn_workspace_size(int T, int H, int E, int F, int k,
  * kernel with events.  Unknown bits return MOE_E_INVAL. */
 typedef enum moe_ffn_stage {
   MOE_STAGE_QUANT = 1,    /* activation quantisation (fp8 formats); the   */
-                          /* tile table of the paired GEMMs (bf16,        */
-                          /* block_m 128)                                 */
+                          /* tile table of the paired GEMMs (bf16 and     */
+                          /* MXFP4, block_m 64 or 128)                    */
   MOE_STAGE_GEMM1 = 2,    /* grouped GEMM1 + SwiGLU epilogue              */
   MOE_STAGE_GEMM2 = 4,    /* grouped GEMM2                                */
   MOE_STAGE_COMBINE = 8,  /* weighted slot-order combine into y           */

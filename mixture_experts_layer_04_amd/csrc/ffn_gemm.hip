@@ -810,8 +810,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
   const int N = G1 ? p.F : p.H;
   const int BNO = G1 ? BNW / 2 : BNW;  // output columns per tile
   const int ntn = N / BNO;
-  const int npairs = p.pairs[0];
   const int nblk = *p.npp / BB;
+  // a pair table left by another shape holds more pairs than blocks exist:
+  // at most one pair per block, and tiles past the blocks are skipped
+  const int npairs = min(p.pairs[0], nblk);
   const int64_t n_valid = (int64_t)npairs * ntn;
   const int64_t per = (n_valid + 7) >> 3;
   const int nk = K / (RB / 2);
@@ -862,140 +864,142 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
     const int nt = (int)(L % ntn);
     const int blk = pe & 0x3FFFFFFF;  // first block of the tile
     const bool two = (pe >> 30) & 1;
-    const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
-    const bool mine = wm == 0 || two;  // this wave's block exists
+    if (blk + (two ? 1 : 0) < nblk) {
+      const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
+      const bool mine = wm == 0 || two;  // this wave's block exists
 
-    // wave w copies tile rows [RW w, RW w + RW): rows of the second block
-    // come from an empty range when the tile holds one block
-    const bool copy_rows = wave < NW / 2 || two;
-    const rsrc_t rA = copy_rows ? ra : rnone;
-    uint32_t ag[LA];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      int row, c;
-      copy_src(wave * RW + (64 / CPR) * i, lane, row, c);
-      bool v;
-      const int src = copy_rows ? a_row_index<G1>(p, blk, BB, row, v) : 0;  // padding rows read token 0
-      ag[i] = (uint32_t)src * rowbytes + 16 * c;
-    }
-    const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes, (uint64_t)erows * rowbytes);
-    uint32_t bg[LB];
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      int row, c;
-      copy_src(wave * RWB + (64 / CPR) * i, lane, row, c);
-      bg[i] = (uint32_t)weight_row(nt, row) * rowbytes + 16 * c;
-    }
-    // copies of step s (clamped to the last step: past the end a step is
-    // copied again into a slot no later step reads, so every barrier waits
-    // for the same count)
-    auto issue_a = [&](int s) {
-      uint8_t* st = lds + (s % NA) * ASZ;
-      s = s < nk ? s : nk - 1;
-#pragma unroll
-      for (int i = 0; i < LA; ++i) buf2lds16(rA, ag[i], s * RB, st + (wave * RW + (64 / CPR) * i) * RB);
-    };
-    auto issue_b = [&](int s) {
-      uint8_t* st = lds + NA * ASZ + (s % NB) * BSZ;
-      s = s < nk ? s : nk - 1;
-#pragma unroll
-      for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * RB, st + (wave * RWB + (64 / CPR) * i) * RB);
-    };
-
-    f32x4_t acc[FM][FN];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    struct Frag {
-      bf16x8_t a[FM];
-      bf16x8_t b[FN];
-    };
-    auto rd = [&](int s, int ks, Frag& f) {
-      const uint8_t* As = lds + (s % NA) * ASZ;
-      const uint8_t* Bs = lds + NA * ASZ + (s % NB) * BSZ;
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int rr = wm * BB + fm * 16 + r;
-        f.a[fm] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(rr, 4 * ks + g));
+      // wave w copies tile rows [RW w, RW w + RW): rows of the second block
+      // come from an empty range when the tile holds one block
+      const bool copy_rows = wave < NW / 2 || two;
+      const rsrc_t rA = copy_rows ? ra : rnone;
+      uint32_t ag[LA];
+  #pragma unroll
+      for (int i = 0; i < LA; ++i) {
+        int row, c;
+        copy_src(wave * RW + (64 / CPR) * i, lane, row, c);
+        bool v;
+        const int src = copy_rows ? a_row_index<G1>(p, blk, BB, row, v) : 0;  // padding rows read token 0
+        ag[i] = (uint32_t)src * rowbytes + 16 * c;
       }
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int rr = frag_lrow(fn) + r;
-        f.b[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rr, 4 * ks + g));
+      const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes, (uint64_t)erows * rowbytes);
+      uint32_t bg[LB];
+  #pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        int row, c;
+        copy_src(wave * RWB + (64 / CPR) * i, lane, row, c);
+        bg[i] = (uint32_t)weight_row(nt, row) * rowbytes + 16 * c;
       }
-    };
-    auto mm = [&](const Frag& f) {
-#pragma unroll
+      // copies of step s (clamped to the last step: past the end a step is
+      // copied again into a slot no later step reads, so every barrier waits
+      // for the same count)
+      auto issue_a = [&](int s) {
+        uint8_t* st = lds + (s % NA) * ASZ;
+        s = s < nk ? s : nk - 1;
+  #pragma unroll
+        for (int i = 0; i < LA; ++i) buf2lds16(rA, ag[i], s * RB, st + (wave * RW + (64 / CPR) * i) * RB);
+      };
+      auto issue_b = [&](int s) {
+        uint8_t* st = lds + NA * ASZ + (s % NB) * BSZ;
+        s = s < nk ? s : nk - 1;
+  #pragma unroll
+        for (int i = 0; i < LB; ++i) buf2lds16(rb, bg[i], s * RB, st + (wave * RWB + (64 / CPR) * i) * RB);
+      };
+
+      f32x4_t acc[FM][FN];
+  #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(f.a[fm], f.b[fn], acc[fm][fn]);
-    };
-    // Before step sn: this wave's LDS reads are done (lgkmcnt), its copies
-    // of A(sn) and B(sn) have landed (vmcnt: only B(sn + 1), the copies
-    // issued last, may remain), barrier, then A(sn + 1) into the A slot of
-    // step sn - 1 and B(sn + 2) into the B slot of step sn - 1.
-    auto next_step = [&](int sn) {
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
-      wait_vm<LB>();
-      barrier_no_fence();
-      issue_a(sn + DA);
-      issue_b(sn + DB);
-    };
+  #pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    issue_a(0);
-    issue_b(0);
-    issue_b(1);
-    for (int s = 0; s < nk; ++s) {
-      next_step(s);
-      if (mine) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Frag f;
-          rd(s, ks, f);
-          mm(f);
+      struct Frag {
+        bf16x8_t a[FM];
+        bf16x8_t b[FN];
+      };
+      auto rd = [&](int s, int ks, Frag& f) {
+        const uint8_t* As = lds + (s % NA) * ASZ;
+        const uint8_t* Bs = lds + NA * ASZ + (s % NB) * BSZ;
+  #pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int rr = wm * BB + fm * 16 + r;
+          f.a[fm] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(rr, 4 * ks + g));
+        }
+  #pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int rr = frag_lrow(fn) + r;
+          f.b[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rr, 4 * ks + g));
+        }
+      };
+      auto mm = [&](const Frag& f) {
+  #pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+  #pragma unroll
+          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(f.a[fm], f.b[fn], acc[fm][fn]);
+      };
+      // Before step sn: this wave's LDS reads are done (lgkmcnt), its copies
+      // of A(sn) and B(sn) have landed (vmcnt: only B(sn + 1), the copies
+      // issued last, may remain), barrier, then A(sn + 1) into the A slot of
+      // step sn - 1 and B(sn + 2) into the B slot of step sn - 1.
+      auto next_step = [&](int sn) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
+        wait_vm<LB>();
+        barrier_no_fence();
+        issue_a(sn + DA);
+        issue_b(sn + DB);
+      };
+
+      issue_a(0);
+      issue_b(0);
+      issue_b(1);
+      for (int s = 0; s < nk; ++s) {
+        next_step(s);
+        if (mine) {
+  #pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            Frag f;
+            rd(s, ks, f);
+            mm(f);
+          }
         }
       }
-    }
-    wait_vm<0>();     // the copies past the last step have landed too
-    __syncthreads();  // every wave is done reading the rings
+      wait_vm<0>();     // the copies past the last step have landed too
+      __syncthreads();  // every wave is done reading the rings
 
-    // ---------------------------------------------------------------- epilogue
-    const int nrows = two ? BMT : BB;
-    if (G1) {
-      constexpr int BNA = BNW / 2;  // SwiGLU columns per tile
-      uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNA]
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int fa = 0; fa < FN / 2; ++fa)
-            st[(wm * BB + fm * 16 + 4 * g + i) * BNA + wn * (BNA / WN) + fa * 16 + r] =
-                (uint16_t)f32_to_bf16_bits(swiglu(acc[fm][fa][i], acc[fm][fa + FN / 2][i], p.lim));
-      __syncthreads();
-      constexpr int CH = BNA * 2 / 16;  // 16-byte chunks per tile row
-      for (int idx = tid; idx < nrows * CH; idx += NT) {
-        const int lr = idx / CH;
-        const int c = idx % CH;
-        const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNA * 2 + c * 16);
-        *reinterpret_cast<uint4*>(p.act + ((size_t)(blk * BB + lr) * p.F + nt * BNA) * 2 + c * 16) = val;
+      // ---------------------------------------------------------------- epilogue
+      const int nrows = two ? BMT : BB;
+      if (G1) {
+        constexpr int BNA = BNW / 2;  // SwiGLU columns per tile
+        uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNA]
+  #pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+  #pragma unroll
+            for (int fa = 0; fa < FN / 2; ++fa)
+              st[(wm * BB + fm * 16 + 4 * g + i) * BNA + wn * (BNA / WN) + fa * 16 + r] =
+                  (uint16_t)f32_to_bf16_bits(swiglu(acc[fm][fa][i], acc[fm][fa + FN / 2][i], p.lim));
+        __syncthreads();
+        constexpr int CH = BNA * 2 / 16;  // 16-byte chunks per tile row
+        for (int idx = tid; idx < nrows * CH; idx += NT) {
+          const int lr = idx / CH;
+          const int c = idx % CH;
+          const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNA * 2 + c * 16);
+          *reinterpret_cast<uint4*>(p.act + ((size_t)(blk * BB + lr) * p.F + nt * BNA) * 2 + c * 16) = val;
+        }
+      } else {
+        RowScatter<NT, BNW * 2 / 16, BMT> rows;
+        rows.load_slots(p, blk * BB, nrows, tid);
+        uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
+  #pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i)
+  #pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
+                  (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
+        __syncthreads();
+        rows.store(p, lds, nt * BNW, tid);
       }
-    } else {
-      RowScatter<NT, BNW * 2 / 16, BMT> rows;
-      rows.load_slots(p, blk * BB, nrows, tid);
-      uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn)
-            st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
-                (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
-      __syncthreads();
-      rows.store(p, lds, nt * BNW, tid);
     }
     if (!dyn) break;
     __syncthreads();  // this tile (and the last index read) is done with LDS
@@ -1161,25 +1165,22 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
         rs = ras;
         sg = (uint32_t)a_row_index<G1>(p, blk, BB, (q < BB || two) ? q : 0, v) * kgroups;
       }
-      // step s's copies of this wave's stream (past the end: the last step
-      // again, into a slot no later step reads)
+      // step s's copies of this wave's stream (none past the last step)
       auto issue = [&](int s) {
+        if (s >= nk) return;
         if (bwave) {
           uint8_t* st = lds + BBASE + (s % NB) * BSZ + cw * RB * BRB;
-          s = s < nk ? s : nk - 1;
 #pragma unroll
           for (int i = 0; i < LB; ++i) buf2lds16(rc, cg[i], s * BRB, st + 16 * i * BRB);
         } else {
           uint8_t* st = lds + ABASE + (s % NA) * ASZ + cw * RA * ARB;
-          s = s < nk ? s : nk - 1;
 #pragma unroll
           for (int i = 0; i < LA; ++i) buf2lds16(rc, cg[i], s * ARB, st + 8 * i * ARB);
         }
       };
       auto issue_sc = [&](int G) {
-        uint8_t* st = lds + SBASE + (G & 1) * SCSZ + wave * 1024;
-        G = G < ng ? G : ng - 1;
-        buf2lds16(rs, sg, G * 16, st);
+        if (G >= ng) return;
+        buf2lds16(rs, sg, G * 16, lds + SBASE + (G & 1) * SCSZ + wave * 1024);
       };
 
       f32x4_t acc[FM][FN];
@@ -1200,15 +1201,18 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
         // this wave's copies of step s have landed: A waves wait for all of
         // theirs but the scale group issued at step s - 1 (if any); weight
         // waves leave the copies of steps s + 1 .. s + 3 in flight (and the
-        // scale group one of those steps issued).  Then the barrier, and the
-        // copies of steps s + 1 (A) / s + 4 (weights) and of the next scale
-        // group.
+        // scale group one of those steps issued).  Near the end, where
+        // fewer copies follow step s's, both wait for all of them.  Then
+        // the barrier, and the copies of steps s + 1 (A) / s + 4 (weights)
+        // and of the next scale group.
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
-        if (bwave) {
+        if (s + DB > nk) {
+          wait_vm<0>();
+        } else if (bwave) {
           if (s % SCG == 0) wait_vm<LB * (DB - 1)>();
           else wait_vm<LB * (DB - 1) + 1>();
         } else {
-          if (s % SCG == 1) wait_vm<1>();
+          if (s % SCG == 1 && s + SCG <= nk) wait_vm<1>();
           else wait_vm<0>();
         }
         barrier_no_fence();
