@@ -349,6 +349,77 @@ def layer_sweep(moe, torch, flush, cases, reps, warm, keep=None):
 ROUTER = (("toy", 1), ("qwen3", 1), ("glm", 1), ("glm", 8), ("glm", 512), ("dsv3", 1), ("dsv4", 1))
 
 
+MFMA_KINDS = [(0, "bf16 16x16x32", 2 * 16 * 16 * 32, (8, 16)), (1, "bf16 32x32x16", 2 * 32 * 32 * 16, (4, 8)),
+              (2, "e4m3 x e4m3 16x16x128", 2 * 16 * 16 * 128, (8, 16)),
+              (3, "e4m3 x e2m1 16x16x128", 2 * 16 * 16 * 128, (8, 16)),
+              (4, "e2m1 x e2m1 16x16x128", 2 * 16 * 16 * 128, (8, 16))]
+
+
+def summarize_profile(d):
+    """Per-kernel figures of a rocprofv3 output directory (csv): for each
+    libmoe kernel and grid size, the number of dispatches and the median,
+    mean and minimum duration in us (kernel traces), or the median of each
+    counter per dispatch (counter collections)."""
+    import collections
+    import csv
+    import glob
+
+    def name_of(r):
+        n = r["Kernel_Name"].replace("void ", "").replace("moe::(anonymous namespace)::", "")
+        return n.replace("moe::", "").split("(")[0]
+
+    def grid_of(r):
+        return r.get("Grid_Size_X") or r.get("Grid_Size") or "?"
+
+    lines = []
+    dur = collections.defaultdict(list)
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "moe::" in r["Kernel_Name"]:
+                    dur[(name_of(r), grid_of(r))].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    for (n, g), v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {n} | {g} | {len(v)} | {statistics.median(v):.2f} | {statistics.mean(v):.2f} | {min(v):.2f} |")
+    if lines:
+        lines.insert(0, "| kernel | grid | dispatches | median us | mean us | min us |\n|---|---|---|---|---|---|")
+    cnt = collections.defaultdict(list)
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "moe::" in r["Kernel_Name"]:
+                    cnt[(name_of(r), grid_of(r), r["Counter_Name"])].append(float(r["Counter_Value"]))
+                elif "FillFunctor" in r["Kernel_Name"]:  # torch.zeros of --copy-probe
+                    cnt[("torch fill", grid_of(r), r["Counter_Name"])].append(float(r["Counter_Value"]))
+    if cnt:
+        lines.append("| kernel | grid | counter | dispatches | median |\n|---|---|---|---|---|")
+        for (n, g, c), v in sorted(cnt.items()):
+            lines.append(f"| {n} | {g} | {c} | {len(v)} | {statistics.median(v):.6g} |")
+    return "\n".join(lines)
+
+
+def mfma_rates(moe, torch, iters=2048, grid=2048):
+    """Issue rate of each matrix-core instruction over the whole chip
+    (moe_probe_mfma: 2048 workgroups of 4 waves, independent accumulator
+    chains); median of 5 timed launches after one untimed."""
+    out = {}
+    sink = torch.empty(int(moe.lib().moe_probe_mfma_sink_len(grid)), dtype=torch.float32, device="cuda")
+    for kind, name, flop, accs in MFMA_KINDS:
+        for na in accs:
+            moe.probe_mfma(kind, na, grid, iters, sink)
+            ts = []
+            for _ in range(5):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                moe.probe_mfma(kind, na, grid, iters, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = statistics.median(ts)
+            out[f"{name}, {na} accumulators"] = round(grid * 4 * iters * na * flop / t / 1e12, 1)
+    return out
+
+
 def router_probe(moe, torch, flush, reps):
     """moe_route alone next to the bare read of its gate weight
     (moe_probe_read, the same bytes) and an empty kernel, all cold; raw
@@ -487,12 +558,19 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens the oracle baseline runs on (0: T / 16)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the decode, prefill, router and EP-share rows")
-    ap.add_argument("--only", choices=("decode", "prefill", "router", "ep"),
+    ap.add_argument("--only", choices=("decode", "prefill", "router", "ep", "mfma"),
                     help="diagnostic: only these rows (for kernel traces), no benchmark line")
+    ap.add_argument("--cases", metavar="NAME:T,...",
+                    help="with --only decode / prefill: just these cases (e.g. glm:1,dsv3:256)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print per-kernel durations / counters of a rocprofv3 csv output directory and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first write MIB MiB with a fill kernel and read them once with moe_probe_read "
                          "(kernels of known traffic that calibrate rocprofv3 WRITE_SIZE / FETCH_SIZE)")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize_profile(args.summarize))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the layer keeps every expert on the one GPU and has no multi-GPU path. "
               "Run with --gpus 1.", file=sys.stderr)
@@ -502,20 +580,24 @@ def main():
     import mixture_experts_layer_04_amd as moe
     from synth import get_config
 
-    flush = Flush(moe, torch)
-    if args.only:
-        rows = {"decode": lambda: layer_sweep(moe, torch, flush, DECODE, args.reps, False),
-                "prefill": lambda: layer_sweep(moe, torch, flush, PREFILL, args.reps, True),
-                "router": lambda: router_probe(moe, torch, flush, args.reps),
-                "ep": lambda: ep_share_sweep(moe, torch, flush, args.reps)}[args.only]()
-        for key, v in rows.items():
-            log(f"{key}: {v}")
-        return 0
     if args.copy_probe:
         buf = torch.zeros(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
         moe.probe_read(buf)
         torch.cuda.synchronize()
         del buf
+    flush = Flush(moe, torch)
+    if args.only:
+        pick = None
+        if args.cases:
+            pick = tuple((c.split(":")[0], int(c.split(":")[1])) for c in args.cases.split(","))
+        rows = {"decode": lambda: layer_sweep(moe, torch, flush, pick or DECODE, args.reps, False),
+                "prefill": lambda: layer_sweep(moe, torch, flush, pick or PREFILL, args.reps, True),
+                "router": lambda: router_probe(moe, torch, flush, args.reps),
+                "ep": lambda: ep_share_sweep(moe, torch, flush, args.reps),
+                "mfma": lambda: mfma_rates(moe, torch)}[args.only]()
+        for key, v in rows.items():
+            log(f"{key}: {v}")
+        return 0
 
     cfg = get_config(args.config)
     T = args.T

@@ -364,12 +364,24 @@ int moe_layer_block_m(int T, int E, int F, int k, int wformat);
  *   16-byte loads and writes one float per workgroup to `sink`
  *   (sink: float32 [moe_probe_read_sink_len(bytes)]); the bare weight-read
  *   kernel of [Router] §3.3.  bytes must be a multiple of 16.
+ * moe_probe_mfma: enqueues `grid` workgroups of 4 waves; each wave issues
+ *   iters x accs matrix-core instructions on register constants, cycling
+ *   through `accs` (4, 8 or 16) independent accumulators, and writes one
+ *   float per thread to `sink` (float32 [moe_probe_mfma_sink_len(grid)]).
+ *   kind: 0 bf16 16x16x32, 1 bf16 32x32x16 (accs 4 or 8), 2 e4m3 x e4m3,
+ *   3 e4m3 x e2m1, 4 e2m1 x e2m1 (the last three 16x16x128 with e8m0
+ *   scales).  FLOPs per instruction: 2 M N K.  The issue-rate ceiling of the
+ *   instruction the grouped GEMMs use for each weight format.  Bad arguments:
+ *   MOE_E_INVAL.
  * ------------------------------------------------------------------------ */
 int32_t moe_debug_error(void* workspace, hipStream_t stream);
 moe_status moe_probe_empty(hipStream_t stream);
 moe_status moe_probe_read(const void* p, size_t bytes, float* sink,
                           hipStream_t stream);
 size_t moe_probe_read_sink_len(size_t bytes);
+moe_status moe_probe_mfma(int kind, int accs, int grid, int iters, float* sink,
+                          hipStream_t stream);
+size_t moe_probe_mfma_sink_len(int grid);
 
 #ifdef __cplusplus
 }

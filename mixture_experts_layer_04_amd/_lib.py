@@ -72,6 +72,8 @@ SIGNATURES = {
     "moe_probe_empty": (_i, [_vp]),
     "moe_probe_read": (_i, [_vp, _sz, _vp, _vp]),
     "moe_probe_read_sink_len": (_sz, [_sz]),
+    "moe_probe_mfma": (_i, [_i, _i, _i, _i, _vp, _vp]),
+    "moe_probe_mfma_sink_len": (_sz, [_i]),
 }
 
 _lib = None

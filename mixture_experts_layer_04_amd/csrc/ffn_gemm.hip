@@ -136,11 +136,16 @@ struct SOp<F_MX> {
 // silu(min(g, lim)) * clamp(u, -lim, lim) ([MegaMoE] §3.5); lim = +inf: no
 // clamp.  silu(g) = g / (1 + e^-g) on the hardware exp2 and reciprocal
 // (about 1 ulp each; e^-g overflows to +inf for g < -88, giving -0 * u)
-__device__ __forceinline__ float swiglu(float g, float u, float lim) {
-  g = fminf(g, lim);
-  u = fminf(fmaxf(u, -lim), lim);
+__device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
 }
+__device__ __forceinline__ float swiglu(float g, float u, float lim) {
+  return silu_mul(fminf(g, lim), fminf(fmaxf(u, -lim), lim));
+}
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 // Rows of a staged GEMM2 output tile (bf16, CH 16-byte chunks per row, LDS
 // row stride CH * 16) to their assignment slots in out [T*k, H]: thread t
@@ -1276,21 +1281,30 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
         // code table; the others are compile-time offsets from it
         uint8_t* const rowp = lds + (wm * BB + 4 * g) * BNA + wn * 32 + r;
         uint8_t* const codep = lds + BMT * BNA + (wm * BB + 4 * g) * (BNA / 32) + wn;
+        // the same code with and without the SwiGLU clamp (no limit: the
+        // clamp's three instructions per value are left out)
+        auto requant = [&](auto clamped) {
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+          for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v0 = swiglu(acc[fm][0][i], acc[fm][FN / 2][i], p.lim);
-            const float v1 = swiglu(acc[fm][1][i], acc[fm][FN / 2 + 1][i], p.lim);
-            // the wave's 32 columns of row lr are one MX group: its amax over
-            // the 16 lanes (one DPP row) that hold the row
-            const float m = row_max16(fmaxf(fabsf(v0), fabsf(v1)));
-            const uint32_t code = mx_group_code(m);
-            const float inv = e8m0_inv(code);
-            if (r == 0) codep[(fm * 16 + i) * (BNA / 32)] = (uint8_t)code;
-            rowp[(fm * 16 + i) * BNA] = (uint8_t)to_e4m3(clamp448(v0 * inv));
-            rowp[(fm * 16 + i) * BNA + 16] = (uint8_t)to_e4m3(clamp448(v1 * inv));
-          }
+            for (int i = 0; i < 4; ++i) {
+              const float v0 = decltype(clamped)::value ? swiglu(acc[fm][0][i], acc[fm][FN / 2][i], p.lim)
+                                                        : silu_mul(acc[fm][0][i], acc[fm][FN / 2][i]);
+              const float v1 = decltype(clamped)::value ? swiglu(acc[fm][1][i], acc[fm][FN / 2 + 1][i], p.lim)
+                                                        : silu_mul(acc[fm][1][i], acc[fm][FN / 2 + 1][i]);
+              // the wave's 32 columns of row lr are one MX group: its amax
+              // over the 16 lanes (one DPP row) that hold the row
+              const float m = row_max16(fmaxf(fabsf(v0), fabsf(v1)));
+              const uint32_t code = mx_group_code(m);
+              const float inv = e8m0_inv(code);
+              if (r == 0) codep[(fm * 16 + i) * (BNA / 32)] = (uint8_t)code;
+              // |v| <= m <= 448 x scale for finite values: no clamp needed
+              rowp[(fm * 16 + i) * BNA] = (uint8_t)to_e4m3(v0 * inv);
+              rowp[(fm * 16 + i) * BNA + 16] = (uint8_t)to_e4m3(v1 * inv);
+            }
+        };
+        if (p.lim < __builtin_inff()) requant(BoolTag<true>{});
+        else requant(BoolTag<false>{});
         __syncthreads();
         // the tile's BNA / 32 codes of a row are one 4-byte word of act_s
         if (tid < nrows)

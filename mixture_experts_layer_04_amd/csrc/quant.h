@@ -40,7 +40,18 @@ __device__ __forceinline__ float e8m0_inv(uint32_t code) { return __uint_as_floa
 // for bf16 inputs) to one side of it.  MX multiplies by e8m0_inv(code), an
 // exact power of two, which is the same value.
 __device__ __forceinline__ float fp8_group_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
-__device__ __forceinline__ uint32_t mx_group_code(float amax) { return e8m0_at_least(amax / 448.f); }
+// MX code without the division: for amax = 1.m x 2^(E-127) with E in
+// [10, 254], the fp32 quotient amax / 448 (448 = 1.75 x 2^8) rounds to at
+// most 2^e exactly when amax <= 448 x 2^e (the rounding boundary above
+// 448 x 2^e lies below the next fp32 value), so the code is E - 8, plus one
+// when m > 1.75 (mantissa field above 0x600000).  Other exponents (tiny or
+// non-finite amax) take the quotient.
+__device__ __forceinline__ uint32_t mx_group_code(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const uint32_t E = (u >> 23) & 0xFFu;
+  if (E >= 10u && E <= 254u) return E - 8u + (((u & 0x7FFFFFu) > 0x600000u) ? 1u : 0u);
+  return e8m0_at_least(amax / 448.f);
+}
 __device__ __forceinline__ float fp8_scaled(float v, float scale) { return clamp448(v / scale); }
 
 }  // namespace moe

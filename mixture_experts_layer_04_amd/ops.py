@@ -218,6 +218,16 @@ def probe_empty(device="cuda"):
     check(lib().moe_probe_empty(_stream(torch.device(device))), "moe_probe_empty")
 
 
+def probe_mfma(kind, accs, grid, iters, sink=None, device="cuda"):
+    """Enqueues the matrix-core issue-rate probe (kind: 0 bf16 16x16x32,
+    1 bf16 32x32x16, 2 e4m3 x e4m3, 3 e4m3 x e2m1, 4 e2m1 x e2m1)."""
+    dev = torch.device(device)
+    if sink is None:
+        sink = torch.empty(int(lib().moe_probe_mfma_sink_len(grid)), dtype=torch.float32, device=dev)
+    check(lib().moe_probe_mfma(kind, accs, grid, iters, _ptr(sink), _stream(dev)), "moe_probe_mfma")
+    return sink
+
+
 def probe_read(t, sink=None):
     """Reads every byte of ``t`` once (the bare weight-read kernel)."""
     nbytes = t.numel() * t.element_size()
