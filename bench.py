@@ -53,7 +53,7 @@ HBM_PEAK = 8.0e12  # B/s, MI355X published
 # profiles/mfma_rates.txt).
 MFMA_PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "mxfp4": 5.0e15}
 MFMA_ISSUED = {"bf16": "bf16 x bf16 (v_mfma_f32_16x16x32_bf16)",
-               "fp8": "e4m3 x e4m3 (v_mfma_scale_f32_16x16x128_f8f6f4)",
+               "fp8": "e4m3 x e4m3 (v_mfma_f32_16x16x128_f8f6f4)",
                "mxfp4": "e4m3 x e2m1 with e8m0 scales (v_mfma_scale_f32_16x16x128_f8f6f4)"}
 DTYPE = {"bf16": "bf16", "fp8": "fp8 (e4m3)", "mxfp4": "fp8 x fp4 (e4m3 x e2m1)"}
 METRIC = "MoE layer µs & tokens/s; HBM TB/s % (T≤256), MFMA % (T≥4k); router µs"

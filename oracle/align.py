@@ -10,7 +10,7 @@ offsets, the block-to-expert table with -1 after the padded length) and
 a = t*k + j, padding rows marked by the sentinel T*k, worst-case sizing
 T*k + E*(BLOCK_M-1) so the padded length can stay on the device).
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave a step open:
 
 * within one expert the assignments keep ascending a (a stable order, which
   is what the docstring example shows);

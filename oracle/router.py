@@ -12,7 +12,7 @@ weight (the unbiased score) is [Router] §1.3 "The Rank Key and the Weight"
 listing of [MoE] ("DeepSeek's actual routing is the grouped, bias-corrected
 variant").
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * ties in the rank key go to the lowest expert id ([Router] §5.3, Fig. 11;
   [Kernels] "Router: one fused kernel");
