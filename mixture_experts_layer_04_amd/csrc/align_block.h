@@ -41,9 +41,9 @@ AlignParams align_params(const int32_t* ids, int T, int k, int E, int block_m, i
 
 // Pair table of the paired tiled GEMMs from the scanned first rows
 // start[0..E] (LDS, start[E] = padded length): tab[0] = number of pairs,
-// tab[1 + j] = first block of pair j with bit 30 set when the pair holds two
-// blocks; an expert's blocks pair up from the first block of its run, in
-// expert order (the layout pair_table_kernel writes from the block table).
+// tab[1 + j] = pair_entry(first block of pair j, two blocks, window bits);
+// an expert's blocks pair up from the first block of its run, in expert
+// order (the layout pair_table_kernel writes from the block table).
 // Wave 0 scans the pair counts into pb[0..E] (LDS scratch); every thread
 // then writes the pairs of its experts.  Ends with a barrier.
 __device__ __forceinline__ void write_pair_table(const int* start, int E, int bm, int32_t* tab, int* pb) {
@@ -71,7 +71,9 @@ __device__ __forceinline__ void write_pair_table(const int* start, int E, int bm
   for (int e = tid; e < E; e += NT) {
     const int nb = (start[e + 1] - start[e]) / bm;
     const int b0 = start[e] / bm;
-    for (int j = 0; 2 * j < nb; ++j) tab[1 + pb[e] + j] = (b0 + 2 * j) | (2 * j + 1 < nb ? (1 << 30) : 0);
+    const int m = (nb + 1) / 2;  // the expert's pairs
+    for (int j = 0; j < m; ++j)
+      tab[1 + pb[e] + j] = pair_entry(b0 + 2 * j, 2 * j + 1 < nb, (j & 1) == 0 && j + 1 < m, (j & 1) == 1);
   }
   if (tid == 0) tab[0] = pb[E];
   __syncthreads();

@@ -106,6 +106,51 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(const bf16x8_t& a, const b
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Pair table entries of the paired GEMM tiles: the first block of the pair
+// (bits 0-28), bit 30 when it holds two blocks, and two window bits.  The
+// pairs of one expert form windows of two (its pairs 0 and 1, 2 and 3, ...;
+// a last odd pair is a window of one): bit 29 marks the first pair of a
+// window of two, bit 31 the second.  A window's N tiles run interleaved,
+// (pair 0, n 0), (pair 1, n 0), (pair 0, n 1), ..., so the two tiles that
+// read the same weight rows run side by side.
+constexpr int32_t kPairTwo = 1 << 30;
+constexpr int32_t kPairWinFirst = 1 << 29;
+constexpr int32_t kPairWinSecond = (int32_t)0x80000000u;
+constexpr int32_t kPairBlockMask = (1 << 29) - 1;
+__device__ __forceinline__ int32_t pair_entry(int first_block, bool two, bool win_first, bool win_second) {
+  return first_block | (two ? kPairTwo : 0) | (win_first ? kPairWinFirst : 0) | (win_second ? kPairWinSecond : 0);
+}
+struct PairTile {
+  int blk;   // first block
+  bool two;  // two blocks
+  int nt;    // N tile
+};
+// Logical tile L (pair-major numbering: L / ntn is a pair, counted over the
+// table's entries) of a table with ntn N tiles per pair, with each window's
+// tiles interleaved.  A window of pairs [w, w + sz) owns the logical tiles
+// [w ntn, (w + sz) ntn); tile w ntn + i is pair w + i % sz, N tile i / sz.
+// npairs bounds the entries read (L < npairs ntn), also for a table whose
+// window bits do not match its count.  WIN = false: plain pair-major order
+// (the window bits are ignored).
+template <bool WIN>
+__device__ __forceinline__ PairTile pair_tile(const int32_t* pairs, int npairs, int64_t L, int ntn) {
+  const int jj = (int)(L / ntn);
+  const int32_t fw = __builtin_amdgcn_readfirstlane(pairs[1 + jj]);
+  int w = jj, sz = 1;
+  if (!WIN) {
+    // nothing to do: one pair per window
+  } else if ((fw & kPairWinFirst) && jj + 1 < npairs) {
+    sz = 2;
+  } else if ((fw & kPairWinSecond) && jj > 0) {
+    w = jj - 1;
+    sz = 2;
+  }
+  const int64_t local = L - (int64_t)ntn * w;
+  const int entry = w + (int)(local % sz);
+  const int32_t pe = entry == jj ? fw : __builtin_amdgcn_readfirstlane(pairs[1 + entry]);
+  return PairTile{(int)(pe & kPairBlockMask), (pe & kPairTwo) != 0, (int)(local / sz)};
+}
+
 }  // namespace moe
 
 // Launch-side helpers (host).

@@ -724,10 +724,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 // ahead) and B (three slots, two steps ahead).
 
 // Pair table: tab[0] = number of pairs, tab[1 + j] = first block of pair j
-// with bit 30 set when the pair holds two blocks.  One workgroup walks the
-// blocks 1024 at a time: an inclusive max-scan of the run starts gives each
-// block the first block of its expert's run, a sum-scan numbers the blocks
-// that start a pair (an even distance from that first block).
+// (bits 0-28), bit 30 set when the pair holds two blocks, and the window
+// bits of pair_tile (common.h): bit 29 when pair j + 1 is the next pair of
+// the same expert and j is an even pair of its expert, bit 31 when j is an
+// odd one.  One workgroup walks the blocks 1024 at a time: an inclusive
+// max-scan of the run starts gives each block the first block of its
+// expert's run, a sum-scan numbers the blocks that start a pair (an even
+// distance from that first block).
 __global__ __launch_bounds__(1024) void pair_table_kernel(const int32_t* be, const int32_t* npp, int bm,
                                                           int32_t* tab) {
   __shared__ int s_max[16];
@@ -767,7 +770,9 @@ __global__ __launch_bounds__(1024) void pair_table_kernel(const int32_t* be, con
     }
     if (start) {
       const bool two = b + 1 < nblk && be[b + 1] == e;
-      tab[1 + carry_pairs + before + pos] = b | (two ? (1 << 30) : 0);
+      const bool next = b + 2 < nblk && be[b + 2] == e;  // the expert has another pair
+      const bool odd = ((b - fb) >> 1) & 1;              // pair index within the expert
+      tab[1 + carry_pairs + before + pos] = pair_entry(b, two, !odd && next, odd);
     }
     carry_first = cf;
     carry_pairs += total;
@@ -865,10 +870,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
     if (j >= per || L >= n_valid) break;
     // tile values are uniform; readfirstlane keeps them (and the buffer
     // descriptors made from them) in scalar registers
-    const int pe = __builtin_amdgcn_readfirstlane(p.pairs[1 + (int)(L / ntn)]);
-    const int nt = (int)(L % ntn);
-    const int blk = pe & 0x3FFFFFFF;  // first block of the tile
-    const bool two = (pe >> 30) & 1;
+    // plain pair-major order (measured: interleaving an expert's pairs left
+    // the MXFP4 kernel 1-3 % faster and this one's GEMM1 2 % slower at
+    // Qwen3 T=4096)
+    const PairTile pt = pair_tile<false>(p.pairs, npairs, L, ntn);
+    const int nt = pt.nt;
+    const int blk = pt.blk;  // first block of the tile
+    const bool two = pt.two;
     if (blk + (two ? 1 : 0) < nblk) {
       const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
       const bool mine = wm == 0 || two;  // this wave's block exists
@@ -1126,10 +1134,12 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   for (;; ) {
     const int64_t L = (int64_t)xcd * per + j;
     if (j >= per || L >= n_valid) break;
-    const int pe = __builtin_amdgcn_readfirstlane(p.pairs[1 + (int)(L / ntn)]);
-    const int nt = (int)(L % ntn);
-    const int blk = pe & 0x3FFFFFFF;  // first block of the tile
-    const bool two = (pe >> 30) & 1;
+    // an expert's pairs interleaved by N tile (measured, DSV4 T=8192: GEMM1
+    // 1155 -> 1140 us, GEMM2 598 -> 581 us)
+    const PairTile pt = pair_tile<true>(p.pairs, npairs, L, ntn);
+    const int nt = pt.nt;
+    const int blk = pt.blk;  // first block of the tile
+    const bool two = pt.two;
     if (blk + (two ? 1 : 0) < nblk) {
       const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
       const bool mine = wm == 0 || two;  // this wave's block exists
