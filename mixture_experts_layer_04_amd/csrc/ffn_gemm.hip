@@ -719,9 +719,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_tiled(GemmP p) {
 // missing half is neither copied (an empty buffer range returns zeros
 // without touching memory) nor multiplied.  8 waves as 2 x 4, two per SIMD,
 // each one block's rows x 64 weight rows (GEMM1: 32 gate rows and the
-// matching 32 up rows), one fragment set; K steps of 128 bytes per row (two
-// 32-wide MFMA steps) with separate LDS rings for A (two slots, one step
-// ahead) and B (three slots, two steps ahead).
+// matching 32 up rows); K steps of 128 bytes per row (two 32-wide MFMA
+// steps) with separate LDS rings for A (two slots, one step ahead) and B
+// (three slots, two steps ahead).  Per sub-step a wave reads its weight
+// fragments, then its A fragments one at a time, each read issued before
+// the MFMAs of the previous one.
 
 // Pair table: tab[0] = number of pairs, tab[1 + j] = first block of pair j
 // (bits 0-28), bit 30 set when the pair holds two blocks, and the window
@@ -924,30 +926,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
   #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-      struct Frag {
-        bf16x8_t a[FM];
-        bf16x8_t b[FN];
-      };
-      auto rd = [&](int s, int ks, Frag& f) {
-        const uint8_t* As = lds + (s % NA) * ASZ;
-        const uint8_t* Bs = lds + NA * ASZ + (s % NB) * BSZ;
-  #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int rr = wm * BB + fm * 16 + r;
-          f.a[fm] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(rr, 4 * ks + g));
-        }
-  #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int rr = frag_lrow(fn) + r;
-          f.b[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rr, 4 * ks + g));
-        }
-      };
-      auto mm = [&](const Frag& f) {
-  #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-  #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(f.a[fm], f.b[fn], acc[fm][fn]);
-      };
       // Before step sn: this wave's LDS reads are done (lgkmcnt), its copies
       // of A(sn) and B(sn) have landed (vmcnt: only B(sn + 1), the copies
       // issued last, may remain), barrier, then A(sn + 1) into the A slot of
@@ -966,11 +944,37 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
       for (int s = 0; s < nk; ++s) {
         next_step(s);
         if (mine) {
+          // per 32-wide sub-step: the weight fragments, then the A fragments
+          // one at a time, each read issued before the MFMAs of the previous
+          // (measured, Qwen3 T=4096: GEMM1 344 -> 330 us against reading all
+          // fragments of a sub-step, then multiplying)
+          const uint8_t* As = lds + (s % NA) * ASZ;
+          const uint8_t* Bs = lds + NA * ASZ + (s % NB) * BSZ;
   #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            Frag f;
-            rd(s, ks, f);
-            mm(f);
+            bf16x8_t bfr[FN];
+  #pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+              bfr[fn] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(frag_lrow(fn) + r, 4 * ks + g));
+            auto read_a = [&](int fm) {
+              return *reinterpret_cast<const bf16x8_t*>(As + lds_off(wm * BB + fm * 16 + r, 4 * ks + g));
+            };
+            auto mult = [&](int fm, const bf16x8_t& a) {
+  #pragma unroll
+              for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32_bf16(a, bfr[fn], acc[fm][fn]);
+            };
+            bf16x8_t a0 = read_a(0), a1;
+  #pragma unroll
+            for (int fm = 0; fm < FM; fm += 2) {
+              a1 = read_a(fm + 1);
+              __builtin_amdgcn_sched_barrier(0);
+              mult(fm, a0);
+              __builtin_amdgcn_sched_barrier(0);
+              if (fm + 2 < FM) a0 = read_a(fm + 2);
+              __builtin_amdgcn_sched_barrier(0);
+              mult(fm + 1, a1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         }
       }
