@@ -454,14 +454,14 @@ EP_SHARE_T = (1, 4, 16, 64, 512)
 EP_SHARE_PAGE_US = {1: 40.0, 4: 68.0, 16: 95.0, 64: 99.0, 512: 112.0}  # B300, the page's figures
 
 
-def ep_share_sweep(moe, torch, flush, reps):
+def ep_share_sweep(moe, torch, flush, reps, Ts=EP_SHARE_T):
     """Cold alignment + expert FFN (fp8 quantisation, both grouped GEMMs and
     the combine) for 32 MXFP4 experts, k = 6, at the page's token counts."""
     from synth import get_config, make_topk_ids, make_weights, make_x
     cfg = get_config("dsv4", E=32)
     W = make_weights(cfg, "cuda")
     out = {}
-    for T in EP_SHARE_T:
+    for T in Ts:
         x = make_x(cfg, T, "cuda")
         ids = make_topk_ids(T, cfg.k, cfg.E, seed=T, kind="uniform", device="cuda")
         g = torch.Generator(device="cpu").manual_seed(T)
@@ -561,7 +561,8 @@ def main():
     ap.add_argument("--only", choices=("decode", "prefill", "router", "ep", "mfma"),
                     help="diagnostic: only these rows (for kernel traces), no benchmark line")
     ap.add_argument("--cases", metavar="NAME:T,...",
-                    help="with --only decode / prefill: just these cases (e.g. glm:1,dsv3:256)")
+                    help="with --only decode / prefill: just these cases (e.g. glm:1,dsv3:256); with --only ep: "
+                         "token counts (e.g. 1,512)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="print per-kernel durations / counters of a rocprofv3 csv output directory and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -588,12 +589,13 @@ def main():
     flush = Flush(moe, torch)
     if args.only:
         pick = None
-        if args.cases:
+        if args.cases and args.only in ("decode", "prefill"):
             pick = tuple((c.split(":")[0], int(c.split(":")[1])) for c in args.cases.split(","))
         rows = {"decode": lambda: layer_sweep(moe, torch, flush, pick or DECODE, args.reps, False),
                 "prefill": lambda: layer_sweep(moe, torch, flush, pick or PREFILL, args.reps, True),
                 "router": lambda: router_probe(moe, torch, flush, args.reps),
-                "ep": lambda: ep_share_sweep(moe, torch, flush, args.reps),
+                "ep": lambda: ep_share_sweep(moe, torch, flush, args.reps,
+                                             tuple(int(t) for t in args.cases.split(",")) if args.cases else EP_SHARE_T),
                 "mfma": lambda: mfma_rates(moe, torch)}[args.only]()
         for key, v in rows.items():
             log(f"{key}: {v}")
