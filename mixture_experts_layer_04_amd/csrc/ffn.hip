@@ -111,7 +111,8 @@ Layout ffn_layout(int T, int H, int E, int F, int k, int block_m, int wformat) {
   L.out = off;
   off += align_up((size_t)T * k * H * 2, 256);
   L.pairs = off;
-  off += ffn_paired(wformat, block_m) ? align_up(((size_t)align_max_blocks(T, k, E, block_m) + 1) * 4, 256) : 0;
+  off += ffn_paired(wformat, block_m, T, k, E) ? align_up(((size_t)align_max_blocks(T, k, E, block_m) + 1) * 4, 256)
+                                                : 0;
   L.total = off;
   return L;
 }
@@ -130,7 +131,7 @@ void ffn_carve(FfnArgs& a, void* ws) {
   a.act_s = b + L.act_s;
   a.act32 = b + L.act32;
   a.out = b + L.out;
-  a.pairs = ffn_paired(a.wformat, a.block_m) ? b + L.pairs : nullptr;
+  a.pairs = ffn_paired(a.wformat, a.block_m, a.T, a.k, a.E) ? b + L.pairs : nullptr;
 }
 
 static moe_status launch_gemm(const FfnArgs& a, int which, hipStream_t s) {

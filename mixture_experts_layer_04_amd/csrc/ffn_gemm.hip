@@ -1755,6 +1755,12 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
   constexpr int NW = (F == F_MX) ? 4 : MOE_TILED_WAVES;
   switch (a.block_m) {
     case 32:  // MX: 256-wide K steps (measured: faster here; at 64 and 128 rows slower, one workgroup per CU)
+      if constexpr (F == F_BF16) {
+        if (a.pairs) {
+          if (which == 1) return launch_pair_one<true, 32>(p, t1, s);
+          if (a.H % 256 == 0) return launch_pair_one<false, 32>(p, t2 / 2, s);
+        }
+      }
       if (which == 1) return launch_tiled_one<F, true, 32, 256, 3, 4, 2>(p, t1, s);
       // MX GEMM2: 256 output columns once that still leaves >= 2048 tiles
       // (measured: DSV4 T=512 layer 770 -> 753 us; with fewer tiles, as for
@@ -1808,8 +1814,17 @@ moe_status launch_gemm_fmt(const FfnArgs& a, int which, hipStream_t s) {
 #ifndef MOE_PAIRED_TILES
 #define MOE_PAIRED_TILES 1
 #endif
-bool ffn_paired(int wformat, int block_m) {
-  return MOE_PAIRED_TILES && (wformat == MOE_W_BF16 || wformat == MOE_W_MXFP4) && (block_m == 128 || block_m == 64);
+bool ffn_paired(int wformat, int block_m, int T, int k, int E) {
+  if (!MOE_PAIRED_TILES) return false;
+  if (block_m == 64 || block_m == 128) return wformat == MOE_W_BF16 || wformat == MOE_W_MXFP4;
+  // bf16 at 32 rows: pairs of 32-row blocks once the experts average two
+  // rows or more and the alignment has a launch of its own (above 64
+  // assignments).  Measured (cold layers, against the 32-row tiled kernel):
+  // GLM T=512 2078 -> 1849 us (the selection bias gives some experts many
+  // blocks, each of which the tiled kernel copies the weights for), Qwen3
+  // T=64 level; GLM T=8 (single blocks) 527 -> 549 us and the toy T=16
+  // layer (an extra pair-table launch) 25 -> 30 us are why the cuts exist.
+  return wformat == MOE_W_BF16 && block_m == 32 && (int64_t)T * k >= 2 * (int64_t)E && (int64_t)T * k > 64;
 }
 
 moe_status launch_pair_table(const FfnArgs& a, hipStream_t s) {

@@ -95,7 +95,7 @@ moe_status ffn_validate(const void* x, int wformat, const void* w13, const void*
 size_t ffn_workspace_size(int T, int H, int E, int F, int k, int block_m, int wformat);
 // Whether the grouped GEMMs run the paired tiled kernel (two blocks of one
 // expert per tile), which needs the pair table built first.
-bool ffn_paired(int wformat, int block_m);
+bool ffn_paired(int wformat, int block_m, int T, int k, int E);
 moe_status launch_pair_table(const FfnArgs& a, hipStream_t stream);
 void ffn_carve(FfnArgs& a, void* ws);
 moe_status launch_ffn(const FfnArgs& a, hipStream_t stream);

@@ -193,7 +193,7 @@ CASES = [("bf16", 256, 256, bm, T) for bm, T in ((16, 5), (16, 300), (32, 300), 
                                                                        (64, 200), (128, 200))]
 
 
-# bf16 at BLOCK_M 64 and 128 runs the paired tiles (two blocks of one
+# bf16 at BLOCK_M 64 and 128 (and 32 with enough rows per expert) runs the paired tiles (two blocks of one
 # expert per tile): experts with an even and an odd number of blocks (uniform ids: 375
 # and 500 rows per expert), uneven counts from skewed ids, one expert with
 # one block (the hot expert set leaves the others empty), and a block table
@@ -203,7 +203,12 @@ PAIRED = [("bf16", 256, 256, 128, 1500, "uniform", None), ("bf16", 512, 384, 128
           ("bf16", 256, 512, 128, 3000, "skewed", None), ("bf16", 256, 256, 128, 100, "hot", None),
           ("bf16", 256, 128, 128, 70000, "uniform", None),
           # 64-row blocks paired too: an odd count (175 rows per expert) and uneven ones
-          ("bf16", 512, 384, 64, 700, "uniform", None), ("bf16", 256, 256, 64, 1100, "skewed", None)]
+          ("bf16", 512, 384, 64, 700, "uniform", None), ("bf16", 256, 256, 64, 1100, "skewed", None),
+          # and 32-row blocks (paired once the experts average two rows or more
+          # and there are more than 64 assignments): odd and uneven counts, and
+          # more tiles than the XCDs' workgroups (per-XCD queues)
+          ("bf16", 512, 384, 32, 700, "uniform", None), ("bf16", 256, 256, 32, 1100, "skewed", None),
+          ("bf16", 256, 128, 32, 20000, "uniform", None)]
 
 
 def _run_exact(fmt, H, F, bm, T, kind="uniform", sample=None, pow2=False):
