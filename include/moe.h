@@ -346,7 +346,7 @@ moe_status moe_layer_noalloc(const void* x, const float* gate, const float* bias
                              hipStream_t stream);
 
 /* The block size moe_layer uses for block_m = 0, from the mean rows per
- * expert m = T*k/E: 32 if 2 <= m <= 24, then 64 while m <= 96 (m <= 52 for
+ * expert m = T*k/E: 32 if 2 <= m <= 24, then 64 while m <= 96 (m <= 44 for
  * MOE_W_FP8_BLOCK128), else 128.  Below
  * m = 2: 16 for MOE_W_FP8_BLOCK128; for bf16 and MXFP4, 32 once the
  * expected number of 32-row GEMM1 tiles, E (1 - (1 - k/E)^T) * 2F / 256,

@@ -86,10 +86,10 @@ int layer_block_m(int T, int k, int E, int F, int wformat) {
   }
   if (m <= 24.0) return 32;
   // fp8 (the tiled kernel, which copies an expert's weight tile once per
-  // block): 128 rows from m = 56 on (measured, DSV3 layers, 64 against 128
-  // rows: m = 40 2260 / 2465 us, m = 48 2404 / 2502, m = 56 2582 / 2547,
-  // m = 64 2730 / 2591, m = 128 4197 / 3776)
-  if (wformat == MOE_W_FP8_BLOCK128) return m <= 52.0 ? 64 : 128;
+  // block and skips the fragments of padding rows): 128 rows from m = 48 on
+  // (measured, DSV3 layers, 64 against 128 rows: m = 32 2148 / 2186 us,
+  // m = 40 2212 / 2237, m = 48 2357 / 2272, m = 64 2670 / 2374)
+  if (wformat == MOE_W_FP8_BLOCK128) return m <= 44.0 ? 64 : 128;
   if (m <= 96.0) return 64;
   return 128;
 }

@@ -138,8 +138,9 @@ def test_block_m_choice(L):
     # (T, E, F, k, wformat): from 2 rows per expert on, by rows per expert
     assert L.moe_layer_block_m(64, 256, 2048, 8, fp8) == 32
     assert L.moe_layer_block_m(4096, 128, 768, 8, bf16) == 128
-    assert L.moe_layer_block_m(2048, 256, 2048, 8, fp8) == 128  # m = 64: fp8 turns to 128 rows above 52
-    assert L.moe_layer_block_m(1536, 256, 2048, 8, fp8) == 64   # m = 48
+    assert L.moe_layer_block_m(2048, 256, 2048, 8, fp8) == 128  # m = 64: fp8 turns to 128 rows above 44
+    assert L.moe_layer_block_m(1536, 256, 2048, 8, fp8) == 128  # m = 48
+    assert L.moe_layer_block_m(1280, 256, 2048, 8, fp8) == 64   # m = 40
     assert L.moe_layer_block_m(2048, 256, 2048, 8, bf16) == 64  # m = 64: the others at 96
     assert L.moe_layer_block_m(384, 128, 768, 8, bf16) == 32   # m = 24
     assert L.moe_layer_block_m(448, 128, 768, 8, bf16) == 64   # m = 28
