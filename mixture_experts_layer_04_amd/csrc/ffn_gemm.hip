@@ -1057,13 +1057,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
 //
 // Copies.  Waves 0-3 copy the A rows (one step ahead: they come from the L2,
 // where the rows of a pair serve all its N tiles) and waves 4-7 the weight
-// rows (four steps ahead: they come from HBM).  A wave's copies complete in
+// rows (three steps ahead: they come from HBM).  A wave's copies complete in
 // issue order, so a wave that copied both would have to wait for its
 // younger weight copies whenever it waits for an A step; split, each half
-// waits for its own stream only.  LDS: two A slots, five weight slots and
-// two slots of e8m0 scales, 160 KiB at BB = 128.  The scales (one byte per
-// row and 32-wide K group) are copied 16 bytes per row at a time, four
-// steps' worth (a CU keeps a fixed number of copy requests in flight).
+// waits for its own stream only.  LDS: two A slots, four weight slots and
+// two slots of e8m0 scales, 144 KiB at BB = 128 (four steps ahead in five
+// slots, 160 KiB, took 2-3 % longer in both GEMMs, DSV4 T=8192; two ahead
+// longer again).  The scales (one byte per row and 32-wide K group) are
+// copied 16 bytes per row at a time, four steps' worth (a CU keeps a fixed
+// number of copy requests in flight).
+//
+// Tiles.  Each workgroup loops over tiles from its XCD's queue.  GEMM1
+// issues the next tile's copies ahead of step 0 before its epilogue, which
+// then runs while they land; the weight waves store the epilogue's rows.
 //
 // Multiply.  Per step a wave reads its weight fragments, then its A
 // fragments one at a time, each read issued before the MFMAs of the
@@ -1078,7 +1084,7 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   constexpr int ARB = 128, BRB = 64;   // A / B bytes per row and step
   constexpr int ASZ = BMT * ARB;       // one A slot
   constexpr int BSZ = BNW * BRB;       // one weight slot
-  constexpr int NA = 2, NB = 5;        // slots: A one step ahead, weights four
+  constexpr int NA = 2, NB = 4;        // slots: A one step ahead, weights three
   constexpr int DA = NA - 1, DB = NB - 1;
   constexpr int SCG = 4;               // steps per scale group
   constexpr int SCSZ = NT * 16;        // a scale group: 16 bytes per row, A rows then weight rows
@@ -1148,225 +1154,314 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   const int xcd = blockIdx.x & 7;
   const int wpx = (int)(gridDim.x >> 3);
   const bool dyn = per > wpx;
-  int j = (int)(blockIdx.x >> 3);
-  for (;; ) {
-    const int64_t L = (int64_t)xcd * per + j;
-    if (j >= per || L >= n_valid) break;
+  auto in_range = [&](int jx) { return jx < per && (int64_t)xcd * per + jx < n_valid; };
+
+  // One tile's copy state: its blocks and N tile, and the copy sources of
+  // this wave's stream.
+  constexpr int LC = LA > LB ? LA : LB;
+  struct Tile {
+    int nt, blk, e;
+    bool two;
+    bool ok;         // the tile lies inside the blocks (tiles of a stale pair table are skipped)
+    bool copy_rows;  // A waves: this wave's rows exist
+    uint32_t sg;
+    uint32_t cg[LC];
+  };
+  // the copy sources as buffer descriptors (rebuilt from the tile's fields:
+  // kept in a struct, the descriptor type ended up in scratch memory)
+  auto src_rc = [&](const Tile& t) {
+    return bwave ? make_rsrc(wsrc + (size_t)t.e * erows * rowbytes_b, (uint64_t)erows * rowbytes_b)
+                 : (t.copy_rows ? ra : rnone);
+  };
+  auto src_rs = [&](const Tile& t) {
+    return bwave ? make_rsrc(wscale + (size_t)t.e * erows * kgroups, (uint64_t)erows * kgroups) : ras;
+  };
+  auto setup = [&](int jx) {
+    Tile t;
     // an expert's pairs interleaved by N tile (measured, DSV4 T=8192: GEMM1
     // 1155 -> 1140 us, GEMM2 598 -> 581 us)
-    const PairTile pt = pair_tile<true>(p.pairs, npairs, L, ntn);
-    const int nt = pt.nt;
-    const int blk = pt.blk;  // first block of the tile
-    const bool two = pt.two;
-    if (blk + (two ? 1 : 0) < nblk) {
-      const int e = __builtin_amdgcn_readfirstlane(p.block_expert[blk]);
-      const bool mine = wm == 0 || two;  // this wave's block exists
-
-      // This wave's copy stream.  A waves: tile rows [RA cw, +RA), 8 per
-      // instruction (rows of a missing second block from the empty range).
-      // Weight waves: weight rows [RB cw, +RB), 16 per instruction.
-      const bool copy_rows = (cw * RA < BB) || two;
-      const rsrc_t rb = make_rsrc(wsrc + (size_t)e * erows * rowbytes_b, (uint64_t)erows * rowbytes_b);
-      const rsrc_t rc = bwave ? rb : (copy_rows ? ra : rnone);
-      constexpr int LC = LA > LB ? LA : LB;
-      uint32_t cg[LC];
+    const PairTile pt = pair_tile<true>(p.pairs, npairs, (int64_t)xcd * per + jx, ntn);
+    t.nt = pt.nt;
+    t.blk = pt.blk;
+    t.two = pt.two;
+    t.ok = pt.blk + (pt.two ? 1 : 0) < nblk;
+    t.e = 0;
+    t.copy_rows = false;
+    t.sg = 0u;
 #pragma unroll
-      for (int i = 0; i < LC; ++i) {
-        if (bwave) {
-          const int rr = cw * RB + 16 * i + lane / 4;
-          const int c = (lane % 4) ^ ((rr >> 1) & 3);
-          cg[i] = i < LB ? (uint32_t)weight_row(nt, rr) * rowbytes_b + 16 * c : 0u;
-        } else {
-          const int rr = cw * RA + 8 * i + lane / 8;
-          const int c = (lane % 8) ^ ((rr >> 1) & 7);
-          bool v;
-          const int src = (i < LA && copy_rows) ? a_row_index<G1>(p, blk, BB, rr, v) : 0;  // padding: row 0
-          cg[i] = (uint32_t)src * rowbytes_a + 16 * c;
-        }
-      }
-      // scale groups: 16 bytes of A row q (A waves, q = tid < BMT; the rest
-      // and rows of a missing block read the tile's first row) or of weight
-      // row q = tid - 256 (weight waves); the descriptor is wave-uniform
-      rsrc_t rs;
-      uint32_t sg;
+    for (int i = 0; i < LC; ++i) t.cg[i] = 0u;
+    if (!t.ok) return t;
+    t.e = __builtin_amdgcn_readfirstlane(p.block_expert[t.blk]);
+    // This wave's copy stream.  A waves: tile rows [RA cw, +RA), 8 per
+    // instruction (rows of a missing second block from the empty range).
+    // Weight waves: weight rows [RB cw, +RB), 16 per instruction.
+    t.copy_rows = (cw * RA < BB) || t.two;
+#pragma unroll
+    for (int i = 0; i < LC; ++i) {
       if (bwave) {
-        rs = make_rsrc(wscale + (size_t)e * erows * kgroups, (uint64_t)erows * kgroups);
-        sg = (uint32_t)weight_row(nt, tid - CW * 64) * kgroups;
+        const int rr = cw * RB + 16 * i + lane / 4;
+        const int c = (lane % 4) ^ ((rr >> 1) & 3);
+        t.cg[i] = i < LB ? (uint32_t)weight_row(t.nt, rr) * rowbytes_b + 16 * c : 0u;
       } else {
-        const int q = tid < BMT ? tid : 0;
+        const int rr = cw * RA + 8 * i + lane / 8;
+        const int c = (lane % 8) ^ ((rr >> 1) & 7);
         bool v;
-        rs = ras;
-        sg = (uint32_t)a_row_index<G1>(p, blk, BB, (q < BB || two) ? q : 0, v) * kgroups;
+        const int src = (i < LA && t.copy_rows) ? a_row_index<G1>(p, t.blk, BB, rr, v) : 0;  // padding: row 0
+        t.cg[i] = (uint32_t)src * rowbytes_a + 16 * c;
       }
-      // step s's copies of this wave's stream (none past the last step)
-      auto issue = [&](int s) {
-        if (s >= nk) return;
-        if (bwave) {
-          uint8_t* st = lds + BBASE + (s % NB) * BSZ + cw * RB * BRB;
+    }
+    // scale groups: 16 bytes of A row q (A waves, q = tid < BMT; the rest
+    // and rows of a missing block read the tile's first row) or of weight
+    // row q = tid - 256 (weight waves); the descriptor is wave-uniform
+    if (bwave) {
+      t.sg = (uint32_t)weight_row(t.nt, tid - CW * 64) * kgroups;
+    } else {
+      const int q = tid < BMT ? tid : 0;
+      bool v;
+      t.sg = (uint32_t)a_row_index<G1>(p, t.blk, BB, (q < BB || t.two) ? q : 0, v) * kgroups;
+    }
+    return t;
+  };
+  // step s's copies of this wave's stream (none past the last step)
+  auto issue = [&](const Tile& t, int s) {
+    if (s >= nk) return;
+    const rsrc_t rc = src_rc(t);
+    if (bwave) {
+      uint8_t* st = lds + BBASE + (s % NB) * BSZ + cw * RB * BRB;
 #pragma unroll
-          for (int i = 0; i < LB; ++i) buf2lds16(rc, cg[i], s * BRB, st + 16 * i * BRB);
-        } else {
-          uint8_t* st = lds + ABASE + (s % NA) * ASZ + cw * RA * ARB;
+      for (int i = 0; i < LB; ++i) buf2lds16(rc, t.cg[i], s * BRB, st + 16 * i * BRB);
+    } else {
+      uint8_t* st = lds + ABASE + (s % NA) * ASZ + cw * RA * ARB;
 #pragma unroll
-          for (int i = 0; i < LA; ++i) buf2lds16(rc, cg[i], s * ARB, st + 8 * i * ARB);
-        }
-      };
-      auto issue_sc = [&](int G) {
-        if (G >= ng) return;
-        buf2lds16(rs, sg, G * 16, lds + SBASE + (G & 1) * SCSZ + wave * 1024);
-      };
+      for (int i = 0; i < LA; ++i) buf2lds16(rc, t.cg[i], s * ARB, st + 8 * i * ARB);
+    }
+  };
+  auto issue_sc = [&](const Tile& t, int G) {
+    if (G >= ng) return;
+    buf2lds16(src_rs(t), t.sg, G * 16, lds + SBASE + (G & 1) * SCSZ + wave * 1024);
+  };
+  // the copies ahead of step 0: scale group 0, then A step 0 or weight
+  // steps 0 .. DB - 1 (into A slot 0, weight slots 0 .. DB - 1, scale slot 0)
+  auto prologue = [&](const Tile& t) {
+    issue_sc(t, 0);
+    if (bwave) {
+#pragma unroll
+      for (int s = 0; s < DB; ++s) issue(t, s);
+    } else {
+      issue(t, 0);
+    }
+  };
 
-      f32x4_t acc[FM][FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Taking a tile from the XCD's queue: thread 0's atomic, then the index
+  // through an LDS word (in scale slot 1, which the copies ahead of a tile's
+  // step 0 leave alone) and one barrier.
+  int* const ctl = reinterpret_cast<int*>(lds + SBASE + SCSZ);
+  int taken = 0;
+  auto take_issue = [&]() {
+    if (tid == 0) taken = atomicAdd(p.queue + xcd, 1);
+  };
+  auto take_finish = [&]() {
+    if (tid == 0) *reinterpret_cast<volatile int*>(ctl) = wpx + taken;
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(ctl));
+  };
 
-      issue_sc(0);
-      if (bwave) {
-#pragma unroll
-        for (int s = 0; s < DB; ++s) issue(s);
-      } else {
-        issue(0);
-      }
-      for (int s = 0; s < nk; ++s) {
-        // Every wave has read the slots about to be refilled (lgkmcnt(0)) and
-        // this wave's copies of step s have landed: A waves wait for all of
-        // theirs but the scale group issued at step s - 1 (if any); weight
-        // waves leave the copies of steps s + 1 .. s + 3 in flight (and the
-        // scale group one of those steps issued).  Near the end, where
-        // fewer copies follow step s's, both wait for all of them.  Then
-        // the barrier, and the copies of steps s + 1 (A) / s + 4 (weights)
-        // and of the next scale group.
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
-        if (s + DB > nk) {
-          wait_vm<0>();
-        } else if (bwave) {
-          if (s % SCG == 0) wait_vm<LB * (DB - 1)>();
-          else wait_vm<LB * (DB - 1) + 1>();
-        } else {
-          if (s % SCG == 1 && s + SCG <= nk) wait_vm<1>();
-          else wait_vm<0>();
-        }
-        barrier_no_fence();
-        issue(s + (bwave ? DB : DA));
-        if (s % SCG == 0) issue_sc(s / SCG + 1);
-        if (mine) {
-          const uint8_t* As = lds + ABASE + (s % NA) * ASZ;
-          const uint8_t* Bs = lds + BBASE + (s % NB) * BSZ;
-          // row q's byte for K group g of step s: 16 q + 4 (s % 4) + g
-          const uint8_t* Ss = lds + SBASE + ((s / SCG) & 1) * SCSZ + 4 * (s % SCG);
-          i32x4_t bfr[FN];
-          int sb[FN];
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int rr = frag_lrow(fn) + r;
-            bfr[fn] = *reinterpret_cast<const i32x4_t*>(Bs + b_off(rr, g));
-            sb[fn] = (int)Ss[(CW * 64 + rr) * 16 + g];
-          }
-          auto read_a = [&](int fm, i32x4_t& lo, i32x4_t& hi, int& sa) {
-            const int rr = wm * BB + fm * 16 + r;
-            lo = *reinterpret_cast<const i32x4_t*>(As + a_off(rr, g));
-            hi = *reinterpret_cast<const i32x4_t*>(As + a_off(rr, 4 + g));
-            sa = (int)Ss[rr * 16 + g];
-          };
-          auto mult = [&](int fm, const i32x4_t& lo, const i32x4_t& hi, int sa) {
-            const i32x8_t af = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-              const i32x4_t v = bfr[fn];
-              acc[fm][fn] = mfma_mx(af, i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0}, acc[fm][fn], sa, sb[fn]);
-            }
-          };
-          // A fragments in two register sets: the reads of fragment fm + 1
-          // go out before the MFMAs of fragment fm
-          i32x4_t lo0, hi0, lo1, hi1;
-          int sa0, sa1;
-          read_a(0, lo0, hi0, sa0);
-#pragma unroll
-          for (int fm = 0; fm < FM; fm += 2) {
-            read_a(fm + 1, lo1, hi1, sa1);
-            __builtin_amdgcn_sched_barrier(0);
-            mult(fm, lo0, hi0, sa0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (fm + 2 < FM) read_a(fm + 2, lo0, hi0, sa0);
-            __builtin_amdgcn_sched_barrier(0);
-            mult(fm + 1, lo1, hi1, sa1);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      wait_vm<0>();     // the copies past the last step have landed too
-      __syncthreads();  // every wave is done reading the rings
-
-
-      // ---------------------------------------------------------------- epilogue
-      const int nrows = two ? BMT : BB;
-      if (G1) {
-        constexpr int BNA = BNW / 2;  // SwiGLU columns per tile
-        uint8_t* acts = static_cast<uint8_t*>(p.act_s);
-        // this lane's first row (fm = 0, i = 0) in the byte tile and in the
-        // code table; the others are compile-time offsets from it
-        uint8_t* const rowp = lds + (wm * BB + 4 * g) * BNA + wn * 32 + r;
-        uint8_t* const codep = lds + BMT * BNA + (wm * BB + 4 * g) * (BNA / 32) + wn;
-        // the same code with and without the SwiGLU clamp (no limit: the
-        // clamp's three instructions per value are left out)
-        auto requant = [&](auto clamped) {
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v0 = decltype(clamped)::value ? swiglu(acc[fm][0][i], acc[fm][FN / 2][i], p.lim)
-                                                        : silu_mul(acc[fm][0][i], acc[fm][FN / 2][i]);
-              const float v1 = decltype(clamped)::value ? swiglu(acc[fm][1][i], acc[fm][FN / 2 + 1][i], p.lim)
-                                                        : silu_mul(acc[fm][1][i], acc[fm][FN / 2 + 1][i]);
-              // the wave's 32 columns of row lr are one MX group: its amax
-              // over the 16 lanes (one DPP row) that hold the row
-              const float m = row_max16(fmaxf(fabsf(v0), fabsf(v1)));
-              const uint32_t code = mx_group_code(m);
-              const float inv = e8m0_inv(code);
-              if (r == 0) codep[(fm * 16 + i) * (BNA / 32)] = (uint8_t)code;
-              // |v| <= m <= 448 x scale for finite values: no clamp needed
-              rowp[(fm * 16 + i) * BNA] = (uint8_t)to_e4m3(v0 * inv);
-              rowp[(fm * 16 + i) * BNA + 16] = (uint8_t)to_e4m3(v1 * inv);
-            }
-        };
-        if (p.lim < __builtin_inff()) requant(BoolTag<true>{});
-        else requant(BoolTag<false>{});
-        __syncthreads();
-        // the tile's BNA / 32 codes of a row are one 4-byte word of act_s
-        if (tid < nrows)
-          *reinterpret_cast<uint32_t*>(acts + (size_t)(blk * BB + tid) * (p.F / 32) + nt * (BNA / 32)) =
-              *reinterpret_cast<const uint32_t*>(lds + BMT * BNA + tid * (BNA / 32));
-        constexpr int CH = BNA / 16;  // 16-byte chunks per tile row
-        for (int idx = tid; idx < nrows * CH; idx += NT) {
-          const int lr = idx / CH;
-          const int c = idx % CH;
-          const uint4 val = *reinterpret_cast<const uint4*>(lds + lr * BNA + c * 16);
-          *reinterpret_cast<uint4*>(p.act + (size_t)(blk * BB + lr) * p.F + nt * BNA + c * 16) = val;
-        }
-      } else {
-        RowScatter<NT, BNW * 2 / 16, BMT> rows;
-        rows.load_slots(p, blk * BB, nrows, tid);
-        uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
+  f32x4_t acc[FM][FN];
+  int j = (int)(blockIdx.x >> 3);
+  if (in_range(j)) {
+    // GEMM1 (PF) issues the next tile's copies ahead of step 0 before its
+    // epilogue, so they land while the SwiGLU and requantisation run; the
+    // queue is read one tile ahead for that
+    constexpr bool PF = G1;
+    Tile cur = setup(j);
+    int jn = per;  // the next tile (per: none)
+    if (dyn) {
+      take_issue();
+      jn = take_finish();
+    }
+    bool pre = false;  // cur's copies ahead of step 0 are in flight
+    for (;;) {
+      const bool mine = wm == 0 || cur.two;  // this wave's block exists
+      if (cur.ok) {
+        if (!pre) prologue(cur);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < nk; ++s) {
+          // Every wave has read the slots about to be refilled (lgkmcnt(0))
+          // and this wave's copies of step s have landed: A waves wait for
+          // all of theirs but the scale group issued at step s - 1 (if
+          // any); weight waves leave the copies of steps s + 1 .. s + DB - 1
+          // in flight (and the scale group one of those steps issued).  Near
+          // the end, where fewer copies follow step s's, both wait for all
+          // of them.  Then the barrier, and the copies of steps s + 1 (A) /
+          // s + DB (weights) and of the next scale group.  Memory operations
+          // issued after a tile's copies ahead of step 0 (the previous
+          // tile's stores) only make these waits stricter.
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
+          if (s + DB > nk) {
+            wait_vm<0>();
+          } else if (bwave) {
+            if (s % SCG == 0) wait_vm<LB * (DB - 1)>();
+            else wait_vm<LB * (DB - 1) + 1>();
+          } else {
+            if (s % SCG == 1 && s + SCG <= nk) wait_vm<1>();
+            else wait_vm<0>();
+          }
+          barrier_no_fence();
+          issue(cur, s + (bwave ? DB : DA));
+          if (s % SCG == 0) issue_sc(cur, s / SCG + 1);
+          if (mine) {
+            const uint8_t* As = lds + ABASE + (s % NA) * ASZ;
+            const uint8_t* Bs = lds + BBASE + (s % NB) * BSZ;
+            // row q's byte for K group g of step s: 16 q + 4 (s % 4) + g
+            const uint8_t* Ss = lds + SBASE + ((s / SCG) & 1) * SCSZ + 4 * (s % SCG);
+            i32x4_t bfr[FN];
+            int sb[FN];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-              st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
-                  (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
-        __syncthreads();
-        rows.store(p, lds, nt * BNW, tid);
+            for (int fn = 0; fn < FN; ++fn) {
+              const int rr = frag_lrow(fn) + r;
+              bfr[fn] = *reinterpret_cast<const i32x4_t*>(Bs + b_off(rr, g));
+              sb[fn] = (int)Ss[(CW * 64 + rr) * 16 + g];
+            }
+            auto read_a = [&](int fm, i32x4_t& lo, i32x4_t& hi, int& sa) {
+              const int rr = wm * BB + fm * 16 + r;
+              lo = *reinterpret_cast<const i32x4_t*>(As + a_off(rr, g));
+              hi = *reinterpret_cast<const i32x4_t*>(As + a_off(rr, 4 + g));
+              sa = (int)Ss[rr * 16 + g];
+            };
+            auto mult = [&](int fm, const i32x4_t& lo, const i32x4_t& hi, int sa) {
+              const i32x8_t af = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn) {
+                const i32x4_t v = bfr[fn];
+                acc[fm][fn] = mfma_mx(af, i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0}, acc[fm][fn], sa, sb[fn]);
+              }
+            };
+            // A fragments in two register sets: the reads of fragment fm + 1
+            // go out before the MFMAs of fragment fm
+            i32x4_t lo0, hi0, lo1, hi1;
+            int sa0, sa1;
+            read_a(0, lo0, hi0, sa0);
+#pragma unroll
+            for (int fm = 0; fm < FM; fm += 2) {
+              read_a(fm + 1, lo1, hi1, sa1);
+              __builtin_amdgcn_sched_barrier(0);
+              mult(fm, lo0, hi0, sa0);
+              __builtin_amdgcn_sched_barrier(0);
+              if (fm + 2 < FM) read_a(fm + 2, lo0, hi0, sa0);
+              __builtin_amdgcn_sched_barrier(0);
+              mult(fm + 1, lo1, hi1, sa1);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+        wait_vm<0>();     // the copies past the last step have landed too
+        __syncthreads();  // every wave is done reading the rings
+      } else {
+        __syncthreads();  // every wave has read the last index (ctl is written again below)
       }
+
+      const bool more = in_range(jn);
+      Tile nx = cur;
+      if (more) {
+        if (PF) {
+          nx = setup(jn);
+          if (nx.ok) prologue(nx);
+        }
+        take_issue();  // the tile after next, or past the end
+      }
+
+      // ---------------------------------------------------------------- epilogue
+      const int nrows = cur.two ? BMT : BB;
+      constexpr int BNA = BNW / 2;  // GEMM1: SwiGLU columns per tile
+      // GEMM1 stages its bytes in A slot 1 and its codes in weight slot
+      // NB - 1, which the copies ahead of the next tile's step 0 leave alone
+      uint8_t* const stg = lds + ABASE + ASZ;
+      uint8_t* const cds = lds + BBASE + (NB - 1) * BSZ;
+      static_assert(BMT * BNA <= ASZ && BMT * (BNA / 32) <= BSZ && DB <= NB - 1, "epilogue staging");
+      static_assert(G1 || BMT * BNW * 2 <= SBASE + SCSZ, "GEMM2's staged tile ends below the queue word");
+      RowScatter<NT, BNW * 2 / 16, BMT> rows;
+      if (cur.ok) {
+        if (G1) {
+          // this lane's first row (fm = 0, i = 0) in the byte tile and in the
+          // code table; the others are compile-time offsets from it
+          uint8_t* const rowp = stg + (wm * BB + 4 * g) * BNA + wn * 32 + r;
+          uint8_t* const codep = cds + (wm * BB + 4 * g) * (BNA / 32) + wn;
+          // the same code with and without the SwiGLU clamp (no limit: the
+          // clamp's three instructions per value are left out)
+          auto requant = [&](auto clamped) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float v0 = decltype(clamped)::value ? swiglu(acc[fm][0][i], acc[fm][FN / 2][i], p.lim)
+                                                          : silu_mul(acc[fm][0][i], acc[fm][FN / 2][i]);
+                const float v1 = decltype(clamped)::value ? swiglu(acc[fm][1][i], acc[fm][FN / 2 + 1][i], p.lim)
+                                                          : silu_mul(acc[fm][1][i], acc[fm][FN / 2 + 1][i]);
+                // the wave's 32 columns of row lr are one MX group: its amax
+                // over the 16 lanes (one DPP row) that hold the row
+                const float m = row_max16(fmaxf(fabsf(v0), fabsf(v1)));
+                const uint32_t code = mx_group_code(m);
+                const float inv = e8m0_inv(code);
+                if (r == 0) codep[(fm * 16 + i) * (BNA / 32)] = (uint8_t)code;
+                // |v| <= m <= 448 x scale for finite values: no clamp needed
+                rowp[(fm * 16 + i) * BNA] = (uint8_t)to_e4m3(v0 * inv);
+                rowp[(fm * 16 + i) * BNA + 16] = (uint8_t)to_e4m3(v1 * inv);
+              }
+          };
+          if (p.lim < __builtin_inff()) requant(BoolTag<true>{});
+          else requant(BoolTag<false>{});
+        } else {
+          rows.load_slots(p, cur.blk * BB, nrows, tid);
+          uint16_t* st = reinterpret_cast<uint16_t*>(lds);  // [BMT][BNW]
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int fn = 0; fn < FN; ++fn)
+                st[(wm * BB + fm * 16 + 4 * g + i) * BNW + wn * (BNW / WN) + fn * 16 + r] =
+                    (uint16_t)f32_to_bf16_bits(acc[fm][fn][i]);
+        }
+      }
+      // the staged tile is complete (and the next index is in ctl)
+      int jnn = per;
+      if (more) jnn = take_finish();
+      else __syncthreads();
+      if (cur.ok) {
+        if (G1) {
+          // the weight waves store (the A waves' first copies of the next
+          // tile then wait for no store)
+          uint8_t* acts = static_cast<uint8_t*>(p.act_s);
+          if (bwave) {
+            const int bt = tid - CW * 64;
+            // the tile's BNA / 32 codes of a row are one 4-byte word of act_s
+            if (bt < nrows)
+              *reinterpret_cast<uint32_t*>(acts + (size_t)(cur.blk * BB + bt) * (p.F / 32) + cur.nt * (BNA / 32)) =
+                  *reinterpret_cast<const uint32_t*>(cds + bt * (BNA / 32));
+            constexpr int CH = BNA / 16;  // 16-byte chunks per tile row
+            for (int idx = bt; idx < nrows * CH; idx += NT / 2) {
+              const int lr = idx / CH;
+              const int c = idx % CH;
+              const uint4 val = *reinterpret_cast<const uint4*>(stg + lr * BNA + c * 16);
+              *reinterpret_cast<uint4*>(p.act + (size_t)(cur.blk * BB + lr) * p.F + cur.nt * BNA + c * 16) = val;
+            }
+          }
+        } else {
+          rows.store(p, lds, cur.nt * BNW, tid);
+        }
+      }
+      if (!more) break;
+      if (!PF) {
+        __syncthreads();  // every wave is done reading the staged tile
+        nx = setup(jn);
+      }
+      cur = nx;
+      pre = PF && nx.ok;
+      jn = jnn;
     }
-    if (!dyn) break;
-    __syncthreads();  // this tile (and the last index read) is done with LDS
-    if (tid == 0) *reinterpret_cast<volatile int*>(lds) = wpx + atomicAdd(p.queue + xcd, 1);
-    __syncthreads();
-    j = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(lds));
-    __syncthreads();  // every wave has the index before the copies overwrite it
   }
   // the last workgroup to finish leaves the counters at zero for the next
   // launch (every workgroup has made its last take before it counts itself)
@@ -1712,7 +1807,7 @@ moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
 
 template <bool G1, int BB>
 moe_status launch_pair_mx_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
-  constexpr size_t lds = (size_t)2 * (2 * BB * 128) + 5 * 256 * 64 + 2 * 512 * 16;  // A: 2 slots, B: 5, scales: 2
+  constexpr size_t lds = (size_t)2 * (2 * BB * 128) + 4 * 256 * 64 + 2 * 512 * 16;  // A: 2 slots, B: 4, scales: 2
   static std::atomic<int> cache[64];
   const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_mx<G1, BB>), 512, lds, cache);
   gemm_pair_mx<G1, BB><<<tile_grid(max_tiles, wgs), 512, lds, s>>>(p);
