@@ -291,6 +291,35 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// vmcnt(min(n, N)) for a wave-uniform n
+template <int N>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  if constexpr (N == 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= N) wait_vm<N>();
+    else wait_vm_upto<N - 1>(n);
+  }
+}
+// Copy instructions a wave has issued after the last one of step s when it
+// waits ahead of step s, for a stream of L copy instructions per step issued
+// D steps ahead (step u's copies at step u - D, the first D steps before step
+// 0) with one scale-group copy right after step u's copies when u is a
+// multiple of SCG (group u / SCG + 1, if it exists): the copies of steps
+// s + 1 .. s + D - 1 that exist, and the scale groups issued at steps
+// max(s - D, 0) .. s - 1.  Copies complete in issue order, so leaving that
+// many in flight means step s's have landed; memory operations issued after
+// a tile's first copies (the previous tile's stores) only make it stricter.
+template <int L, int D, int SCG>
+__device__ __forceinline__ int copies_after(int s, int nk, int ng) {
+  int n = L * (min(s + D - 1, nk - 1) - s);
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const int u = s - D + i;
+    if (u >= 0 && u % SCG == 0 && u / SCG + 1 < ng) ++n;
+  }
+  return n;
+}
 // Workgroup barrier for the copy pipeline: each wave has already waited for
 // its own copies of the step (wait_vm), so no memory fence is needed, and a
 // fence would also wait for the copies still in flight for later steps.
@@ -1076,6 +1105,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_pair_bf16(GemmP p) {
 // previous one so that LDS latency overlaps the matrix cores.  GEMM1's
 // epilogue requantises each row's 32 SwiGLU columns of a wave (one MX group)
 // with the power-of-two scale pow2_at_least(amax / 448) ([MegaMoE] §3.5).
+// Ring depth of the paired MXFP4 kernels: A slots (the A stream copies
+// MOE_MX_A_SLOTS - 1 steps ahead) and weight slots (MOE_MX_B_SLOTS - 1 ahead).
+#ifndef MOE_MX_A_SLOTS
+#define MOE_MX_A_SLOTS 2
+#endif
+#ifndef MOE_MX_B_SLOTS
+#define MOE_MX_B_SLOTS 4
+#endif
 template <bool G1, int BB>  // BB: rows per block (64 or 128)
 __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   constexpr int NW = 8, NT = 64 * NW, WN = NW / 2;
@@ -1084,8 +1121,8 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   constexpr int ARB = 128, BRB = 64;   // A / B bytes per row and step
   constexpr int ASZ = BMT * ARB;       // one A slot
   constexpr int BSZ = BNW * BRB;       // one weight slot
-  constexpr int NA = 2, NB = 4;        // slots: A one step ahead, weights three
-  constexpr int DA = NA - 1, DB = NB - 1;
+  constexpr int NA = MOE_MX_A_SLOTS, NB = MOE_MX_B_SLOTS;  // ring slots (A, weights)
+  constexpr int DA = NA - 1, DB = NB - 1;                    // steps copied ahead
   constexpr int SCG = 4;               // steps per scale group
   constexpr int SCSZ = NT * 16;        // a scale group: 16 bytes per row, A rows then weight rows
   constexpr int FM = BB / 16;          // 16-row fragments per wave (one block's rows)
@@ -1097,7 +1134,8 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   constexpr int LB = RB / 16;          //                        16 weight rows of 64 bytes
   constexpr int ABASE = 0, BBASE = NA * ASZ, SBASE = NA * ASZ + NB * BSZ;
   static_assert(BMT <= CW * 64 && BNW == CW * 64 && SBASE + 2 * SCSZ <= 163840 && LA >= 1 && LB >= 1 &&
-                FN % 2 == 0 && LB * (DB - 1) + 1 <= 63 && FM % 2 == 0, "tile, LDS, copies and vmcnt");
+                FN % 2 == 0 && LB * (DB - 1) + DB <= 63 && LA * (DA - 1) + DA <= 63 && FM % 2 == 0 &&
+                DA >= 1 && DB >= 1, "tile, LDS, copies and vmcnt");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -1240,17 +1278,19 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
     if (G >= ng) return;
     buf2lds16(src_rs(t), t.sg, G * 16, lds + SBASE + (G & 1) * SCSZ + wave * 1024);
   };
-  // the copies ahead of step 0: scale group 0, then A step 0 or weight
-  // steps 0 .. DB - 1 (into A slot 0, weight slots 0 .. DB - 1, scale slot 0)
+  // the copies ahead of step 0: scale group 0, then A steps 0 .. DA - 1 or
+  // weight steps 0 .. DB - 1 (into the first DA / DB slots, scale slot 0)
   auto prologue = [&](const Tile& t) {
     issue_sc(t, 0);
     if (bwave) {
 #pragma unroll
       for (int s = 0; s < DB; ++s) issue(t, s);
     } else {
-      issue(t, 0);
+#pragma unroll
+      for (int s = 0; s < DA; ++s) issue(t, s);
     }
   };
+
 
   // Taking a tile from the XCD's queue: thread 0's atomic, then the index
   // through an LDS word (in scale slot 1, which the copies ahead of a tile's
@@ -1290,25 +1330,13 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
           for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < nk; ++s) {
           // Every wave has read the slots about to be refilled (lgkmcnt(0))
-          // and this wave's copies of step s have landed: A waves wait for
-          // all of theirs but the scale group issued at step s - 1 (if
-          // any); weight waves leave the copies of steps s + 1 .. s + DB - 1
-          // in flight (and the scale group one of those steps issued).  Near
-          // the end, where fewer copies follow step s's, both wait for all
-          // of them.  Then the barrier, and the copies of steps s + 1 (A) /
-          // s + DB (weights) and of the next scale group.  Memory operations
-          // issued after a tile's copies ahead of step 0 (the previous
-          // tile's stores) only make these waits stricter.
+          // and this wave's copies of step s have landed (the copies issued
+          // after them stay in flight: copies_after).  Then the barrier, and
+          // the copies of steps s + DA (A) / s + DB (weights) and of the
+          // next scale group.
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
-          if (s + DB > nk) {
-            wait_vm<0>();
-          } else if (bwave) {
-            if (s % SCG == 0) wait_vm<LB * (DB - 1)>();
-            else wait_vm<LB * (DB - 1) + 1>();
-          } else {
-            if (s % SCG == 1 && s + SCG <= nk) wait_vm<1>();
-            else wait_vm<0>();
-          }
+          if (bwave) wait_vm_upto<LB * (DB - 1) + DB>(copies_after<LB, DB, SCG>(s, nk, ng));
+          else wait_vm_upto<LA * (DA - 1) + DA>(copies_after<LA, DA, SCG>(s, nk, ng));
           barrier_no_fence();
           issue(cur, s + (bwave ? DB : DA));
           if (s % SCG == 0) issue_sc(cur, s / SCG + 1);
@@ -1376,9 +1404,9 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
       // ---------------------------------------------------------------- epilogue
       const int nrows = cur.two ? BMT : BB;
       constexpr int BNA = BNW / 2;  // GEMM1: SwiGLU columns per tile
-      // GEMM1 stages its bytes in A slot 1 and its codes in weight slot
+      // GEMM1 stages its bytes in A slot NA - 1 and its codes in weight slot
       // NB - 1, which the copies ahead of the next tile's step 0 leave alone
-      uint8_t* const stg = lds + ABASE + ASZ;
+      uint8_t* const stg = lds + ABASE + (NA - 1) * ASZ;
       uint8_t* const cds = lds + BBASE + (NB - 1) * BSZ;
       static_assert(BMT * BNA <= ASZ && BMT * (BNA / 32) <= BSZ && DB <= NB - 1, "epilogue staging");
       static_assert(G1 || BMT * BNW * 2 <= SBASE + SCSZ, "GEMM2's staged tile ends below the queue word");
@@ -1807,7 +1835,8 @@ moe_status launch_pair_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
 
 template <bool G1, int BB>
 moe_status launch_pair_mx_one(const GemmP& p, int64_t max_tiles, hipStream_t s) {
-  constexpr size_t lds = (size_t)2 * (2 * BB * 128) + 4 * 256 * 64 + 2 * 512 * 16;  // A: 2 slots, B: 4, scales: 2
+  constexpr size_t lds = (size_t)MOE_MX_A_SLOTS * (2 * BB * 128) + (size_t)MOE_MX_B_SLOTS * 256 * 64 +
+                        2 * 512 * 16;  // A, weight and (2) scale-group slots
   static std::atomic<int> cache[64];
   const int wgs = resident_wgs(reinterpret_cast<const void*>(&gemm_pair_mx<G1, BB>), 512, lds, cache);
   gemm_pair_mx<G1, BB><<<tile_grid(max_tiles, wgs), 512, lds, s>>>(p);

@@ -260,7 +260,10 @@ def test_expert_ffn_exact_paired_tiles(fmt, H, F, bm, T, kind, sample):
 # changes the exact result.  Stream (16) and tiled (32 / 64 / 128) kernels.
 POW2 = [(f, 512, 512, bm, T) for f in ("fp8", "mxfp4") for bm, T in ((16, 3), (16, 200), (32, 200), (64, 200),
                                                                      (128, 200))] + \
-       [("fp8", 1024, 512, 128, 600), ("mxfp4", 512, 1024, 64, 600)]
+       [("fp8", 1024, 512, 128, 600), ("mxfp4", 512, 1024, 64, 600),
+        # the paired MXFP4 kernels over 16 / 8 K steps (their copy rings and
+        # the waits that end them run as at the full layer shapes)
+        ("mxfp4", 2048, 1024, 128, 600), ("mxfp4", 2048, 1024, 64, 600)]
 
 
 @pytest.mark.parametrize("fmt,H,F,bm,T", POW2)
