@@ -28,7 +28,8 @@ Also reported in the same line:
                   replays and cold replays, MFMA and HBM fractions
   router        - moe_route alone at T = 1 for every configuration (and GLM
                   at 8 and 512 rows) next to the bare read of its gate
-                  weight and an empty kernel, cold
+                  weight and an empty kernel, cold; also with the gate rows
+                  in bf16 (gate_is_fp32 = 0)
   ep_share      - one GPU's share of DeepSeek-V4 expert parallelism (32
                   MXFP4 experts), cold
   cpu_baseline  - the float64 oracle timed on a token sample of the
@@ -347,6 +348,8 @@ def layer_sweep(moe, torch, flush, cases, reps, warm, keep=None):
 
 
 ROUTER = (("toy", 1), ("qwen3", 1), ("glm", 1), ("glm", 8), ("glm", 512), ("dsv3", 1), ("dsv4", 1))
+# also timed with the gate rows in bf16 ([Router] §1.1: 2.4 MB for GLM's 288 x 4096)
+ROUTER_BF16_GATE = (("qwen3", 1), ("glm", 1), ("glm", 8), ("glm", 512), ("dsv3", 1), ("dsv4", 1))
 
 
 MFMA_KINDS = [(0, "bf16 16x16x32", 2 * 16 * 16 * 32, (8, 16)), (1, "bf16 32x32x16", 2 * 32 * 32 * 16, (4, 8)),
@@ -443,6 +446,18 @@ def router_probe(moe, torch, flush, reps):
         res[f"{name}_T{T}"] = {"route_us": summary(r), "bare_gate_read_us": summary(b), "gate_bytes": gate.numel() * 4,
                                "ratio": round(rm / bm_, 3)}
         log(f"router {name} T={T}: {rm:.2f} us vs bare read {bm_:.2f} us (x{rm / bm_:.2f})")
+        if (name, T) in ROUTER_BF16_GATE:
+            # the same router on the gate rows rounded to bf16 (half the
+            # bytes, one MFMA per K step), against the bare read of those bytes
+            g16 = gate.to(torch.bfloat16)
+            r = cold_times(torch, flush, lambda: moe.route(x, g16, bias, cfg.k, cfg.scoring, cfg.n_group,
+                                                            cfg.topk_group, cfg.renormalize, cfg.routed_scale,
+                                                            ws=ws), reps)
+            b = cold_times(torch, flush, lambda: moe.probe_read(g16, sink), reps)
+            rm, bm_ = statistics.median(r), statistics.median(b)
+            res[f"{name}_T{T}_bf16_gate"] = {"route_us": summary(r), "bare_gate_read_us": summary(b),
+                                             "gate_bytes": g16.numel() * 2, "ratio": round(rm / bm_, 3)}
+            log(f"router {name} T={T}, bf16 gate: {rm:.2f} us vs bare read {bm_:.2f} us (x{rm / bm_:.2f})")
         del ids
     return res
 

@@ -113,7 +113,10 @@ const char* moe_source_hash(void);
  * kernel").
  *
  *  x        bf16 [T, H]      hidden states
- *  gate     float32 [E, H]   gate weight (one row per expert)
+ *  gate     [E, H]           gate weight (one row per expert): float32 if
+ *                            gate_is_fp32 is 1, bf16 if it is 0 (the form
+ *                            [Router] §1.1 / §2.4 / §5.1 describes engines
+ *                            storing: bf16 rows, fp32 logits; half the bytes)
  *  bias     float32 [E]      selection bias added to the score to form the
  *                            rank key (NULL: rank key = score).  Only the
  *                            choice uses it; weights use the unbiased score.
@@ -129,15 +132,17 @@ const char* moe_source_hash(void);
  *  topk_weights float32 [T, k] out: their weights
  *  logits_out float32 [T, E] optional out (NULL allowed): the fp32 logits
  *
- * Arithmetic: logits accumulate bf16(x) * fp32(gate) to fp32 accuracy
- * (the gate split exactly into three bf16 planes on matrix cores) in one
- * fixed order for every T: a token's logits and choice do not depend on the
- * batch it is in ([Router] §9).  Scores, keys and weights are fp32.
- * Constraints: 0 <= T <= 2^24, H >= 128 and a multiple of 128,
+ * Arithmetic: logits accumulate bf16(x) * gate to fp32 accuracy (an fp32
+ * gate split exactly into three bf16 planes on matrix cores; a bf16 gate
+ * taken as it is) in one fixed order for every T: a token's logits and
+ * choice do not depend on the batch it is in ([Router] §9).  Scores, keys
+ * and weights are fp32.
+ * Constraints: gate_is_fp32 in {0, 1}; 0 <= T <= 2^24, H >= 128 and a
+ * multiple of 128,
  * 1 <= k <= E <= 1024, k <= 16; n_group divides E, E/n_group >= 2 when n_group > 1,
  * 1 <= topk_group <= n_group, k <= topk_group * E / n_group.
  * ------------------------------------------------------------------------ */
-moe_status moe_route(const void* x, const float* gate, const float* bias,
+moe_status moe_route(const void* x, const void* gate, int gate_is_fp32, const float* bias,
                      int T, int H, int E, int k, int n_group, int topk_group,
                      int scoring, int renormalize, float routed_scale,
                      int32_t* topk_ids, float* topk_weights, float* logits_out,
@@ -204,7 +209,7 @@ int64_t moe_align_max_blocks(int T, int k, int E, int block_m);
  * k + n_shared > 16: MOE_E_INVAL.  The workspace must hold
  * moe_route_align_workspace_size(T, H, E, k, n_shared) bytes.
  * ------------------------------------------------------------------------ */
-moe_status moe_route_align(const void* x, const float* gate, const float* bias,
+moe_status moe_route_align(const void* x, const void* gate, int gate_is_fp32, const float* bias,
                            int T, int H, int E, int k, int n_shared,
                            int n_group, int topk_group,
                            int scoring, int renormalize, float routed_scale,
@@ -300,7 +305,7 @@ moe_status moe_expert_ffn_stages(const void* x, int wformat,
  *  topk_ids_out, topk_weights_out   optional outputs (NULL allowed),
  *                 [T, k + n_shared].
  * ------------------------------------------------------------------------ */
-moe_status moe_layer(const void* x, const float* gate, const float* bias,
+moe_status moe_layer(const void* x, const void* gate, int gate_is_fp32, const float* bias,
                      int wformat, const void* w13, const void* w13_scale,
                      const void* w2, const void* w2_scale,
                      int T, int H, int E, int F, int k, int n_shared,
@@ -335,7 +340,7 @@ size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, int n_shared,
  *    streams, two threads) RACE and give undefined results.  Serialise them.
  * ------------------------------------------------------------------------ */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
-moe_status moe_layer_noalloc(const void* x, const float* gate, const float* bias,
+moe_status moe_layer_noalloc(const void* x, const void* gate, int gate_is_fp32, const float* bias,
                              int wformat, const void* w13, const void* w13_scale,
                              const void* w2, const void* w2_scale,
                              int T, int H, int E, int F, int k, int n_shared,

@@ -48,9 +48,9 @@ _i32 = ctypes.c_int32
 SIGNATURES = {
     "moe_status_str": (ctypes.c_char_p, [_i]),
     "moe_source_hash": (ctypes.c_char_p, []),
-    "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_workspace_size": (_sz, [_i, _i, _i]),
-    "moe_route_align": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp,
+    "moe_route_align": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp, _vp, _vp, _vp, _vp,
                              _vp, _sz, _vp]),
     "moe_route_align_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "moe_align": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -62,10 +62,10 @@ SIGNATURES = {
     "moe_expert_ffn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn_stages": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _i, _vp]),
-    "moe_layer": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f,
+    "moe_layer": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _i, _f,
                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
-    "moe_layer_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+    "moe_layer_noalloc": (_i, [_vp, _vp, _i, _vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                _i, _f, _vp, _vp, _vp, _vp]),
     "moe_layer_block_m": (_i, [_i, _i, _i, _i, _i]),
     "moe_debug_error": (_i32, [_vp, _vp]),

@@ -132,7 +132,8 @@ extern "C" size_t moe_layer_workspace_size(int T, int H, int E, int F, int k, in
 
 namespace moe {
 
-moe_status layer_validate(const void* x, const float* gate, int wformat, const void* w13, const void* w13_scale,
+moe_status layer_validate(const void* x, const void* gate, int gate_is_fp32, int wformat, const void* w13,
+                          const void* w13_scale,
                           const void* w2, const void* w2_scale, int T, int H, int E, int F, int k, int n_shared,
                           int n_group, int topk_group, int scoring, int block_m, float swiglu_limit, const void* y) {
   if (n_shared != 0 && n_shared != 1) return MOE_E_INVAL;
@@ -140,20 +141,21 @@ moe_status layer_validate(const void* x, const float* gate, int wformat, const v
   if (block_m == 0) block_m = (T >= 0 && k >= 1 && E >= 1 && F >= 1) ? layer_block_m(T, ka, Ea, F, wformat) : 16;
   int32_t dummy_i = 0;
   float dummy_f = 0.f;
-  moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, &dummy_i, &dummy_f);
+  moe_status st = route_validate(x, gate, gate_is_fp32, T, H, E, k, n_group, topk_group, scoring, &dummy_i, &dummy_f);
   if (st != MOE_OK) return st;
   return ffn_validate(x, wformat, w13, w13_scale, w2, w2_scale, &dummy_i, &dummy_f, &dummy_i, &dummy_i, &dummy_i,
                       T, H, Ea, F, ka, block_m, swiglu_limit, y);
 }
 
-moe_status layer_enqueue(const void* x, const float* gate, const float* bias, int wformat, const void* w13,
+moe_status layer_enqueue(const void* x, const void* gate, int gate_is_fp32, const float* bias, int wformat,
+                         const void* w13,
                          const void* w13_scale, const void* w2, const void* w2_scale, int T, int H, int E, int F,
                          int k, int n_shared, int n_group, int topk_group, int scoring, int renormalize,
                          float routed_scale, int block_m, float swiglu_limit, void* y, int32_t* topk_ids_out,
                          float* topk_weights_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // validate everything before enqueuing anything
-  moe_status st = layer_validate(x, gate, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k, n_shared, n_group,
-                                 topk_group, scoring, block_m, swiglu_limit, y);
+  moe_status st = layer_validate(x, gate, gate_is_fp32, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k,
+                                 n_shared, n_group, topk_group, scoring, block_m, swiglu_limit, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   const int Ea = E + n_shared, ka = k + n_shared;  // the expert FFN sees the shared expert as expert E
@@ -186,7 +188,8 @@ moe_status layer_enqueue(const void* x, const float* gate, const float* bias, in
   // the alignment also writes the paired tiles' pair table where it can
   // (one launch fewer); the FFN builds it otherwise
   bool pairs_written = false;
-  st = launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+  st = launch_route_align(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                          routed_scale,
                           n_shared, block_m, ids, w, sorted, bexp, npp, b + L.ctrl, stream, a.xq, a.xs, qfmt,
                           static_cast<int32_t*>(a.pairs), &pairs_written, /*fill_tail=*/false);
   if (st != MOE_OK) return st;
@@ -196,13 +199,14 @@ moe_status layer_enqueue(const void* x, const float* gate, const float* bias, in
 
 }  // namespace moe
 
-extern "C" moe_status moe_layer(const void* x, const float* gate, const float* bias, int wformat,
+extern "C" moe_status moe_layer(const void* x, const void* gate, int gate_is_fp32, const float* bias, int wformat,
                                 const void* w13, const void* w13_scale, const void* w2, const void* w2_scale,
                                 int T, int H, int E, int F, int k, int n_shared, int n_group, int topk_group,
                                 int scoring, int renormalize, float routed_scale, int block_m, float swiglu_limit,
                                 void* y, int32_t* topk_ids_out, float* topk_weights_out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
-  return moe::layer_enqueue(x, gate, bias, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k, n_shared, n_group,
+  return moe::layer_enqueue(x, gate, gate_is_fp32, bias, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k,
+                            n_shared, n_group,
                             topk_group, scoring, renormalize, routed_scale, block_m, swiglu_limit, y, topk_ids_out,
                             topk_weights_out, workspace, workspace_bytes, stream);
 }

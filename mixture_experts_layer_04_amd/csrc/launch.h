@@ -23,10 +23,11 @@ constexpr size_t kTileQueueOffset = 16;
 constexpr size_t kCounterOffset = 256;
 constexpr int kMaxCounters = (int)((kCtrlBytes - kCounterOffset) / 4);
 
-moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
+moe_status route_validate(const void* x, const void* gate, int gate_is_fp32, int T, int H, int E, int k, int n_group,
                           int topk_group, int scoring, const int32_t* ids, const float* w);
 size_t route_workspace_size(int T, int H, int E);
-moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+moe_status launch_route(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H, int E,
+                        int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream);
 
@@ -37,7 +38,8 @@ moe_status launch_route(const void* x, const float* gate, const float* bias, int
 // ids / weights rows hold k + 1 slots and the alignment covers E + 1 experts.
 // qfmt 1 (FP8) / 2 (MX): where route_quantizes_x(T, E), the router also
 // quantises x into xq / xs as the FFN's activation stage would; 0: no.
-moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+moe_status launch_route_align(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H,
+                              int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
@@ -114,10 +116,12 @@ int tile_grid(int64_t n_tiles, int max_wgs);
 // moe_layer's checks (scalars, formats, non-null pointers), and moe_layer on
 // a caller-chosen workspace (checks first, then route + align + expert FFN).
 size_t layer_workspace_bytes(int T, int H, int E, int F, int k, int n_shared, int block_m, int wformat);
-moe_status layer_validate(const void* x, const float* gate, int wformat, const void* w13, const void* w13_scale,
+moe_status layer_validate(const void* x, const void* gate, int gate_is_fp32, int wformat, const void* w13,
+                          const void* w13_scale,
                           const void* w2, const void* w2_scale, int T, int H, int E, int F, int k, int n_shared,
                           int n_group, int topk_group, int scoring, int block_m, float swiglu_limit, const void* y);
-moe_status layer_enqueue(const void* x, const float* gate, const float* bias, int wformat, const void* w13,
+moe_status layer_enqueue(const void* x, const void* gate, int gate_is_fp32, const float* bias, int wformat,
+                         const void* w13,
                          const void* w13_scale, const void* w2, const void* w2_scale, int T, int H, int E, int F,
                          int k, int n_shared, int n_group, int topk_group, int scoring, int renormalize,
                          float routed_scale, int block_m, float swiglu_limit, void* y, int32_t* topk_ids_out,

@@ -90,7 +90,8 @@ moe_status clear_until_done(int dev, void* ptr, hipStream_t stream) {
 
 }  // namespace
 
-extern "C" moe_status moe_layer_noalloc(const void* x, const float* gate, const float* bias, int wformat,
+extern "C" moe_status moe_layer_noalloc(const void* x, const void* gate, int gate_is_fp32, const float* bias,
+                                        int wformat,
                                         const void* w13, const void* w13_scale, const void* w2,
                                         const void* w2_scale, int T, int H, int E, int F, int k, int n_shared,
                                         int n_group, int topk_group, int scoring, int renormalize,
@@ -98,8 +99,8 @@ extern "C" moe_status moe_layer_noalloc(const void* x, const float* gate, const 
                                         int32_t* topk_ids_out, float* topk_weights_out, hipStream_t stream) {
   // host checks first: nothing is looked up or enqueued for a call that
   // fails them or that the scratch array cannot hold
-  moe_status st = moe::layer_validate(x, gate, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k, n_shared,
-                                      n_group, topk_group, scoring, block_m, swiglu_limit, y);
+  moe_status st = moe::layer_validate(x, gate, gate_is_fp32, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k,
+                                      n_shared, n_group, topk_group, scoring, block_m, swiglu_limit, y);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (moe::layer_workspace_bytes(T, H, E, F, k, n_shared, block_m, wformat) > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
@@ -112,7 +113,8 @@ extern "C" moe_status moe_layer_noalloc(const void* x, const float* gate, const 
   if (st != MOE_OK) return st;
   st = clear_until_done(dev, ws, stream);
   if (st != MOE_OK) return st;
-  return moe::layer_enqueue(x, gate, bias, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k, n_shared, n_group,
+  return moe::layer_enqueue(x, gate, gate_is_fp32, bias, wformat, w13, w13_scale, w2, w2_scale, T, H, E, F, k,
+                            n_shared, n_group,
                             topk_group, scoring, renormalize, routed_scale, block_m, swiglu_limit, y, topk_ids_out,
                             topk_weights_out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

@@ -12,7 +12,11 @@
 //    g = hi + mid + lo (hi: g with its low 16 bits cleared; mid: the same for
 //    the remainder; lo: the last <= 8 significant bits), and x is bf16, so
 //    every product x * plane is exact in fp32 and v_mfma_f32_16x16x32_bf16
-//    accumulates bf16(x) * fp32(gate) to fp32 accuracy;
+//    accumulates bf16(x) * fp32(gate) to fp32 accuracy; a bf16 gate (the
+//    form the page's engines store, [Router] §1.1, §2.4 and §5.1: bf16
+//    hidden states times bf16 gate rows into fp32 logits; half the gate
+//    bytes) is its own hi plane and takes one MFMA per K step instead of
+//    three (its mid and lo planes are zero);
 //  * K is cut into chunks of 128; P_c = MFMA chain over chunk c from zero
 //    (4 K-steps, each hi, mid, lo in that order);
 //  * G_j = P_4j + P_4j+1 + P_4j+2 + P_4j+3 (left to right), and
@@ -61,7 +65,7 @@ static_assert(SMALL_T_TILE4 / 4 <= kMaxCounters, "router counters");
 
 struct RouteParams {
   const uint16_t* x;
-  const float* gate;
+  const void* gate;  // fp32 [E, H], or bf16 [E, H] in the GB kernels
   const float* bias;
   float* part;        // decode layout: group sums [NG][T][E]
   float* logits_out;  // optional [T][E]
@@ -116,6 +120,15 @@ __device__ __forceinline__ f32x4_t mfma3(const bf16x8_t& a, const bf16x8_t& bh, 
   acc = mfma_16x16x32_bf16(a, bm, acc);
   acc = mfma_16x16x32_bf16(a, bl, acc);
   return acc;
+}
+
+// The K step of one 16 x 16 logit tile: three planes of an fp32 gate, or the
+// one plane of a bf16 gate (GB).
+template <bool GB>
+__device__ __forceinline__ f32x4_t gate_step(const bf16x8_t& a, const bf16x8_t& bh, const bf16x8_t& bm,
+                                             const bf16x8_t& bl, f32x4_t acc) {
+  if constexpr (GB) return mfma_16x16x32_bf16(a, bh, acc);
+  return mfma3(a, bh, bm, bl, acc);
 }
 
 // Selection for one token from its E fp32 logits (l[s] = logit of expert
@@ -390,7 +403,7 @@ __device__ __forceinline__ void quant_chunk(const RouteParams& p, int t, bool tv
 // only): the selecting workgroup also aligns, from the ids it keeps in LDS
 // (one wave for at most 64 assignments, else dynamic LDS of (5 E + 1) ints,
 // E counting the shared expert).
-template <int SLOTS, bool FUSE>
+template <int SLOTS, bool FUSE, bool GB>
 __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -408,24 +421,31 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   if (c < p.NC) {
     const int e = min(f * 16 + r, p.E - 1);
-    const float* grow = p.gate + (size_t)e * p.H + c * KCH + q * 8;
+    const size_t goff = (size_t)e * p.H + c * KCH + q * 8;
     const int t = t0 + r;
     const bool tv = r < p.tt && t < p.T;
     const uint16_t* xrow = p.x + (size_t)(tv ? t : 0) * p.H + c * KCH + q * 8;
     float4 g0[4], g1[4];
+    bf16x8_t gb[4];
     bf16x8_t a[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      g0[s] = *reinterpret_cast<const float4*>(grow + 32 * s);
-      g1[s] = *reinterpret_cast<const float4*>(grow + 32 * s + 4);
+      if constexpr (GB) {
+        gb[s] = *reinterpret_cast<const bf16x8_t*>(static_cast<const uint16_t*>(p.gate) + goff + 32 * s);
+      } else {
+        const float* grow = static_cast<const float*>(p.gate) + goff;
+        g0[s] = *reinterpret_cast<const float4*>(grow + 32 * s);
+        g1[s] = *reinterpret_cast<const float4*>(grow + 32 * s + 4);
+      }
       a[s] = *reinterpret_cast<const bf16x8_t*>(xrow + 32 * s);
       if (!tv) a[s] = bf16x8_t{};
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8_t bh, bm, bl;
-      split8(g0[s], g1[s], bh, bm, bl);
-      acc = mfma3(a[s], bh, bm, bl, acc);
+      if constexpr (GB) bh = gb[s];
+      else split8(g0[s], g1[s], bh, bm, bl);
+      acc = gate_step<GB>(a[s], bh, bm, bl, acc);
     }
     // the workgroups of expert fragment 0 cover every chunk of the tile once
     if (p.qfmt != 0 && f == 0) quant_chunk(p, t, tv, c, q, a);
@@ -502,6 +522,7 @@ constexpr int PF = 1;   // steps loaded ahead (measured: 1 against 4, the same
                         // DSV4 T=8192 115.5 -> 101.1 us: fewer registers, more
                         // workgroups per CU)
 
+template <bool GB>
 __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t planes[LE * PROW];
   const int tid = threadIdx.x;
@@ -523,8 +544,12 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
   const int sk = (tid & 7) * 4;
   const bool sv0 = e0 + se < p.E;
   const bool sv1 = e0 + se + 32 < p.E;
-  const float* g0p = p.gate + (size_t)min(e0 + se, p.E - 1) * p.H + k0 + sk;
-  const float* g1p = p.gate + (size_t)min(e0 + se + 32, p.E - 1) * p.H + k0 + sk;
+  const size_t g0o = (size_t)min(e0 + se, p.E - 1) * p.H + k0 + sk;
+  const size_t g1o = (size_t)min(e0 + se + 32, p.E - 1) * p.H + k0 + sk;
+  const float* g0p = static_cast<const float*>(p.gate) + g0o;
+  const float* g1p = static_cast<const float*>(p.gate) + g1o;
+  const uint16_t* b0p = static_cast<const uint16_t*>(p.gate) + g0o;
+  const uint16_t* b1p = static_cast<const uint16_t*>(p.gate) + g1o;
   const uint16_t* xr[TFR];
   bool tv[TFR];
 #pragma unroll
@@ -543,13 +568,21 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
       grp[a][b] = part[a][b];
     }
 
-  // register ring of PF steps (past the last step: the last step again)
-  float4 rg0[PF], rg1[PF];
+  // register ring of PF steps (past the last step: the last step again), as
+  // raw bits: four fp32 gate values per row, or four bf16 ones in .x / .y
+  uint4 rg0[PF], rg1[PF];
   bf16x8_t rx[PF][TFR];
   auto load = [&](int st, int slot) {
     const int kb = min(st, nsteps - 1) * 32;
-    rg0[slot] = *reinterpret_cast<const float4*>(g0p + kb);
-    rg1[slot] = *reinterpret_cast<const float4*>(g1p + kb);
+    if constexpr (GB) {
+      const uint2 v0 = *reinterpret_cast<const uint2*>(b0p + kb);
+      const uint2 v1 = *reinterpret_cast<const uint2*>(b1p + kb);
+      rg0[slot] = make_uint4(v0.x, v0.y, 0u, 0u);
+      rg1[slot] = make_uint4(v1.x, v1.y, 0u, 0u);
+    } else {
+      rg0[slot] = *reinterpret_cast<const uint4*>(g0p + kb);
+      rg1[slot] = *reinterpret_cast<const uint4*>(g1p + kb);
+    }
 #pragma unroll
     for (int tf = 0; tf < TFR; ++tf) rx[slot][tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
   };
@@ -561,22 +594,28 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
     for (int u = 0; u < PF; ++u) {
       const int st = s0 + u;
       if (st >= nsteps) break;
-      const float4 g0 = sv0 ? rg0[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 g1 = sv1 ? rg1[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint4 g0 = sv0 ? rg0[u] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 g1 = sv1 ? rg1[u] : make_uint4(0u, 0u, 0u, 0u);
       bf16x8_t a[TFR];
 #pragma unroll
       for (int tf = 0; tf < TFR; ++tf) a[tf] = tv[tf] ? rx[u][tf] : bf16x8_t{};
       load(st + PF, u);
       __syncthreads();  // the previous step's planes are consumed
-      {
+      if constexpr (GB) {  // the bf16 gate is the hi plane
+        uint16_t* row = planes + se * PROW + sk;
+        *reinterpret_cast<uint2*>(row) = make_uint2(g0.x, g0.y);
+        *reinterpret_cast<uint2*>(row + 32 * PROW) = make_uint2(g1.x, g1.y);
+      } else {
         uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
         uint16_t* row = planes + se * PROW + sk;
-        split3(g0.x, h0, m0, l0); split3(g0.y, h1, m1, l1); split3(g0.z, h2, m2, l2); split3(g0.w, h3, m3, l3);
+        split3(__uint_as_float(g0.x), h0, m0, l0); split3(__uint_as_float(g0.y), h1, m1, l1);
+        split3(__uint_as_float(g0.z), h2, m2, l2); split3(__uint_as_float(g0.w), h3, m3, l3);
         *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
         *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
         *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
         row += 32 * PROW;
-        split3(g1.x, h0, m0, l0); split3(g1.y, h1, m1, l1); split3(g1.z, h2, m2, l2); split3(g1.w, h3, m3, l3);
+        split3(__uint_as_float(g1.x), h0, m0, l0); split3(__uint_as_float(g1.y), h1, m1, l1);
+        split3(__uint_as_float(g1.z), h2, m2, l2); split3(__uint_as_float(g1.w), h3, m3, l3);
         *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
         *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
         *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
@@ -586,10 +625,13 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
       for (int ef = 0; ef < 2; ++ef) {
         const uint16_t* pr = planes + (wn * 32 + ef * 16 + r) * PROW + q * 8;
         const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pr);
-        const bf16x8_t bm = *reinterpret_cast<const bf16x8_t*>(pr + 32);
-        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pr + 64);
+        bf16x8_t bm{}, bl{};
+        if constexpr (!GB) {
+          bm = *reinterpret_cast<const bf16x8_t*>(pr + 32);
+          bl = *reinterpret_cast<const bf16x8_t*>(pr + 64);
+        }
 #pragma unroll
-        for (int tf = 0; tf < TFR; ++tf) part[tf][ef] = mfma3(a[tf], bh, bm, bl, part[tf][ef]);
+        for (int tf = 0; tf < TFR; ++tf) part[tf][ef] = gate_step<GB>(a[tf], bh, bm, bl, part[tf][ef]);
       }
       if ((st & 3) == 3 || st == nsteps - 1) {  // end of a chunk: G_j += P_c (P_c from zero)
         const bool first = st < 4;
@@ -632,18 +674,18 @@ bool use_large(int T, int E, int H) {
 }
 
 // ap: the alignment to fuse into the decode layout, or nullptr
-template <int SLOTS>
+template <int SLOTS, bool GB>
 moe_status launch_slots(const RouteParams& p, const AlignParams* ap, hipStream_t stream) {
   if (use_large(p.T, p.E, p.H)) {
-    route_logits_group<<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE), p.NG), 256, 0, stream>>>(p);
+    route_logits_group<GB><<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE), p.NG), 256, 0, stream>>>(p);
     MOE_CHECK_LAUNCH();
     route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
   } else {
     dim3 grid(p.NF * p.NG, ceil_div(p.T, p.tt));
     if (ap)  // align_block's LDS: (4 waves + 1) x the alignment's experts (E + n_shared) + 1
-      route_small<SLOTS, true><<<grid, 256, (5 * (size_t)ap->E + 1) * sizeof(int), stream>>>(p, *ap);
+      route_small<SLOTS, true, GB><<<grid, 256, (5 * (size_t)ap->E + 1) * sizeof(int), stream>>>(p, *ap);
     else
-      route_small<SLOTS, false><<<grid, 256, 0, stream>>>(p, AlignParams{});
+      route_small<SLOTS, false, GB><<<grid, 256, 0, stream>>>(p, AlignParams{});
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
@@ -656,11 +698,12 @@ size_t route_workspace_size(int T, int H, int E) {
   return kCtrlBytes + align_up(per_token * T * sizeof(float), 256);
 }
 
-moe_status route_validate(const void* x, const float* gate, int T, int H, int E, int k, int n_group,
+moe_status route_validate(const void* x, const void* gate, int gate_is_fp32, int T, int H, int E, int k, int n_group,
                           int topk_group, int scoring, const int32_t* ids, const float* w) {
   if (T < 0 || T > (1 << 24) || H < 128 || H % 128 != 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E)
     return MOE_E_INVAL;
   if (scoring != MOE_SOFTMAX && scoring != MOE_SIGMOID && scoring != MOE_SQRTSOFTPLUS) return MOE_E_INVAL;
+  if (gate_is_fp32 != 0 && gate_is_fp32 != 1) return MOE_E_INVAL;
   if (n_group < 1 || n_group > 64 || E % n_group != 0) return MOE_E_INVAL;
   if (n_group > 1 && (E / n_group < 2)) return MOE_E_INVAL;
   if (topk_group < 1 || topk_group > n_group) return MOE_E_INVAL;
@@ -671,7 +714,18 @@ moe_status route_validate(const void* x, const float* gate, int T, int H, int E,
 
 namespace {
 
-moe_status route_launch(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+template <bool GB>
+moe_status launch_gate(const RouteParams& p, const AlignParams* ap, int slots, hipStream_t stream) {
+  if (slots <= 1) return launch_slots<1, GB>(p, ap, stream);
+  if (slots <= 2) return launch_slots<2, GB>(p, ap, stream);
+  if (slots <= 4) return launch_slots<4, GB>(p, ap, stream);
+  if (slots <= 5) return launch_slots<5, GB>(p, ap, stream);
+  if (slots <= 8) return launch_slots<8, GB>(p, ap, stream);
+  return launch_slots<16, GB>(p, ap, stream);
+}
+
+moe_status route_launch(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H, int E,
+                        int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int n_shared, int32_t* ids, float* weights, float* logits_out, void* ws,
                         const AlignParams* ap, hipStream_t stream, void* xq = nullptr, void* xs = nullptr,
@@ -704,21 +758,18 @@ moe_status route_launch(const void* x, const float* gate, const float* bias, int
   p.NC = H / KCH;
   p.NG = ceil_div(p.NC, CPG);
   const int slots = ceil_div(E, kWave);
-  if (slots <= 1) return launch_slots<1>(p, ap, stream);
-  if (slots <= 2) return launch_slots<2>(p, ap, stream);
-  if (slots <= 4) return launch_slots<4>(p, ap, stream);
-  if (slots <= 5) return launch_slots<5>(p, ap, stream);
-  if (slots <= 8) return launch_slots<8>(p, ap, stream);
-  return launch_slots<16>(p, ap, stream);
+  if (gate_is_fp32) return launch_gate<false>(p, ap, slots, stream);
+  return launch_gate<true>(p, ap, slots, stream);
 }
 }  // namespace
 
-moe_status launch_route(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+moe_status launch_route(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H, int E,
+                        int k,
                         int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                         int32_t* ids, float* weights, float* logits_out, void* ws, hipStream_t stream) {
   if (T == 0) return MOE_OK;
-  return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale, 0, ids,
-                      weights, logits_out, ws, nullptr, stream);
+  return route_launch(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                      routed_scale, 0, ids, weights, logits_out, ws, nullptr, stream);
 }
 
 size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
@@ -728,7 +779,8 @@ size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
 
 bool route_quantizes_x(int T, int E, int H) { return !use_large(T, E, H); }
 
-moe_status launch_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E, int k,
+moe_status launch_route_align(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H,
+                              int E, int k,
                               int n_group, int topk_group, int scoring, int renormalize, float routed_scale,
                               int n_shared, int block_m, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* num_post_padded, void* ws, hipStream_t stream,
@@ -742,20 +794,20 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
     // one token tile: its selecting workgroup aligns in the same launch
     AlignParams ap = align_params(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws);
     ap.fill_tail = fill_tail;
-    return route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
-                        n_shared, ids, weights, nullptr, ws, &ap, stream, xq, xs, qfmt);
+    return route_launch(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                        routed_scale, n_shared, ids, weights, nullptr, ws, &ap, stream, xq, xs, qfmt);
   }
   if (!use_large(T, E, H)) {
     // several token tiles: a launch of its own aligns (measured: faster than
     // a second election among the tiles and an alignment by the last one's
     // four waves, Qwen3 T=16 route + align 15.5 against about 13 us)
-    moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+    moe_status st = route_launch(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
                                  routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream, xq, xs, qfmt);
     if (st != MOE_OK) return st;
     return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream, pairs,
                         pairs_written, fill_tail);
   }
-  moe_status st = route_launch(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+  moe_status st = route_launch(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
                                routed_scale, n_shared, ids, weights, nullptr, ws, nullptr, stream);
   if (st != MOE_OK) return st;
   return launch_align(ids, T, ka, Ea, block_m, sorted_ids, block_expert, num_post_padded, ws, stream, pairs,
@@ -764,18 +816,20 @@ moe_status launch_route_align(const void* x, const float* gate, const float* bia
 
 }  // namespace moe
 
-extern "C" moe_status moe_route(const void* x, const float* gate, const float* bias, int T, int H, int E,
+extern "C" moe_status moe_route(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H,
+                                int E,
                                 int k, int n_group, int topk_group, int scoring, int renormalize,
                                 float routed_scale, int32_t* topk_ids, float* topk_weights,
                                 float* logits_out, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   using namespace moe;
-  moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, topk_ids, topk_weights);
+  moe_status st = route_validate(x, gate, gate_is_fp32, T, H, E, k, n_group, topk_group, scoring, topk_ids,
+                                 topk_weights);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (!workspace) return MOE_E_INVAL;
   if (workspace_bytes < route_workspace_size(T, H, E)) return MOE_E_WORKSPACE;
-  return launch_route(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+  return launch_route(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
                       topk_ids, topk_weights, logits_out, workspace, stream);
 }
 
@@ -784,7 +838,8 @@ extern "C" size_t moe_route_workspace_size(int T, int H, int E) {
   return moe::route_workspace_size(T, H, E);
 }
 
-extern "C" moe_status moe_route_align(const void* x, const float* gate, const float* bias, int T, int H, int E,
+extern "C" moe_status moe_route_align(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T,
+                                      int H, int E,
                                       int k, int n_shared, int n_group, int topk_group, int scoring,
                                       int renormalize, float routed_scale, int block_m, int32_t* topk_ids,
                                       float* topk_weights, int32_t* sorted_ids, int32_t* block_expert,
@@ -792,13 +847,15 @@ extern "C" moe_status moe_route_align(const void* x, const float* gate, const fl
                                       hipStream_t stream) {
   using namespace moe;
   if (n_shared != 0 && n_shared != 1) return MOE_E_INVAL;
-  moe_status st = route_validate(x, gate, T, H, E, k, n_group, topk_group, scoring, topk_ids, topk_weights);
+  moe_status st = route_validate(x, gate, gate_is_fp32, T, H, E, k, n_group, topk_group, scoring, topk_ids,
+                                 topk_weights);
   if (st != MOE_OK) return st;
   st = align_validate(topk_ids, T, k + n_shared, E + n_shared, block_m, sorted_ids, block_expert, num_post_padded);
   if (st != MOE_OK) return st;
   if (!workspace) return MOE_E_INVAL;
   if (workspace_bytes < route_align_workspace_size(T, H, E, k, n_shared)) return MOE_E_WORKSPACE;
-  return launch_route_align(x, gate, bias, T, H, E, k, n_group, topk_group, scoring, renormalize, routed_scale,
+  return launch_route_align(x, gate, gate_is_fp32, bias, T, H, E, k, n_group, topk_group, scoring, renormalize,
+                            routed_scale,
                             n_shared, block_m, topk_ids, topk_weights, sorted_ids, block_expert, num_post_padded,
                             workspace, stream, nullptr, nullptr, 0);
 }

@@ -2,7 +2,8 @@
 out.  Argument marshalling only - every step runs in the HIP kernels.
 
 Tensors must be CUDA (HIP) tensors, contiguous, with the dtypes of
-include/moe.h: x bf16 [T, H]; gate float32 [E, H]; bias float32 [E] or None;
+include/moe.h: x bf16 [T, H]; gate float32 or bf16 [E, H] (the dtype sets
+gate_is_fp32); bias float32 [E] or None;
 w13 / w2 in the layout of the weight format (bf16, or uint8 codes plus
 float32 (fp8) / uint8 e8m0 (mxfp4) scales).  Work goes onto the current
 stream.  The workspace is a zero-initialised byte tensor cached per device
@@ -55,6 +56,14 @@ def _check_cuda(*ts):
                 raise ValueError("libmoe ops take contiguous tensors")
 
 
+def _gate_is_fp32(gate):
+    if gate.dtype == torch.float32:
+        return 1
+    if gate.dtype == torch.bfloat16:
+        return 0
+    raise ValueError(f"the gate is float32 or bfloat16, not {gate.dtype}")
+
+
 def align_max_padded(T, k, E, block_m):
     return int(lib().moe_align_max_padded(T, k, E, block_m))
 
@@ -78,7 +87,7 @@ def route(x, gate, bias, k, scoring="softmax", n_group=1, topk_group=1, renormal
     logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if return_logits else None
     need = lib().moe_route_workspace_size(T, H, E)
     ws = workspace(x.device, need) if ws is None else ws
-    check(lib().moe_route(_ptr(x), _ptr(gate), _ptr(bias), T, H, E, k, n_group, topk_group,
+    check(lib().moe_route(_ptr(x), _ptr(gate), _gate_is_fp32(gate), _ptr(bias), T, H, E, k, n_group, topk_group,
                           SCORING[scoring], int(bool(renormalize)), float(routed_scale),
                           _ptr(ids), _ptr(w), _ptr(logits), _ptr(ws), ws.numel(), _stream(x.device)),
           "moe_route")
@@ -101,9 +110,9 @@ def route_align(x, gate, bias, k, block_m, scoring="softmax", n_group=1, topk_gr
     npp = torch.empty(1, dtype=torch.int32, device=dev)
     need = lib().moe_route_align_workspace_size(T, H, E, k, n_shared)
     ws = workspace(dev, need) if ws is None else ws
-    check(lib().moe_route_align(_ptr(x), _ptr(gate), _ptr(bias), T, H, E, k, n_shared, n_group, topk_group,
-                                SCORING[scoring], int(bool(renormalize)), float(routed_scale), block_m,
-                                _ptr(ids), _ptr(w), _ptr(sorted_ids), _ptr(block_expert), _ptr(npp),
+    check(lib().moe_route_align(_ptr(x), _ptr(gate), _gate_is_fp32(gate), _ptr(bias), T, H, E, k, n_shared,
+                                n_group, topk_group, SCORING[scoring], int(bool(renormalize)), float(routed_scale),
+                                block_m, _ptr(ids), _ptr(w), _ptr(sorted_ids), _ptr(block_expert), _ptr(npp),
                                 _ptr(ws), ws.numel(), _stream(dev)), "moe_route_align")
     return ids, w, sorted_ids, block_expert, npp
 
@@ -177,8 +186,8 @@ def layer(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_group=1,
     wf = WFORMAT[wformat]
     need = lib().moe_layer_workspace_size(T, H, E, F, k, n_shared, block_m, wf)
     ws = workspace(x.device, need) if ws is None else ws
-    check(lib().moe_layer(_ptr(x), _ptr(gate), _ptr(bias), wf, _ptr(w13), _ptr(w13_scale), _ptr(w2),
-                          _ptr(w2_scale), T, H, E, F, k, n_shared, n_group, topk_group, SCORING[scoring],
+    check(lib().moe_layer(_ptr(x), _ptr(gate), _gate_is_fp32(gate), _ptr(bias), wf, _ptr(w13), _ptr(w13_scale),
+                          _ptr(w2), _ptr(w2_scale), T, H, E, F, k, n_shared, n_group, topk_group, SCORING[scoring],
                           int(bool(renormalize)), float(routed_scale), block_m, float(swiglu_limit), _ptr(y),
                           _ptr(ids), _ptr(w),
                           _ptr(ws), ws.numel(), _stream(x.device)), "moe_layer")
@@ -201,10 +210,11 @@ def layer_noalloc(x, gate, bias, w13, w2, k, scoring="softmax", n_group=1, topk_
     if return_routing:
         ids = torch.empty((T, k + n_shared), dtype=torch.int32, device=x.device)
         w = torch.empty((T, k + n_shared), dtype=torch.float32, device=x.device)
-    check(lib().moe_layer_noalloc(_ptr(x), _ptr(gate), _ptr(bias), WFORMAT[wformat], _ptr(w13), _ptr(w13_scale),
-                                  _ptr(w2), _ptr(w2_scale), T, H, E, F, k, n_shared, n_group, topk_group,
-                                  SCORING[scoring], int(bool(renormalize)), float(routed_scale), block_m,
-                                  float(swiglu_limit), _ptr(y), _ptr(ids), _ptr(w), _stream(x.device)),
+    check(lib().moe_layer_noalloc(_ptr(x), _ptr(gate), _gate_is_fp32(gate), _ptr(bias), WFORMAT[wformat],
+                                  _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), T, H, E, F, k, n_shared,
+                                  n_group, topk_group, SCORING[scoring], int(bool(renormalize)),
+                                  float(routed_scale), block_m, float(swiglu_limit), _ptr(y), _ptr(ids), _ptr(w),
+                                  _stream(x.device)),
           "moe_layer_noalloc")
     return (y, ids, w) if return_routing else y
 

@@ -45,6 +45,10 @@ class LazyExperts:
 
 
 def oracle_route(cfg, x, gate, bias):
+    """The oracle router on the same inputs; a bf16 gate is handed over as
+    its values (widened to float32, which is exact)."""
+    if gate.dtype == torch.bfloat16:
+        gate = gate.to(torch.float32)
     return orouter.route(to_numpy(x), to_numpy(gate), to_numpy(bias), cfg.k, cfg.scoring,
                          cfg.n_group, cfg.topk_group, cfg.renormalize, cfg.routed_scale)
 

@@ -52,9 +52,12 @@ def test_status_strings(L):
 
 
 def test_route_argument_checks(L):
-    def call(T=4, H=128, E=8, k=2, ng=1, tg=1, scoring=0, ws=FAKE, nbytes=1 << 20):
-        return L.moe_route(FAKE, FAKE, None, T, H, E, k, ng, tg, scoring, 1, 1.0, FAKE, FAKE, None, ws, nbytes, None)
+    def call(T=4, H=128, E=8, k=2, ng=1, tg=1, scoring=0, ws=FAKE, nbytes=1 << 20, gf=1):
+        return L.moe_route(FAKE, FAKE, gf, None, T, H, E, k, ng, tg, scoring, 1, 1.0, FAKE, FAKE, None, ws, nbytes,
+                           None)
     assert call(T=-1) == 1
+    assert call(gf=2) == 1 and call(gf=-1) == 1  # gate_is_fp32 is 0 (bf16) or 1 (fp32)
+    assert call(gf=0, k=9) == 1       # a bf16 gate is checked the same way
     assert call(H=192) == 1           # H not a multiple of 128
     assert call(k=0) == 1
     assert call(k=9) == 1             # k > E
@@ -82,10 +85,11 @@ def test_align_argument_checks(L):
 
 
 def test_route_align_argument_checks(L):
-    def call(T=4, H=128, E=8, k=2, bm=16, ws=FAKE, nbytes=1 << 22, ns=0):
-        return L.moe_route_align(FAKE, FAKE, None, T, H, E, k, ns, 1, 1, 0, 1, 1.0, bm, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                 ws, nbytes, None)
+    def call(T=4, H=128, E=8, k=2, bm=16, ws=FAKE, nbytes=1 << 22, ns=0, gf=1):
+        return L.moe_route_align(FAKE, FAKE, gf, None, T, H, E, k, ns, 1, 1, 0, 1, 1.0, bm, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, ws, nbytes, None)
     assert call(H=192) == 1           # router checks
+    assert call(gf=3) == 1
     assert call(k=9) == 1
     assert call(bm=0) == 1            # alignment checks
     assert call(bm=2048) == 1
@@ -115,10 +119,11 @@ def test_ffn_and_layer_argument_checks(L):
     assert ffn(T=300000, H=7168, F=2048, E=256, k=8, bm=128) == 2
     assert ffn(T=4, H=32768, F=32768) == 2
 
-    def layer(T=4, H=256, E=8, F=128, k=2, bm=0, ws=FAKE, nbytes=1 << 30, ns=0):
-        return L.moe_layer(FAKE, FAKE, None, 0, FAKE, None, FAKE, None, T, H, E, F, k, ns, 1, 1, 0, 1, 1.0, bm,
+    def layer(T=4, H=256, E=8, F=128, k=2, bm=0, ws=FAKE, nbytes=1 << 30, ns=0, gf=1):
+        return L.moe_layer(FAKE, FAKE, gf, None, 0, FAKE, None, FAKE, None, T, H, E, F, k, ns, 1, 1, 0, 1, 1.0, bm,
                            math.inf, FAKE, None, None, ws, nbytes, None)
     assert layer(bm=48) == 1
+    assert layer(gf=2) == 1
     assert layer(ns=2) == 1 and layer(ns=-1) == 1
     assert layer(nbytes=1000) == 3
     assert layer(T=0) == 0

@@ -36,13 +36,16 @@ def run_layer(cfg, W, x, block_m=0, limit=np.inf):
                      swiglu_limit=limit)
 
 
-def check_layer(cfg, T, block_m=0, limit=np.inf, dense=True):
+def check_layer(cfg, T, block_m=0, limit=np.inf, dense=True, gate_bf16=False):
     """moe_layer against the oracle on every token.  ``dense``: against the
     dense-equivalent oracle (the headline tolerance); the quantised formats
-    are also checked against the emulate-mode oracle."""
+    are also checked against the emulate-mode oracle.  ``gate_bf16``: the
+    router takes the gate rows rounded to bf16 (both sides)."""
     say(f"layer {cfg.name} {cfg.wformat} E={cfg.E} H={cfg.H} F={cfg.F} k={cfg.k} T={T} block_m={block_m}"
-        + (f" SwiGLU limit {limit}" if np.isfinite(limit) else ""))
+        + (f" SwiGLU limit {limit}" if np.isfinite(limit) else "") + (" bf16 gate" if gate_bf16 else ""))
     W = weights_for(cfg)
+    if gate_bf16:
+        W = dict(W, gate=W["gate"].to(torch.bfloat16))
     x = make_x(cfg, T, "cuda")
     y, ids, w = run_layer(cfg, W, x, block_m, limit)
     torch.cuda.synchronize()
@@ -130,6 +133,20 @@ def test_layer_full_size_all_tokens(name, T):
     times (block_m chosen by the library), every token compared."""
     cfg = get_config(name)
     check_layer(cfg, T, 0)
+
+
+# the router on bf16 gate rows inside the layer: the one-launch decode
+# router with its fused alignment (and x quantisation for MXFP4), and the
+# prefill layout
+BF16_GATE = [("toy", dict(E=16, k=4, H=384, F=256, scoring="sigmoid", has_bias=True), 333, 0),
+             ("toy", dict(F=256), 3, 0), ("dsv4", dict(E=16, H=1024, F=512, k=4), 2, 0),
+             ("dsv4", dict(E=16, H=1024, F=512, k=4), 300, 64), ("glm", {}, 8, 0)]
+
+
+@pytest.mark.parametrize("name,over,T,bm", BF16_GATE)
+def test_layer_bf16_gate(name, over, T, bm):
+    cfg = get_config(name, **over)
+    check_layer(cfg, T, bm, gate_bf16=True)
 
 
 RENORM_OFF = [("toy", dict(F=256), 100, 16), ("qwen3", {}, 64, 0)]

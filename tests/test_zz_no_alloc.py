@@ -66,7 +66,7 @@ def test_layer_noalloc_rejects_oversized_shapes():
 
     def call(T, H, E, F, k, wformat=0, bm=0):
         sc = fake if wformat else None
-        return L.moe_layer_noalloc(fake, fake, None, wformat, fake, sc, fake, sc, T, H, E, F, k, 0, 1, 1, 0, 1,
+        return L.moe_layer_noalloc(fake, fake, 1, None, wformat, fake, sc, fake, sc, T, H, E, F, k, 0, 1, 1, 0, 1,
                                    1.0, bm, float("inf"), fake, None, None, None)
 
     big = (8192, 4096, 256, 2048, 6)  # the 8192-token DeepSeek-V4-Flash-shaped prefill
