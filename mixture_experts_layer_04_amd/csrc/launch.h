@@ -36,7 +36,7 @@ moe_status launch_route(const void* x, const void* gate, int gate_is_fp32, const
 // two launches and launch_align.
 // n_shared = 1: slot k of every token is the shared expert (id E, weight 1),
 // ids / weights rows hold k + 1 slots and the alignment covers E + 1 experts.
-// qfmt 1 (FP8) / 2 (MX): where route_quantizes_x(T, E), the router also
+// qfmt 1 (FP8) / 2 (MX): where route_quantizes_x(T, E, H), the router also
 // quantises x into xq / xs as the FFN's activation stage would; 0: no.
 moe_status launch_route_align(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H,
                               int E, int k,

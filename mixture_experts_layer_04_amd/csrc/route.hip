@@ -506,24 +506,31 @@ __global__ __launch_bounds__(256) void route_small(RouteParams p, AlignParams ap
 }
 
 // ---------------------------------------------------------------------------
-// Prefill layout, first kernel: the group sum G_j of a 128-token x 64-expert
+// Prefill layout, first kernel: the group sum G_j of a 128-token x 32 EW-expert
 // tile for one K group j (4 chunks of 128), written to part[j][t][e].
-// 4 waves as 2 x 2, each 64 tokens x 32 experts (4 x 2 fragments).  Per
-// 32-wide K step the 256 threads split the tile's 64 x 32 gate values once
+// 4 waves as 2 x 2, each 64 tokens x 16 EW experts (4 x EW fragments).  Per
+// 32-wide K step the 256 threads split the tile's 32 EW x 32 gate values once
 // into LDS planes (each gate value is split once per 128 tokens: the split
 // and its two barriers per step cost more than the step's multiplies at
 // 64 tokens); the gate and x values of the next PF steps are in flight
 // meanwhile.
 constexpr int TFR = 4;             // token fragments per wave
 constexpr int LT = 2 * 16 * TFR;   // tokens per tile
-constexpr int LE = 64;  // experts per tile
 constexpr int PF = 1;   // steps loaded ahead (measured: 1 against 4, the same
                         // at Qwen3 T=4096 and GLM T=512, DSV3 T=2048 66.9 -> 60.5 us,
                         // DSV4 T=8192 115.5 -> 101.1 us: fewer registers, more
                         // workgroups per CU)
+// Expert fragments per wave: a tile holds 32 EW experts, and each expert
+// tile reads the token rows' x once.  EW = 4 (227 VGPRs, two waves per SIMD)
+// where its grid still has at least kWideTiles workgroups, else 2 (142
+// VGPRs, three).  Measured (router alone, warm, EW 2 against 4): DSV4 T=8192
+// 114.5 / 98 us (1024 wide tiles), DSV3 T=2048 64.7 / 56 us (448), but Qwen3
+// T=4096 35 / 43.5 (128), GLM T=512 32 / 39.7 (96), DSV3 T=256 33 / 41 (56).
+constexpr int kWideTiles = 384;
 
-template <bool GB>
+template <bool GB, int EW>
 __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
+  constexpr int LE = 32 * EW;  // experts per tile
   __shared__ __attribute__((aligned(16))) uint16_t planes[LE * PROW];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -538,18 +545,19 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
   const int k0 = j * KCH * CPG;                 // first K of the group
   const int nsteps = min(KCH * CPG, p.H - k0) / 32;
 
-  // this thread's two float4 pieces of each K step: expert row (tid >> 3) and
-  // (tid >> 3) + 32, K offset (tid & 7) * 4
+  // this thread's EW pieces of four gate values per K step: expert rows
+  // (tid >> 3) + 32 i, K offset (tid & 7) * 4
   const int se = tid >> 3;
   const int sk = (tid & 7) * 4;
-  const bool sv0 = e0 + se < p.E;
-  const bool sv1 = e0 + se + 32 < p.E;
-  const size_t g0o = (size_t)min(e0 + se, p.E - 1) * p.H + k0 + sk;
-  const size_t g1o = (size_t)min(e0 + se + 32, p.E - 1) * p.H + k0 + sk;
-  const float* g0p = static_cast<const float*>(p.gate) + g0o;
-  const float* g1p = static_cast<const float*>(p.gate) + g1o;
-  const uint16_t* b0p = static_cast<const uint16_t*>(p.gate) + g0o;
-  const uint16_t* b1p = static_cast<const uint16_t*>(p.gate) + g1o;
+  bool sv[EW];
+  size_t go[EW];
+#pragma unroll
+  for (int i = 0; i < EW; ++i) {
+    sv[i] = e0 + se + 32 * i < p.E;
+    go[i] = (size_t)min(e0 + se + 32 * i, p.E - 1) * p.H + k0 + sk;
+  }
+  const float* g32 = static_cast<const float*>(p.gate);
+  const uint16_t* g16 = static_cast<const uint16_t*>(p.gate);
   const uint16_t* xr[TFR];
   bool tv[TFR];
 #pragma unroll
@@ -559,29 +567,29 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
     xr[tf] = p.x + (size_t)(tv[tf] ? t : 0) * p.H + k0 + q * 8;
   }
 
-  f32x4_t part[TFR][2], grp[TFR][2];
+  f32x4_t part[TFR][EW], grp[TFR][EW];
 #pragma unroll
   for (int a = 0; a < TFR; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < EW; ++b) {
       part[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       grp[a][b] = part[a][b];
     }
 
   // register ring of PF steps (past the last step: the last step again), as
   // raw bits: four fp32 gate values per row, or four bf16 ones in .x / .y
-  uint4 rg0[PF], rg1[PF];
+  uint4 rg[PF][EW];
   bf16x8_t rx[PF][TFR];
   auto load = [&](int st, int slot) {
     const int kb = min(st, nsteps - 1) * 32;
-    if constexpr (GB) {
-      const uint2 v0 = *reinterpret_cast<const uint2*>(b0p + kb);
-      const uint2 v1 = *reinterpret_cast<const uint2*>(b1p + kb);
-      rg0[slot] = make_uint4(v0.x, v0.y, 0u, 0u);
-      rg1[slot] = make_uint4(v1.x, v1.y, 0u, 0u);
-    } else {
-      rg0[slot] = *reinterpret_cast<const uint4*>(g0p + kb);
-      rg1[slot] = *reinterpret_cast<const uint4*>(g1p + kb);
+#pragma unroll
+    for (int i = 0; i < EW; ++i) {
+      if constexpr (GB) {
+        const uint2 v = *reinterpret_cast<const uint2*>(g16 + go[i] + kb);
+        rg[slot][i] = make_uint4(v.x, v.y, 0u, 0u);
+      } else {
+        rg[slot][i] = *reinterpret_cast<const uint4*>(g32 + go[i] + kb);
+      }
     }
 #pragma unroll
     for (int tf = 0; tf < TFR; ++tf) rx[slot][tf] = *reinterpret_cast<const bf16x8_t*>(xr[tf] + kb);
@@ -594,36 +602,34 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
     for (int u = 0; u < PF; ++u) {
       const int st = s0 + u;
       if (st >= nsteps) break;
-      const uint4 g0 = sv0 ? rg0[u] : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 g1 = sv1 ? rg1[u] : make_uint4(0u, 0u, 0u, 0u);
+      uint4 gv[EW];
+#pragma unroll
+      for (int i = 0; i < EW; ++i) gv[i] = sv[i] ? rg[u][i] : make_uint4(0u, 0u, 0u, 0u);
       bf16x8_t a[TFR];
 #pragma unroll
       for (int tf = 0; tf < TFR; ++tf) a[tf] = tv[tf] ? rx[u][tf] : bf16x8_t{};
       load(st + PF, u);
       __syncthreads();  // the previous step's planes are consumed
-      if constexpr (GB) {  // the bf16 gate is the hi plane
-        uint16_t* row = planes + se * PROW + sk;
-        *reinterpret_cast<uint2*>(row) = make_uint2(g0.x, g0.y);
-        *reinterpret_cast<uint2*>(row + 32 * PROW) = make_uint2(g1.x, g1.y);
-      } else {
-        uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
-        uint16_t* row = planes + se * PROW + sk;
-        split3(__uint_as_float(g0.x), h0, m0, l0); split3(__uint_as_float(g0.y), h1, m1, l1);
-        split3(__uint_as_float(g0.z), h2, m2, l2); split3(__uint_as_float(g0.w), h3, m3, l3);
-        *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
-        *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-        row += 32 * PROW;
-        split3(__uint_as_float(g1.x), h0, m0, l0); split3(__uint_as_float(g1.y), h1, m1, l1);
-        split3(__uint_as_float(g1.z), h2, m2, l2); split3(__uint_as_float(g1.w), h3, m3, l3);
-        *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
-        *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+#pragma unroll
+      for (int i = 0; i < EW; ++i) {
+        uint16_t* row = planes + (se + 32 * i) * PROW + sk;
+        if constexpr (GB) {  // the bf16 gate is the hi plane
+          *reinterpret_cast<uint2*>(row) = make_uint2(gv[i].x, gv[i].y);
+        } else {
+          uint32_t h0, m0, l0, h1, m1, l1, h2, m2, l2, h3, m3, l3;
+          split3(__uint_as_float(gv[i].x), h0, m0, l0);
+          split3(__uint_as_float(gv[i].y), h1, m1, l1);
+          split3(__uint_as_float(gv[i].z), h2, m2, l2);
+          split3(__uint_as_float(gv[i].w), h3, m3, l3);
+          *reinterpret_cast<uint2*>(row) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+          *reinterpret_cast<uint2*>(row + 32) = make_uint2(m0 | (m1 << 16), m2 | (m3 << 16));
+          *reinterpret_cast<uint2*>(row + 64) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+        }
       }
       __syncthreads();
 #pragma unroll
-      for (int ef = 0; ef < 2; ++ef) {
-        const uint16_t* pr = planes + (wn * 32 + ef * 16 + r) * PROW + q * 8;
+      for (int ef = 0; ef < EW; ++ef) {
+        const uint16_t* pr = planes + (wn * 16 * EW + ef * 16 + r) * PROW + q * 8;
         const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pr);
         bf16x8_t bm{}, bl{};
         if constexpr (!GB) {
@@ -638,7 +644,7 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
 #pragma unroll
         for (int tf = 0; tf < TFR; ++tf)
 #pragma unroll
-          for (int ef = 0; ef < 2; ++ef) {
+          for (int ef = 0; ef < EW; ++ef) {
             grp[tf][ef] = first ? part[tf][ef] : grp[tf][ef] + part[tf][ef];
             part[tf][ef] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
@@ -648,11 +654,11 @@ __global__ __launch_bounds__(256) void route_logits_group(RouteParams p) {
 #pragma unroll
   for (int tf = 0; tf < TFR; ++tf)
 #pragma unroll
-    for (int ef = 0; ef < 2; ++ef)
+    for (int ef = 0; ef < EW; ++ef)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int t = t0 + wm * (LT / 2) + tf * 16 + 4 * q + ii;
-        const int e = e0 + wn * 32 + ef * 16 + r;
+        const int e = e0 + wn * 16 * EW + ef * 16 + r;
         if (t < p.T && e < p.E) p.part[((size_t)j * p.T + t) * p.E + e] = grp[tf][ef][ii];
       }
 }
@@ -677,7 +683,11 @@ bool use_large(int T, int E, int H) {
 template <int SLOTS, bool GB>
 moe_status launch_slots(const RouteParams& p, const AlignParams* ap, hipStream_t stream) {
   if (use_large(p.T, p.E, p.H)) {
-    route_logits_group<GB><<<dim3(ceil_div(p.T, LT), ceil_div(p.E, LE), p.NG), 256, 0, stream>>>(p);
+    const dim3 wide(ceil_div(p.T, LT), ceil_div(p.E, 128), p.NG);
+    if (p.E > 64 && (int64_t)wide.x * wide.y * wide.z >= kWideTiles)
+      route_logits_group<GB, 4><<<wide, 256, 0, stream>>>(p);
+    else
+      route_logits_group<GB, 2><<<dim3(ceil_div(p.T, LT), ceil_div(p.E, 64), p.NG), 256, 0, stream>>>(p);
     MOE_CHECK_LAUNCH();
     route_select<SLOTS><<<ceil_div(p.T, 4), 256, 0, stream>>>(p);
   } else {
@@ -749,7 +759,7 @@ moe_status route_launch(const void* x, const void* gate, int gate_is_fp32, const
   p.xq = nullptr;
   p.xs = nullptr;
   p.qfmt = 0;
-  if (!use_large(T, E, H) && qfmt != 0) {
+  if (qfmt != 0 && route_quantizes_x(T, E, H)) {
     p.xq = static_cast<uint8_t*>(xq);
     p.xs = xs;
     p.qfmt = qfmt;
@@ -777,6 +787,9 @@ size_t route_align_workspace_size(int T, int H, int E, int k, int n_shared) {
   return r > a ? r : a;
 }
 
+// The decode layout quantises x on the way.  (The prefill layout could too,
+// a 32-wide K step being one MX group, but its 32-byte pieces of each xq row
+// made the layer slower: DSV4 T=8192 1868 -> 1879 us, same process.)
 bool route_quantizes_x(int T, int E, int H) { return !use_large(T, E, H); }
 
 moe_status launch_route_align(const void* x, const void* gate, int gate_is_fp32, const float* bias, int T, int H,
