@@ -12,9 +12,12 @@ namespace moe {
 template <int KM>
 __device__ __forceinline__ uint4 combine8(const uint16_t* out, const int32_t* ids, const float* w, int t, int h,
                                           int H, int E, int k) {
-  uint4 o[KM];  // all k rows in flight at once, then added in slot order
+  uint4 o[KM];  // all k rows in flight at once (read once: non-temporal), then added in slot order
 #pragma unroll
-  for (int j = 0; j < KM; ++j) o[j] = *reinterpret_cast<const uint4*>(out + ((size_t)t * k + j) * H + h);
+  for (int j = 0; j < KM; ++j) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(out + ((size_t)t * k + j) * H + h));
+    o[j] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < KM; ++j) {

@@ -172,7 +172,10 @@ struct RowScatter {
       if (sid[i] >= p.A) continue;  // padding, or past the tile's rows
       const int lr = tid / CH + RP * i;
       const uint4 val = *reinterpret_cast<const uint4*>(st + lr * CH * 16 + c * 16);
-      *reinterpret_cast<uint4*>(p.out + (size_t)sid[i] * p.H + col0 + c * 8) = val;
+      // non-temporal: the combine reads these rows once, later; the L2 keeps
+      // the GEMM's own operands instead (DSV4 T=8192 layer about 7 us faster)
+      __builtin_nontemporal_store(u32x4_t{val.x, val.y, val.z, val.w},
+                                  reinterpret_cast<u32x4_t*>(p.out + (size_t)sid[i] * p.H + col0 + c * 8));
     }
   }
 };
