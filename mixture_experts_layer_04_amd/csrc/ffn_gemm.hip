@@ -294,15 +294,22 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// vmcnt(min(n, N)) for a wave-uniform n
+// vmcnt(clamp(n, LO, HI)) for a wave-uniform n, by bisection (the count is an
+// immediate of the instruction)
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_in(int n) {
+  if constexpr (LO == HI) {
+    wait_vm<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vm_in<MID, HI>(n);
+    else wait_vm_in<LO, MID - 1>(n);
+  }
+}
+// vmcnt(min(n, N)) for a wave-uniform n >= 0
 template <int N>
 __device__ __forceinline__ void wait_vm_upto(int n) {
-  if constexpr (N == 0) {
-    wait_vm<0>();
-  } else {
-    if (n >= N) wait_vm<N>();
-    else wait_vm_upto<N - 1>(n);
-  }
+  wait_vm_in<0, N>(n);
 }
 // Copy instructions a wave has issued after the last one of step s when it
 // waits ahead of step s, for a stream of L copy instructions per step issued
@@ -330,6 +337,34 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+// A barrier after which every wave sees the LDS writes made before it, with
+// no wait on vector memory operations (copies into LDS and global stores stay
+// in flight, unlike __syncthreads())
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
+  barrier_no_fence();
+}
+typedef __attribute__((address_space(3))) int lds_int_t;
+// the LDS byte address of a pointer into the workgroup's LDS
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Two 16-byte LDS reads, at byte address addr and addr + OFF, waited for in
+// the same instruction group.  Reads the compiler sees after copies into LDS
+// (buffer_load ... lds) are preceded by a wait for every such copy in flight
+// when it cannot tell the addresses apart; these are not.  Only for LDS that
+// no copy in flight writes.
+template <int OFF>
+__device__ __forceinline__ void lds_read2_b128(uint32_t addr, u32x4_t& a, u32x4_t& b) {
+  static_assert(OFF > 0 && OFF < 65536, "offset");
+  asm volatile(
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %2 offset:%3\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(addr), "n"(OFF)
+      : "memory");
 }
 template <int CPR>
 __device__ __forceinline__ int swz(int c, int row) {
@@ -1136,14 +1171,22 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   constexpr int LA = RA / 8;           // 1 KiB copies per step: 8 A rows of 128 bytes
   constexpr int LB = RB / 16;          //                        16 weight rows of 64 bytes
   constexpr int ABASE = 0, BBASE = NA * ASZ, SBASE = NA * ASZ + NB * BSZ;
+  // most stores per weight wave that a GEMM1 epilogue issues after the next
+  // tile's first copies (rows of BNW / 2 bytes in 16-byte pieces over 256
+  // threads); GEMM2 stores before them
+  constexpr int SXM = G1 ? BMT * (BNW / 32) / (NT / 2) : 0;
   static_assert(BMT <= CW * 64 && BNW == CW * 64 && SBASE + 2 * SCSZ <= 163840 && LA >= 1 && LB >= 1 &&
-                FN % 2 == 0 && LB * (DB - 1) + DB <= 63 && LA * (DA - 1) + DA <= 63 && FM % 2 == 0 &&
+                FN % 2 == 0 && LB * (DB - 1) + DB + SXM <= 63 && LA * (DA - 1) + DA + SXM <= 63 && FM % 2 == 0 &&
                 DA >= 1 && DB >= 1, "tile, LDS, copies and vmcnt");
+  // a scale group goes out after the copies of the step D before its first
+  // step; with D < SCG that is before the copies of its first step
+  static_assert(DA < SCG && DB < SCG, "scale groups land before the steps that read them");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool bwave = wave >= CW;  // copies weight rows (else A rows)
+  const int bt = tid - CW * 64;   // weight waves: thread index among them
   const int cw = wave % CW;       // index among the waves of its copy stream
   const int lane = tid & 63;
   const int wm = wave / WN;  // rows [BB wm, +BB): the tile's first or second block
@@ -1198,7 +1241,10 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   auto in_range = [&](int jx) { return jx < per && (int64_t)xcd * per + jx < n_valid; };
 
   // One tile's copy state: its blocks and N tile, and the copy sources of
-  // this wave's stream.
+  // this wave's stream.  Only GEMM1's A rows are gathered (cg, per tile); the
+  // other streams read rows at a fixed offset from the tile's first one: a
+  // per-lane offset set once (cl) plus the tile's wave-uniform byte offset so,
+  // which rides in the copy's scalar offset.
   constexpr int LC = LA > LB ? LA : LB;
   struct Tile {
     int nt, blk, e;
@@ -1206,8 +1252,22 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
     bool ok;         // the tile lies inside the blocks (tiles of a stale pair table are skipped)
     bool copy_rows;  // A waves: this wave's rows exist
     uint32_t sg;
-    uint32_t cg[LC];
+    uint32_t so;
+    uint32_t cg[G1 ? LC : 1];
   };
+  uint32_t cl[LC];
+#pragma unroll
+  for (int i = 0; i < LC; ++i) {
+    if (bwave) {
+      const int rr = cw * RB + 16 * i + lane / 4;
+      const int c = (lane % 4) ^ ((rr >> 1) & 3);
+      cl[i] = i < LB ? (uint32_t)weight_row(0, rr) * rowbytes_b + 16 * c : 0u;
+    } else {
+      const int rr = cw * RA + 8 * i + lane / 8;
+      const int c = (lane % 8) ^ ((rr >> 1) & 7);
+      cl[i] = (G1 ? 0u : (uint32_t)rr * rowbytes_a) + 16 * c;
+    }
+  }
   // the copy sources as buffer descriptors (rebuilt from the tile's fields:
   // kept in a struct, the descriptor type ended up in scratch memory)
   auto src_rc = [&](const Tile& t) {
@@ -1229,26 +1289,26 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
     t.e = 0;
     t.copy_rows = false;
     t.sg = 0u;
+    t.so = 0u;
 #pragma unroll
-    for (int i = 0; i < LC; ++i) t.cg[i] = 0u;
+    for (int i = 0; i < (G1 ? LC : 1); ++i) t.cg[i] = 0u;
     if (!t.ok) return t;
     t.e = __builtin_amdgcn_readfirstlane(p.block_expert[t.blk]);
     // This wave's copy stream.  A waves: tile rows [RA cw, +RA), 8 per
     // instruction (rows of a missing second block from the empty range).
     // Weight waves: weight rows [RB cw, +RB), 16 per instruction.
     t.copy_rows = (cw * RA < BB) || t.two;
+    if (bwave) t.so = (uint32_t)(t.nt * BNO) * rowbytes_b;
+    else if (!G1) t.so = (uint32_t)(t.blk * BB) * rowbytes_a;  // GEMM2's A rows are the padded rows themselves
+    if constexpr (G1) {
+      if (!bwave) {
 #pragma unroll
-    for (int i = 0; i < LC; ++i) {
-      if (bwave) {
-        const int rr = cw * RB + 16 * i + lane / 4;
-        const int c = (lane % 4) ^ ((rr >> 1) & 3);
-        t.cg[i] = i < LB ? (uint32_t)weight_row(t.nt, rr) * rowbytes_b + 16 * c : 0u;
-      } else {
-        const int rr = cw * RA + 8 * i + lane / 8;
-        const int c = (lane % 8) ^ ((rr >> 1) & 7);
-        bool v;
-        const int src = (i < LA && t.copy_rows) ? a_row_index<G1>(p, t.blk, BB, rr, v) : 0;  // padding: row 0
-        t.cg[i] = (uint32_t)src * rowbytes_a + 16 * c;
+        for (int i = 0; i < LC; ++i) {
+          const int rr = cw * RA + 8 * i + lane / 8;
+          bool v;
+          const int src = (i < LA && t.copy_rows) ? a_row_index<G1>(p, t.blk, BB, rr, v) : 0;  // padding: row 0
+          t.cg[i] = (uint32_t)src * rowbytes_a + cl[i];
+        }
       }
     }
     // scale groups: 16 bytes of A row q (A waves, q = tid < BMT; the rest
@@ -1270,11 +1330,14 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
     if (bwave) {
       uint8_t* st = lds + BBASE + (s % NB) * BSZ + cw * RB * BRB;
 #pragma unroll
-      for (int i = 0; i < LB; ++i) buf2lds16(rc, t.cg[i], s * BRB, st + 16 * i * BRB);
+      for (int i = 0; i < LB; ++i) buf2lds16(rc, cl[i], t.so + s * BRB, st + 16 * i * BRB);
     } else {
       uint8_t* st = lds + ABASE + (s % NA) * ASZ + cw * RA * ARB;
 #pragma unroll
-      for (int i = 0; i < LA; ++i) buf2lds16(rc, t.cg[i], s * ARB, st + 8 * i * ARB);
+      for (int i = 0; i < LA; ++i) {
+        if constexpr (G1) buf2lds16(rc, t.cg[i], s * ARB, st + 8 * i * ARB);
+        else buf2lds16(rc, cl[i], t.so + s * ARB, st + 8 * i * ARB);
+      }
     }
   };
   auto issue_sc = [&](const Tile& t, int G) {
@@ -1303,10 +1366,13 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   auto take_issue = [&]() {
     if (tid == 0) taken = atomicAdd(p.queue + xcd, 1);
   };
+  // (the word is accessed as LDS: through a generic pointer it would take
+  // flat instructions, whose waits cover every vector memory operation)
+  volatile lds_int_t* const ctl3 = (volatile lds_int_t*)ctl;
   auto take_finish = [&]() {
-    if (tid == 0) *reinterpret_cast<volatile int*>(ctl) = wpx + taken;
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(ctl));
+    if (tid == 0) *ctl3 = wpx + taken;
+    lds_barrier();
+    return __builtin_amdgcn_readfirstlane(*ctl3);
   };
 
   f32x4_t acc[FM][FN];
@@ -1314,7 +1380,8 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
   if (in_range(j)) {
     // GEMM1 (PF) issues the next tile's copies ahead of step 0 before its
     // epilogue, so they land while the SwiGLU and requantisation run; the
-    // queue is read one tile ahead for that
+    // queue is read one tile ahead for that.  (GEMM2 staging its output in
+    // quarters to do the same measured slower, DSV4 T=8192: 572 -> 724 us.)
     constexpr bool PF = G1;
     Tile cur = setup(j);
     int jn = per;  // the next tile (per: none)
@@ -1323,10 +1390,17 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
       jn = take_finish();
     }
     bool pre = false;  // cur's copies ahead of step 0 are in flight
+    // stores this wave issued after cur's copies ahead of step 0 (a lower
+    // bound): the waits of steps 0 .. D - 1 leave them in flight too
+    // (vector memory operations complete in issue order)
+    int sx = 0;
     for (;;) {
       const bool mine = wm == 0 || cur.two;  // this wave's block exists
       if (cur.ok) {
-        if (!pre) prologue(cur);
+        if (!pre) {
+          prologue(cur);
+          sx = 0;
+        }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -1338,8 +1412,9 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
           // the copies of steps s + DA (A) / s + DB (weights) and of the
           // next scale group.
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no other count
-          if (bwave) wait_vm_upto<LB * (DB - 1) + DB>(copies_after<LB, DB, SCG>(s, nk, ng));
-          else wait_vm_upto<LA * (DA - 1) + DA>(copies_after<LA, DA, SCG>(s, nk, ng));
+          const int sxs = s < (bwave ? DB : DA) ? sx : 0;
+          if (bwave) wait_vm_upto<LB * (DB - 1) + DB + SXM>(copies_after<LB, DB, SCG>(s, nk, ng) + sxs);
+          else wait_vm_upto<LA * (DA - 1) + DA + SXM>(copies_after<LA, DA, SCG>(s, nk, ng) + sxs);
           barrier_no_fence();
           issue(cur, s + (bwave ? DB : DA));
           if (s % SCG == 0) issue_sc(cur, s / SCG + 1);
@@ -1397,11 +1472,11 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
       const bool more = in_range(jn);
       Tile nx = cur;
       if (more) {
+        take_issue();  // the tile after next, or past the end
         if (PF) {
           nx = setup(jn);
           if (nx.ok) prologue(nx);
         }
-        take_issue();  // the tile after next, or past the end
       }
 
       // ---------------------------------------------------------------- epilogue
@@ -1458,26 +1533,34 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
         }
       }
       // the staged tile is complete (and the next index is in ctl)
+      sx = 0;
       int jnn = per;
       if (more) jnn = take_finish();
-      else __syncthreads();
+      else lds_barrier();
       if (cur.ok) {
         if (G1) {
           // the weight waves store (the A waves' first copies of the next
           // tile then wait for no store)
           uint8_t* acts = static_cast<uint8_t*>(p.act_s);
           if (bwave) {
-            const int bt = tid - CW * 64;
             // the tile's BNA / 32 codes of a row are one 4-byte word of act_s
             if (bt < nrows)
               *reinterpret_cast<uint32_t*>(acts + (size_t)(cur.blk * BB + bt) * (p.F / 32) + cur.nt * (BNA / 32)) =
                   *reinterpret_cast<const uint32_t*>(cds + bt * (BNA / 32));
-            constexpr int CH = BNA / 16;  // 16-byte chunks per tile row
-            for (int idx = bt; idx < nrows * CH; idx += NT / 2) {
-              const int lr = idx / CH;
-              const int c = idx % CH;
-              const uint4 val = *reinterpret_cast<const uint4*>(stg + lr * BNA + c * 16);
-              *reinterpret_cast<uint4*>(p.act + (size_t)(cur.blk * BB + lr) * p.F + cur.nt * BNA + c * 16) = val;
+            // piece bt + it NT / 2 (it = 0 .. nrows / RPI - 1) of the tile:
+            // chunk bt % CH of row bt / CH + it RPI, read two at a time
+            constexpr int CH = BNA / 16;       // 16-byte chunks per tile row
+            constexpr int RPI = NT / 2 / CH;   // rows per piece index step
+            static_assert(NT / 2 % CH == 0 && BB % (2 * RPI) == 0, "every thread stores as many pieces, in pairs");
+            sx = nrows / RPI;  // the act_s word above may be skipped: not counted
+            const int c = bt % CH;
+            const uint32_t a0 = lds_addr(stg + (bt / CH) * BNA + c * 16);
+            uint8_t* const g0 = p.act + (size_t)(cur.blk * BB + bt / CH) * p.F + cur.nt * BNA + c * 16;
+            for (int it = 0; it < nrows / RPI; it += 2) {
+              u32x4_t v0, v1;
+              lds_read2_b128<RPI * BNA>(a0 + (uint32_t)(it * RPI * BNA), v0, v1);
+              *reinterpret_cast<u32x4_t*>(g0 + (size_t)(it * RPI) * p.F) = v0;
+              *reinterpret_cast<u32x4_t*>(g0 + (size_t)((it + 1) * RPI) * p.F) = v1;
             }
           }
         } else {
@@ -1486,7 +1569,7 @@ __global__ __launch_bounds__(512) void gemm_pair_mx(GemmP p) {
       }
       if (!more) break;
       if (!PF) {
-        __syncthreads();  // every wave is done reading the staged tile
+        lds_barrier();  // every wave is done reading the staged tile
         nx = setup(jn);
       }
       cur = nx;
